@@ -1,0 +1,165 @@
+/*
+ * pa.h — C ABI of libpagedattn: paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * The KV cache lives in fixed-size physical blocks of `block_size` tokens (16 or 32) that may sit
+ * anywhere in a pool; each sequence reaches its blocks through a block table that maps logical
+ * token positions to physical block ids ("Serving engine internals" lesson, section
+ * "PagedAttention as a virtual memory system"; "Inference optimization" lesson, section "Paged
+ * attention"; vLLM-on-H100 article, section "PagedAttention borrows from operating systems").
+ * Attention itself is max-subtracted softmax(q·kᵀ·scale)·v ("Inference optimization", Build it,
+ * Step 2: attention with a KV cache), with grouped-query heads (exercises of the same lesson).
+ *
+ * Conventions for every entry point
+ *   - All arrays are device pointers owned by the caller; the library allocates no device memory,
+ *     keeps no device state between calls, and never synchronises the stream.
+ *   - bf16 tensors are raw 16-bit bfloat16 bit patterns, contiguous, 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call enqueues its kernels on
+ *     that stream and returns immediately.
+ *   - Errors that can be seen from host-side scalars and pointer values are returned before any
+ *     launch, with no buffer touched: PA_ERR_NULL_POINTER, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED,
+ *     PA_ERR_WORKSPACE.  PA_ERR_HIP means a launch failed.  pa_last_error() then holds a message
+ *     for the calling thread.
+ *   - Contents of device arrays (lengths, table entries, slots) are preconditions, not checked on
+ *     the host.  Kernels clamp what they must to stay inside the buffers they were given (a slot
+ *     past the pool is skipped), but results for inputs that break a precondition are unspecified.
+ *
+ * Pool layout (the library's own; the pages fix only that blocks are fixed-size and placed
+ * anywhere).  key_cache and value_cache are each [num_blocks][num_kv_heads][block_size*head_dim]
+ * bf16.  A block is cut into sub-blocks of 16 tokens; inside a sub-block
+ *   K is [head_dim/32][16][32]: per 32-wide slice of the head dimension, 16 tokens x 32 values;
+ *   V is [head_dim][16]:         per head-dimension index, the 16 tokens' values.
+ * Element (token o of the block, dim d) therefore sits at, counting from the (block, head) tile,
+ *   K: (o/16)*16*head_dim + (d/32)*512 + (o%16)*32 + d%32
+ *   V: (o/16)*16*head_dim + d*16 + o%16
+ * Callers write the pools only through pa_reshape_and_cache, so the layout is opaque to them.
+ */
+#ifndef PAGEDATTN_PA_H
+#define PAGEDATTN_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status_t;
+
+#define PA_OK 0
+#define PA_ERR_NULL_POINTER 1 /* a required pointer is NULL */
+#define PA_ERR_INVALID_ARG 2  /* negative size, Hq % Hkv != 0, misaligned pointer, bad stride ... */
+#define PA_ERR_UNSUPPORTED 3  /* head_dim not in {64,128,256}, block_size not in {16,32}, group too wide */
+#define PA_ERR_WORKSPACE 4    /* workspace NULL or smaller than the *_workspace_bytes query */
+#define PA_ERR_HIP 5          /* a kernel launch failed; see pa_last_error() */
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t pa_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * pa_reshape_and_cache — write the K/V rows of new tokens into their cache slots.
+ *
+ * Source: blocks fill as tokens arrive and a sequence that outgrows its blocks gets one more
+ * ("Serving engine internals", PagedAttention section); the slot of logical position p of a
+ * sequence is  block_table[p / block_size] * block_size + p % block_size.
+ *
+ *   key, value     bf16 [num_tokens] rows; token t, head h, dim d at t*kv_token_stride + h*head_dim + d
+ *   kv_token_stride elements between consecutive tokens (>= num_kv_heads*head_dim, multiple of 8)
+ *   key_cache, value_cache  pools as described above, modified in place
+ *   slot_mapping   int64 [num_tokens]; negative = skip this token; slots past the pool are skipped
+ *   num_blocks     physical blocks in each pool
+ * Slots must be pairwise distinct within one call (otherwise which row lands is unspecified).
+ * The copy is bit-exact.  num_tokens == 0 is a no-op.
+ */
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_token_stride,
+                                 void* key_cache, void* value_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, void* stream);
+
+/*
+ * Bytes of workspace pa_decode needs for this batch shape.  The workspace holds per-partition
+ * partial softmax states of sequences longer than one partition; 0 means none is needed and
+ * `workspace` may then be NULL.  It may be reused across calls on one stream and needs no
+ * initialisation.  Calls that run concurrently on different streams need separate workspaces.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_seq_len);
+
+/*
+ * pa_decode — one query token per sequence against that sequence's whole paged context.
+ *
+ * Source: decode produces one token per step and re-reads the accumulated KV cache each time
+ * ("Inference optimization", section "Prefill vs decode"; vLLM-on-H100 article, section "Decode is
+ * a memory problem"); the attention is Step 2 of the same lesson with a single query row.
+ * Query head h reads KV head h / (num_q_heads/num_kv_heads).
+ *
+ *   out            bf16 [num_seqs][num_q_heads][head_dim] (written; must not alias inputs)
+ *   query          bf16 [num_seqs][num_q_heads][head_dim]
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]; only the first ceil(L/block_size)
+ *                  entries of a row are read
+ *   seq_lens       int32 [num_seqs]; L = cached tokens including the query's own K/V
+ *                  (0 <= L <= max_seq_len); L == 0 yields a zero output row
+ *   max_seq_len    an upper bound of every seq_lens entry, known on the host
+ *                  (<= max_blocks_per_seq*block_size); sizes the work grid and the workspace
+ *   scale          softmax scale, normally 1/sqrt(head_dim)
+ *   workspace      device buffer of at least pa_decode_workspace_bytes(...) bytes
+ * Output is fp32-accumulated and rounded to bf16 (nearest even).  Supported: head_dim 64 with
+ * group size <= 16, head_dim 128 with group <= 8, head_dim 256 with group <= 4.
+ */
+pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
+                      const void* value_cache, const int32_t* block_tables,
+                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_prefill_chunk needs for this batch shape. */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                                  int32_t head_dim, int32_t max_seq_len);
+
+/*
+ * pa_prefill_chunk — causal attention of a chunk of query tokens per sequence over the
+ * sequence's paged context (chunked prefill).
+ *
+ * Source: long prompts are processed in fixed-size chunks (512 tokens by default) that attend to
+ * everything cached before them and are batched with decode tokens ("Serving engine internals",
+ * section "Chunked prefill protects the TTFT tail"); the mask is Step 2's causal mask aligned to
+ * the end of the key range, so chunk row i (0-based) of a sequence of L cached tokens with q_len
+ * chunk rows sees keys 0 .. L - q_len + i.
+ *
+ *   out            bf16 [total_q][num_q_heads][head_dim]
+ *   query          bf16 [total_q][num_q_heads][head_dim]; sequence i owns rows
+ *                  query_start_loc[i] .. query_start_loc[i+1]-1
+ *   query_start_loc int32 [num_seqs+1], non-decreasing, query_start_loc[num_seqs] == total_q
+ *   seq_lens       int32 [num_seqs]; L_i = prior context + chunk length; the chunk's own K/V must
+ *                  already be in the cache (pa_reshape_and_cache first); L_i >= q_len_i
+ *   max_q_len      host-side upper bound of the chunk lengths
+ *   max_seq_len    host-side upper bound of seq_lens (<= max_blocks_per_seq*block_size)
+ *   workspace      at least pa_prefill_workspace_bytes(...) bytes
+ * Same head_dim / group limits as pa_decode.
+ */
+pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache,
+                             const void* value_cache, const int32_t* block_tables,
+                             const int32_t* query_start_loc, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Kernel timing (tracing).  While enabled, every kernel the library launches is bracketed by a
+ * pair of HIP events recorded on its stream.  pa_trace_read synchronises on the recorded events,
+ * returns the number of launches and their summed duration (milliseconds) for one kernel name, and
+ * forgets those records.  Kernel names: "reshape_and_cache", "decode_partition", "decode_merge",
+ * "prefill_chunk", "prefill_merge".  Events are host-side driver objects; no device memory is used.
+ */
+pa_status_t pa_trace_enable(int32_t enable);
+pa_status_t pa_trace_read(const char* kernel_name, int32_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_PA_H */

@@ -1,0 +1,203 @@
+"""Python binding of libpagedattn (paged KV-cache attention for MI355X / gfx950).
+
+Argument marshalling only: every operation runs in the library's HIP kernels.  Tensors are torch
+tensors on the current HIP device; their data pointers and torch's current stream are handed to the
+C ABI declared in include/pa.h.  There is no fallback: if the shared library is missing or fails to
+load, importing the ops raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "load_library", "reshape_and_cache", "decode", "prefill_chunk", "decode_workspace_bytes",
+    "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_OK = 0
+STATUS_NAMES = {1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_INVALID_ARG", 3: "PA_ERR_UNSUPPORTED",
+                4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP"}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "pa_version": (_I32, []),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_reshape_and_cache": (_I32, [_P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _P]),
+    "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "pa_decode": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                         ctypes.c_float, _P, _SZ, _P]),
+    "pa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_prefill_chunk": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                _I32, _I32, _I32, ctypes.c_float, _P, _SZ, _P]),
+    "pa_trace_enable": (_I32, [_I32]),
+    "pa_trace_read": (_I32, [ctypes.c_char_p, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double)]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_444_amd.build_lib`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        raise PagedAttentionError(status, load_library().pa_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _bf16(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 values (bfloat16 or a 16-bit integer view)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _ints(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU {dtype} tensor")
+    return t.data_ptr()
+
+
+def pool_shape(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int):
+    """Shape of one K or V pool tensor: [num_blocks][num_kv_heads * block_size * head_dim]."""
+    return (num_blocks, num_kv_heads * block_size * head_dim)
+
+
+def _num_blocks(pool: torch.Tensor, num_kv_heads: int, block_size: int, head_dim: int) -> int:
+    per = num_kv_heads * block_size * head_dim
+    if pool.numel() % per:
+        raise ValueError("pool size is not a whole number of blocks")
+    return pool.numel() // per
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor, *, num_kv_heads: int,
+                      head_dim: int, block_size: int) -> None:
+    """Write key/value rows [T][Hkv][D] into the pools at `slot_mapping` (int64 [T], -1 = skip)."""
+    lib = load_library()
+    T = slot_mapping.numel()
+    if key.shape != value.shape or key.numel() != T * num_kv_heads * head_dim:
+        raise ValueError("key/value must be [T][num_kv_heads][head_dim]")
+    n = _num_blocks(key_cache, num_kv_heads, block_size, head_dim)
+    _check(lib.pa_reshape_and_cache(_bf16(key, "key"), _bf16(value, "value"), num_kv_heads * head_dim,
+                                    _bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache"),
+                                    _ints(slot_mapping, torch.int64, "slot_mapping"), T, num_kv_heads,
+                                    head_dim, block_size, n, _stream()))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int) -> int:
+    return int(load_library().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len))
+
+
+def prefill_workspace_bytes(num_seqs: int, total_q: int, num_q_heads: int, head_dim: int,
+                            max_seq_len: int) -> int:
+    return int(load_library().pa_prefill_workspace_bytes(num_seqs, total_q, num_q_heads, head_dim,
+                                                         max_seq_len))
+
+
+def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> tuple:
+    if nbytes == 0:
+        return 0, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    # A too-small workspace is passed through: the library reports PA_ERR_WORKSPACE.
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+           block_tables: torch.Tensor, seq_lens: torch.Tensor, *, num_kv_heads: int, block_size: int,
+           scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged decode attention: query [B][Hq][D] bf16 -> out [B][Hq][D] bf16.
+
+    `max_seq_len` must bound seq_lens; if omitted it is read back from the device (a sync).
+    """
+    lib = load_library()
+    B, Hq, D = query.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(query)
+    ws, ws_bytes = _workspace(decode_workspace_bytes(B, Hq, D, max_seq_len), workspace, query.device)
+    _check(lib.pa_decode(_bf16(out, "out"), _bf16(query, "query"), _bf16(key_cache, "key_cache"),
+                         _bf16(value_cache, "value_cache"), _ints(block_tables, torch.int32, "block_tables"),
+                         _ints(seq_lens, torch.int32, "seq_lens"), B, Hq, num_kv_heads, D, block_size,
+                         block_tables.shape[1], max_seq_len, float(scale), ws, ws_bytes, _stream()))
+    return out
+
+
+def prefill_chunk(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                  block_tables: torch.Tensor, query_start_loc: torch.Tensor, seq_lens: torch.Tensor, *,
+                  num_kv_heads: int, block_size: int, max_q_len: int, max_seq_len: int,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal chunked-prefill attention: query [total_q][Hq][D] -> out [total_q][Hq][D] bf16."""
+    lib = load_library()
+    total_q, Hq, D = query.shape
+    n = seq_lens.numel()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(query)
+    ws, ws_bytes = _workspace(prefill_workspace_bytes(n, total_q, Hq, D, max_seq_len), workspace,
+                              query.device)
+    _check(lib.pa_prefill_chunk(_bf16(out, "out"), _bf16(query, "query"), _bf16(key_cache, "key_cache"),
+                                _bf16(value_cache, "value_cache"),
+                                _ints(block_tables, torch.int32, "block_tables"),
+                                _ints(query_start_loc, torch.int32, "query_start_loc"),
+                                _ints(seq_lens, torch.int32, "seq_lens"), n, total_q, max_q_len, Hq,
+                                num_kv_heads, D, block_size, block_tables.shape[1], max_seq_len,
+                                float(scale), ws, ws_bytes, _stream()))
+    return out
+
+
+def trace_enable(on: bool = True) -> None:
+    _check(load_library().pa_trace_enable(1 if on else 0))
+
+
+def trace_read(kernel_name: str):
+    """(launches, total_ms) recorded for `kernel_name` since the last read; forgets them."""
+    n = _I32()
+    ms = ctypes.c_double()
+    _check(load_library().pa_trace_read(kernel_name.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

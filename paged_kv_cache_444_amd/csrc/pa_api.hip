@@ -1,0 +1,281 @@
+// C ABI of libpagedattn: argument validation, launch geometry, workspace sizing, kernel tracing.
+// Every check that host scalars allow happens here, before any launch.
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status_t fail(pa_status_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pa_status_t fail(pa_status_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+pa_status_t ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+pa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+bool supported_block(int bs) { return bs == 16 || bs == 32; }
+
+// Group size (query heads per KV head) must be a power of two with group*head_dim <= 1024.
+bool supported_group(int g, int d) { return g >= 1 && g <= 16 && (g & (g - 1)) == 0 && g * d <= 1024; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Common validation of the attention entry points.
+pa_status_t check_attention_shape(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_blocks_per_seq,
+                                  int32_t max_seq_len, float scale) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "head counts must be positive (got %d query, %d kv)",
+                num_q_heads, num_kv_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", head_dim);
+  if (!supported_block(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not in {16,32}", block_size);
+  const int g = num_q_heads / num_kv_heads;
+  if (!supported_group(g, head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "group size %d with head_dim %d not supported", g, head_dim);
+  if (max_blocks_per_seq <= 0 || max_seq_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d / max_seq_len %d out of range",
+                max_blocks_per_seq, max_seq_len);
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_seq*block_size %lld",
+                max_seq_len, (long long)max_blocks_per_seq * block_size);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Tracing
+std::atomic<bool> g_trace_on{false};
+std::mutex g_trace_mu;
+struct TraceRec {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::vector<TraceRec> g_trace_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace pa {
+
+TraceScope::TraceScope(const char* name, hipStream_t stream) : slot_(-1), stream_(stream) {
+  if (!g_trace_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return;
+  if (hipEventRecord(a, stream) != hipSuccess) return;
+  g_trace_recs.push_back({name, a, b});
+  slot_ = (int)g_trace_recs.size() - 1;
+}
+
+TraceScope::~TraceScope() {
+  if (slot_ < 0) return;
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  (void)hipEventRecord(g_trace_recs[slot_].stop, stream_);
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int32_t pa_version(void) { return 100; }
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status_t pa_trace_enable(int32_t enable) {
+  g_trace_on.store(enable != 0);
+  return ok();
+}
+
+pa_status_t pa_trace_read(const char* kernel_name, int32_t* launches, double* total_ms) {
+  if (!kernel_name || !launches || !total_ms) return fail(PA_ERR_NULL_POINTER, "null argument");
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  int n = 0;
+  double ms = 0.0;
+  std::vector<TraceRec> keep;
+  for (auto& r : g_trace_recs) {
+    if (r.name != kernel_name) {
+      keep.push_back(r);
+      continue;
+    }
+    hipError_t e = hipEventSynchronize(r.stop);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess) return hip_status(e, "pa_trace_read");
+    ms += t;
+    ++n;
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_trace_recs.swap(keep);
+  *launches = n;
+  *total_ms = ms;
+  return ok();
+}
+
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_token_stride,
+                                 void* key_cache, void* value_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, void* stream) {
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+  if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d <= 0", num_kv_heads);
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", head_dim);
+  if (!supported_block(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not in {16,32}", block_size);
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks %lld <= 0", (long long)num_blocks);
+  if (kv_token_stride < (int64_t)num_kv_heads * head_dim || kv_token_stride % 8 != 0)
+    return fail(PA_ERR_INVALID_ARG, "kv_token_stride %lld must be >= %d and a multiple of 8",
+                (long long)kv_token_stride, num_kv_heads * head_dim);
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_NULL_POINTER, "null pointer argument");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for bf16 arrays)");
+  pa::ReshapeParams p{};
+  p.key = static_cast<const uint16_t*>(key);
+  p.value = static_cast<const uint16_t*>(value);
+  p.token_stride = kv_token_stride;
+  p.kpool = static_cast<uint16_t*>(key_cache);
+  p.vpool = static_cast<uint16_t*>(value_cache);
+  p.slots = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  return hip_status(pa::launch_reshape(p, static_cast<hipStream_t>(stream)), "reshape_and_cache");
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_seq_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
+  const int part = pa::decode_partition_tokens();
+  const size_t P = (size_t)((max_seq_len + part - 1) / part);
+  if (P <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * P;
+  return align_up(rows * 2 * sizeof(float), 256) + rows * head_dim * sizeof(float);
+}
+
+pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
+                      const void* value_cache, const int32_t* block_tables,
+                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+  pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
+                                         max_blocks_per_seq, max_seq_len, scale);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens)
+    return fail(PA_ERR_NULL_POINTER, "null pointer argument");
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for bf16 arrays)");
+  if (out == query) return fail(PA_ERR_INVALID_ARG, "out must not alias query");
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  const int part = pa::decode_partition_tokens();
+  pa::DecodeParams p{};
+  p.out = static_cast<uint16_t*>(out);
+  p.query = static_cast<const uint16_t*>(query);
+  p.kpool = static_cast<const uint16_t*>(key_cache);
+  p.vpool = static_cast<const uint16_t*>(value_cache);
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.part_tokens = part;
+  p.max_parts = max_seq_len > 0 ? (max_seq_len + part - 1) / part : 1;
+  p.len_cap = (int)std::min<int64_t>((int64_t)p.max_parts * part,
+                                     (int64_t)max_blocks_per_seq * block_size);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  if (need > 0) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * p.max_parts;
+    p.ws_ml = static_cast<float*>(workspace);
+    p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align_up(rows * 2 * sizeof(float), 256));
+  }
+  return hip_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)), "decode");
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                                  int32_t head_dim, int32_t max_seq_len) {
+  (void)num_seqs;
+  (void)total_q;
+  (void)num_q_heads;
+  (void)head_dim;
+  (void)max_seq_len;
+  return 0;
+}
+
+pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache,
+                             const void* value_cache, const int32_t* block_tables,
+                             const int32_t* query_start_loc, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)out; (void)query; (void)key_cache; (void)value_cache; (void)block_tables;
+  (void)query_start_loc; (void)seq_lens; (void)num_seqs; (void)total_q; (void)max_q_len;
+  (void)num_q_heads; (void)num_kv_heads; (void)head_dim; (void)block_size;
+  (void)max_blocks_per_seq; (void)max_seq_len; (void)scale; (void)workspace;
+  (void)workspace_bytes; (void)stream;
+  return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk is not built yet");
+}
+
+}  // extern "C"

@@ -17,36 +17,69 @@ a scheduler performs (block id times block size plus the offset in the block).
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
+import threading
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
 
-# Draws are made in chunks of this many values so that multi-GiB pools never
-# need a full fp32 temporary; the chunking is part of the stream definition.
-_CHUNK = 1 << 24
+# Normal draws for large arrays are made in fixed chunks of this many values.  Chunk c of a draw
+# uses its own generator seeded with (case seed, draw label, c), so chunks are independent and can
+# be filled by several threads; the result does not depend on the thread count.
+_CHUNK = 1 << 22
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even); return the bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    out = rounded.astype(np.uint16)
-    nan = np.isnan(x)
-    if nan.any():
-        out[nan] = BF16_NAN
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _bf16_into(x.reshape(-1), out.reshape(-1), np.empty(x.size, dtype=np.uint32))
     return out
 
 
-def normal_bf16(rng: np.random.Generator, count: int) -> np.ndarray:
-    """`count` N(0,1) draws rounded to bf16, as a flat uint16 array."""
+def _bf16_into(x: np.ndarray, out: np.ndarray, tmp: np.ndarray) -> None:
+    """bf16 rounding of float32 `x` into uint16 `out`, using uint32 scratch `tmp` (same length)."""
+    u = x.view(np.uint32)
+    np.right_shift(u, 16, out=tmp)
+    np.bitwise_and(tmp, 1, out=tmp)
+    np.add(tmp, 0x7FFF, out=tmp)
+    np.add(tmp, u, out=tmp)
+    np.right_shift(tmp, 16, out=tmp)
+    out[...] = tmp
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN
+
+
+def normal_bf16(seed: Sequence[int], label: int, count: int) -> np.ndarray:
+    """`count` N(0,1) draws rounded to bf16, as a flat uint16 array (see _CHUNK)."""
     out = np.empty(count, dtype=np.uint16)
-    for start in range(0, count, _CHUNK):
+    starts = list(range(0, count, _CHUNK))
+    local = threading.local()
+
+    def fill(ci: int) -> None:
+        if not hasattr(local, "f"):
+            local.f = np.empty(_CHUNK, dtype=np.float32)
+            local.u = np.empty(_CHUNK, dtype=np.uint32)
+        start = starts[ci]
         n = min(_CHUNK, count - start)
-        out[start:start + n] = bf16_bits(rng.standard_normal(n, dtype=np.float32))
+        g = np.random.default_rng([*seed, label, ci])
+        f = local.f[:n]
+        g.standard_normal(out=f, dtype=np.float32)
+        _bf16_into(f, out[start:start + n], local.u[:n])
+
+    if len(starts) <= 1:
+        for ci in range(len(starts)):
+            fill(ci)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(_THREADS, len(starts))) as ex:
+            list(ex.map(fill, range(len(starts))))
     return out
 
 
@@ -201,7 +234,8 @@ def _blocks_for(n_tokens: int, bs: int) -> int:
 
 
 def build_case(spec: Spec) -> Case:
-    """Generate one workload.  Draw order: block ids, queries, K pool, V pool, new K/V."""
+    """Generate one workload.  Block ids come from one generator seeded with the spec's seed;
+    queries, K pool, V pool and new K/V rows are separate labelled normal draws (labels 1..6)."""
     rng = np.random.default_rng(list(spec.seed))
     Hq, Hkv, D, bs = spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size
     dec_lens = [int(x) for x in spec.decode_lens]
@@ -254,11 +288,12 @@ def build_case(spec: Spec) -> Case:
     # --- draws ----------------------------------------------------------------------
     n_dec = len(dec_lens)
     total_q = sum(q for _, q in pre)
-    q_dec = normal_bf16(rng, n_dec * Hq * D).reshape(n_dec, Hq, D)
-    q_pre = normal_bf16(rng, total_q * Hq * D).reshape(total_q, Hq, D)
+    seed = tuple(spec.seed)
+    q_dec = normal_bf16(seed, 1, n_dec * Hq * D).reshape(n_dec, Hq, D)
+    q_pre = normal_bf16(seed, 2, total_q * Hq * D).reshape(total_q, Hq, D)
     elems = Hkv * bs * D
-    kc = normal_bf16(rng, num_blocks * elems).reshape(num_blocks, elems)
-    vc = normal_bf16(rng, num_blocks * elems).reshape(num_blocks, elems)
+    kc = normal_bf16(seed, 3, num_blocks * elems).reshape(num_blocks, elems)
+    vc = normal_bf16(seed, 4, num_blocks * elems).reshape(num_blocks, elems)
     kc[poison] = BF16_NAN
     vc[poison] = BF16_NAN
 
@@ -276,8 +311,8 @@ def build_case(spec: Spec) -> Case:
     if slots:
         T = len(slots)
         reshape = ReshapeBatch(
-            key=normal_bf16(rng, T * Hkv * D).reshape(T, Hkv, D),
-            value=normal_bf16(rng, T * Hkv * D).reshape(T, Hkv, D),
+            key=normal_bf16(seed, 5, T * Hkv * D).reshape(T, Hkv, D),
+            value=normal_bf16(seed, 6, T * Hkv * D).reshape(T, Hkv, D),
             slot_mapping=np.asarray(slots, dtype=np.int64),
         )
 

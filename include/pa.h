@@ -79,13 +79,16 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_
                                  int32_t block_size, int64_t num_blocks, void* stream);
 
 /*
- * Bytes of workspace pa_decode needs for this batch shape.  The workspace holds per-partition
- * partial softmax states of sequences longer than one partition; 0 means none is needed and
- * `workspace` may then be NULL.  It may be reused across calls on one stream and needs no
- * initialisation.  Calls that run concurrently on different streams need separate workspaces.
+ * Bytes of workspace pa_decode needs for this batch shape on the current device (0 if the shape is
+ * unsupported or num_seqs <= 0).  The workspace holds partial softmax states of sequences whose
+ * context is split over several waves and a counter that hands out work; it must be filled with
+ * zeros before its first use, and every pa_decode call leaves it ready for the next one (reuse it
+ * across calls on one stream).  Calls that may run concurrently (different streams) need
+ * separate workspaces.  The size depends on num_seqs, num_kv_heads, head_dim, the group size and
+ * the device, not on the lengths; max_seq_len is accepted for symmetry with pa_decode.
  */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_seq_len);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len);
 
 /*
  * pa_decode — one query token per sequence against that sequence's whole paged context.
@@ -97,19 +100,27 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *
  *   out            bf16 [num_seqs][num_q_heads][head_dim] (written; must not alias inputs)
  *   query          bf16 [num_seqs][num_q_heads][head_dim]
+ *   key_cache, value_cache  pools of num_blocks blocks (layout above)
+ *   num_blocks     blocks in each pool; table entries are clamped into [0, num_blocks) so a bad
+ *                  entry cannot read outside the pool (its result is then unspecified)
  *   block_tables   int32 [num_seqs][max_blocks_per_seq]; only the first ceil(L/block_size)
  *                  entries of a row are read
  *   seq_lens       int32 [num_seqs]; L = cached tokens including the query's own K/V
- *                  (0 <= L <= max_seq_len); L == 0 yields a zero output row
+ *                  (0 <= L <= max_seq_len; larger values are clamped to max_seq_len);
+ *                  L == 0 yields a zero output row
  *   max_seq_len    an upper bound of every seq_lens entry, known on the host
- *                  (<= max_blocks_per_seq*block_size); sizes the work grid and the workspace
- *   scale          softmax scale, normally 1/sqrt(head_dim)
- *   workspace      device buffer of at least pa_decode_workspace_bytes(...) bytes
- * Output is fp32-accumulated and rounded to bf16 (nearest even).  Supported: head_dim 64 with
- * group size <= 16, head_dim 128 with group <= 8, head_dim 256 with group <= 4.
+ *                  (<= max_blocks_per_seq*block_size)
+ *   scale          softmax scale (> 0), normally 1/sqrt(head_dim)
+ *   workspace      device buffer of at least pa_decode_workspace_bytes(...) bytes (never NULL
+ *                  when num_seqs > 0), zero-filled before its first use; a workspace that was
+ *                  not gives unspecified results (never an access outside the buffers)
+ * Output is fp32-accumulated and rounded to bf16 (nearest even); results are bitwise
+ * reproducible for the same inputs and do not depend on which physical blocks hold the context.
+ * Supported: head_dim 64 with group size <= 16, head_dim 128 with group <= 8, head_dim 256 with
+ * group <= 4; group sizes are powers of two.
  */
 pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
-                      const void* value_cache, const int32_t* block_tables,
+                      const void* value_cache, int64_t num_blocks, const int32_t* block_tables,
                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,

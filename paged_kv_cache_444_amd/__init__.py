@@ -44,8 +44,8 @@ _SIGNATURES = {
     "pa_version": (_I32, []),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_reshape_and_cache": (_I32, [_P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _P]),
-    "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
-    "pa_decode": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+    "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_decode": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                          ctypes.c_float, _P, _SZ, _P]),
     "pa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pa_prefill_chunk": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -123,8 +123,11 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
                                     head_dim, block_size, n, _stream()))
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int) -> int:
-    return int(load_library().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len))
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_seq_len: int) -> int:
+    """Workspace bytes pa_decode needs on the current device (0 for unsupported shapes)."""
+    return int(load_library().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                        max_seq_len))
 
 
 def prefill_workspace_bytes(num_seqs: int, total_q: int, num_q_heads: int, head_dim: int,
@@ -134,10 +137,12 @@ def prefill_workspace_bytes(num_seqs: int, total_q: int, num_q_heads: int, head_
 
 
 def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> tuple:
+    """Pointer and size of the workspace; a fresh one is zero-filled, as the library requires
+    before a workspace's first use (a caller-provided one must have been zeroed once)."""
     if nbytes == 0:
         return 0, 0
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     # A too-small workspace is passed through: the library reports PA_ERR_WORKSPACE.
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
@@ -158,9 +163,12 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
         max_seq_len = int(seq_lens.max().item()) if B else 0
     if out is None:
         out = torch.empty_like(query)
-    ws, ws_bytes = _workspace(decode_workspace_bytes(B, Hq, D, max_seq_len), workspace, query.device)
+    ws, ws_bytes = _workspace(decode_workspace_bytes(B, Hq, num_kv_heads, D, max_seq_len), workspace,
+                              query.device)
+    n = _num_blocks(key_cache, num_kv_heads, block_size, D)
     _check(lib.pa_decode(_bf16(out, "out"), _bf16(query, "query"), _bf16(key_cache, "key_cache"),
-                         _bf16(value_cache, "value_cache"), _ints(block_tables, torch.int32, "block_tables"),
+                         _bf16(value_cache, "value_cache"), n,
+                         _ints(block_tables, torch.int32, "block_tables"),
                          _ints(seq_lens, torch.int32, "seq_lens"), B, Hq, num_kv_heads, D, block_size,
                          block_tables.shape[1], max_seq_len, float(scale), ws, ws_bytes, _stream()))
     return out

@@ -1,303 +1,737 @@
-// Split-K paged decode attention for gfx950.
+// Paged decode attention for gfx950: one query token per sequence against its whole paged
+// context.
 //
-// One query token per sequence attends to the sequence's whole paged context ("Inference
-// optimization" lesson, Step 2 with one query row; decode re-reads the KV cache every step, which
-// makes it a bandwidth-bound matrix-vector product — same lesson, "Prefill vs decode", and the
-// vLLM-on-H100 article, "Decode is a memory problem").  No matrix cores: the contraction per KV
-// head is an [G x D] by [D x 16] product per 16-token step, far below the MFMA ridge.
+// What is computed: the attention of the "Inference optimization" lesson (Build it, Step 2:
+// attention with a KV cache) with a single query row, max-subtracted softmax(q·kᵀ·scale)·v, where
+// the sequence's keys and values are reached through its block table ("Serving engine internals"
+// lesson, PagedAttention section).  Decode re-reads the whole KV cache every step and does about
+// one multiply-add per byte per query head, so it is bound by HBM bandwidth ("Inference
+// optimization", Prefill vs decode; vLLM-on-H100 article, "Decode is a memory problem").  The
+// contraction therefore runs on the vector ALUs (v_dot2_f32_bf16) with DPP / swizzle reductions;
+// matrix cores would sit idle waiting for memory.
 //
-// Work unit: (sequence s, KV head h, partition p of `part` tokens).  A 256-thread workgroup (four
-// waves) owns one unit; the waves take the unit's 16-token steps round-robin.  Per step a wave
-// loads the step's K tile (16 tokens x D) and V tile (D x 16 tokens) with 16-byte loads, each
-// instruction covering 1 KiB of contiguous pool memory, and
-//   K side: lane l holds token l/4 and head-dim chunk l%4 of every 32-wide slice, so the G scores
-//           of a token are finished with two quad DPP adds;
-//   softmax: online (running max and sum) per octet of tokens — tokens 0..7 live in lanes 0..31,
-//           8..15 in lanes 32..63 — in the log2 domain;
-//   V side: lane l holds head-dim rows l%32 (+32k) for the 8 tokens of octet l/32, so P·V is
-//           v_dot2 over token pairs with the probabilities read back from LDS as bf16 pairs.
-// Each (wave, octet) keeps its own (m, l, acc) state; the eight states of a workgroup are merged
-// through LDS at the end.  A sequence that fits in one partition is written straight to the
-// output; otherwise the unit's state goes to the workspace and decode_merge combines partitions.
+// Work decomposition (balanced split-K).  A "step" is 16 tokens of one (sequence, KV head)
+// "unit"; units are numbered s * num_kv_heads + h and laid end to end.  The T steps of the whole
+// batch are cut into contiguous ranges ("virtual workers"): equal static ranges, one per resident
+// wave, optionally followed by small dynamic chunks that idle waves take from an atomic counter
+// (see Plan).  A wave keeps an online-softmax state (running max m, running sum l, accumulator
+// acc) per query head; when a worker's range ends or leaves a unit it finishes that piece: a unit
+// wholly inside one worker is normalised and written to the output; otherwise the piece's
+// (m, l, acc) goes to its partial slot (worker + unit, unique per piece) and decode_merge
+// combines the pieces of the unit in worker order.  Which wave runs which worker never changes
+// the arithmetic, so results are bitwise reproducible and independent of where blocks sit.
+//
+// Lane roles within a step (one 16-token sub-block of one physical block, one KV head; the pool
+// layout puts K as [D/32][16][32] and V as [D][16] inside the sub-block):
+//   K side: lane l holds tokens l/8 and 8 + l/8 and the head-dim slice [c*D/8, (c+1)*D/8),
+//           c = l % 8; the same slice of the G query rows stays in registers for the whole piece
+//           (G*D/16 registers, at most 64), and three DPP adds finish each score.
+//   softmax: online in the log2 domain with one running max per head for the whole wave; lane
+//           l computes the probabilities of its own head(s) c + 8j.  The max is only raised (and
+//           acc rescaled) when a score exceeds it by more than kRescaleSlack, which after the
+//           first step almost never happens.
+//   V side: lane l holds head-dim rows l%32 (+32k) of octet l/32, and P·V is v_dot2 over token
+//           pairs with the probabilities read back from LDS as bf16 pairs.
+// The next step's K and V are loaded into a second register set while the current step is
+// computed.
 
 #include "pa_device.h"
 #include "pa_internal.h"
 
 #include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
 
 namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// Fewer steps than this per wave would make partial slots outweigh the work.
+constexpr int kMinStepsPerWave = 8;
+// log2-domain slack before the running max is raised: probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.0f;
+// Dynamic chunks: batches of at most kMaxPrefixSeqs sequences keep their prefix sums in LDS; the
+// workspace holds kDynSlotsPerWorker chunk slots per worker wave.
+constexpr int kMaxPrefixSeqs = 4096;
+constexpr int kPrefixLdsBytes = (kMaxPrefixSeqs + 1) * 4;
+constexpr int kDynSlotsPerWorker = 2;
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
-  constexpr int R = D / kSlice;  // 16-byte K loads per lane per step, and V loads
-  const int part_idx = blockIdx.x;
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
+__device__ __forceinline__ int clamped_len(const DecodeParams& p, int s) {
+  return min(max(p.seq_lens[s], 0), p.len_cap);
+}
+
+__device__ __forceinline__ int steps_of(const DecodeParams& p, int s) {
+  return (clamped_len(p, s) + kSub - 1) / kSub;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
   const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-
-  const int L = min(max(p.seq_lens[s], 0), p.len_cap);
-  const int tok0 = part_idx * p.part_tokens;
-  const int Hq = p.num_q_heads;
-  if (tok0 >= L) {
-    if (part_idx == 0) {  // empty sequence: zero output
-      for (int i = threadIdx.x; i < G * D; i += kThreads)
-        p.out[((size_t)s * Hq + h * G) * D + i] = 0;
-    }
-    return;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  const int tok1 = min(L, tok0 + p.part_tokens);
-  const int nsteps = (tok1 - tok0 + kSub - 1) / kSub;
-  const int n_parts = (L + p.part_tokens - 1) / p.part_tokens;
+  return x;
+}
+
+// How the T steps of a call are split over "virtual workers".  Workers [0, ns) are static: worker
+// v takes steps [v*S/ns, (v+1)*S/ns) and runs on wave v.  Workers [ns, ns+nd) are dynamic chunks
+// of C steps covering [S, T), taken by whichever wave is free (an atomic counter hands them out).
+// Which wave runs a worker never changes what the worker computes, and every piece of work has a
+// fixed partial slot (worker + unit), so results do not depend on the dynamic order.
+struct Plan {
+  long long T, S, ns, C, nd;
+  __device__ long long start(long long v) const {
+    return v <= ns ? v * S / ns : min(T, S + (v - ns) * C);
+  }
+  __device__ long long owner(long long x) const {
+    return x < S ? ((x + 1) * ns - 1) / S : ns + (x - S) / C;
+  }
+};
+
+// K-side lane roles: lane l holds token 8p + l/8 of the step's two octets (p = 0, 1) and the
+// D/8 head-dim values [c*D/8, (c+1)*D/8) with c = l % 8; the 8 lanes of a token finish its scores
+// with three DPP adds.  V-side: lane l holds head-dim rows l%32 + 32x of octet l/32.
+template <int D>
+struct StepRegs {
+  uint4 k[2][D / 64];
+  uint4 v[D / kSlice];
+};
+
+// Query heads a lane computes probabilities for: heads c + 8j (j < kOwn) of the G sharing the
+// KV head, where c = lane % 8; for G < 8 only lanes with c < G own a head.
+template <int G>
+constexpr int kOwn = (G + 7) / 8;
+
+// Online-softmax state of one piece.  Scores are kept unscaled: m[g] is the running maximum of
+// raw scores of head g (the same in every lane), nmc = -m * scale * log2(e) (0 while m is -inf),
+// thr = m + slack / (scale * log2(e)).  The own_* copies hold those of the lane's own heads, l the
+// lane's partial sums of its own heads' probabilities.
+template <int D, int G>
+struct PieceState {
+  float m[G], nmc[G], thr[G];
+  float own_nmc[kOwn<G>], own_thr[kOwn<G>], l[kOwn<G>];
+  float acc[G][D / kSlice];
+};
+
+__device__ __forceinline__ float uniform_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+// Head owned by this lane in slot j, or -1.
+template <int G>
+__device__ __forceinline__ int own_head(int c, int j) {
+  const int g = c + 8 * j;
+  return g < G ? g : -1;
+}
+
+// Issue the loads of step i of the current unit.  `win`/`ids` hold up to 64 physical block ids
+// of the unit, one per lane, starting at logical block `win`.
+template <int D>
+__device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodeParams& p,
+                                          const int* bt, int blk_last, int& win, int& ids,
+                                          size_t head_off, size_t block_elems) {
+  constexpr int R = D / kSlice;
+  constexpr int DL = D / 8;  // head-dim values per K-side lane
+  const int lane = threadIdx.x & 63;
   const int bs = p.block_size;
-
-  __shared__ uint16_t p_lds[kWaves][2][G][8];
-  __shared__ float st_m[kWaves][2][G];
-  __shared__ float st_l[kWaves][2][G];
-  __shared__ float st_acc[kWaves][2][G][D];
-
-  // K-side and V-side lane roles.
-  const int kt = lane >> 2;   // token within the step
-  const int kj = lane & 3;    // 8-wide chunk within each 32-wide slice
-  const int vd = lane & 31;   // head-dim row (plus 32*k)
-  const int vo = lane >> 5;   // token octet
-
-  // Query of the G heads sharing KV head h, restricted to this lane's head-dim chunks.
-  uint4 q[G][R];
-  {
-    const uint16_t* qb = p.query + ((size_t)s * Hq + (size_t)h * G) * D + 8 * kj;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int r = 0; r < R; ++r) q[g][r] = *(const uint4*)(qb + g * D + r * kSlice);
+  const int t0 = i * kSub;
+  const int b = t0 >> (bs == 32 ? 5 : 4);
+  if (b - win >= 64) {  // rare: refill the block-id window
+    win = b;
+    const int id = (win + lane <= blk_last) ? bt[win + lane] : 0;
+    ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
-
-  // Physical ids of the unit's blocks, one per lane (a partition spans at most 64 blocks).
-  const int first_blk = tok0 / bs;
-  const int nblk = (tok1 - 1) / bs - first_blk + 1;
-  const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq + first_blk;
-  const int blk_id = lane < nblk ? bt[lane] : 0;
-
-  const size_t tile = (size_t)bs * D;                   // elements per (block, head)
-  const size_t block_elems = (size_t)p.num_kv_heads * tile;
-  const size_t head_off = (size_t)h * tile;
-
-  float m[G], l[G], acc[G][R];
+  const int id = __builtin_amdgcn_readlane(ids, b - win);
+  const size_t off = (size_t)id * block_elems + head_off + (size_t)(t0 & (bs - 1)) * D;
+  const uint16_t* kp = p.kpool + off;
+  const uint16_t* vp = p.vpool + off;
+  const int c = lane & 7, tt = lane >> 3;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.f;
+  for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[g][r] = 0.f;
-  }
+    for (int x = 0; x < D / 64; ++x) {
+      const int d = c * DL + 8 * x;
+      r.k[pp][x] = *(const uint4*)(kp + (d >> 5) * (kSub * kSlice) + (8 * pp + tt) * kSlice +
+                                   (d & 31));
+    }
+  const int vd = lane & 31, vo = lane >> 5;
+#pragma unroll
+  for (int x = 0; x < R; ++x) r.v[x] = *(const uint4*)(vp + (vd + 32 * x) * kSub + 8 * vo);
+}
 
-  for (int i = wave; i < nsteps; i += kWaves) {
-    const int t0 = tok0 + i * kSub;
-    const int id = __builtin_amdgcn_readlane(blk_id, t0 / bs - first_blk);
-    const size_t off = (size_t)id * block_elems + head_off + (size_t)((t0 % bs) / kSub) * kSub * D;
-    const uint16_t* kp = p.kpool + off;
-    const uint16_t* vp = p.vpool + off;
-    uint4 kr[R], vr[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) kr[r] = *(const uint4*)(kp + r * (kSub * kSlice) + 8 * lane);
-#pragma unroll
-    for (int k = 0; k < R; ++k) vr[k] = *(const uint4*)(vp + (vd + 32 * k) * kSub + 8 * vo);
+// One 16-token step: scores, online softmax, P·V.  nvalid = tokens of the step inside the piece
+// (>= 1); only the last step of a piece can have fewer than 16.
+template <int D, int G>
+__device__ __forceinline__ void compute_step(const StepRegs<D>& r, const uint4 (&q)[G][D / 64],
+                                             int nvalid, float c, float slack_raw,
+                                             uint16_t (*p_sh)[G][8], PieceState<D, G>& st) {
+  constexpr int R = D / kSlice;
+  constexpr int O = kOwn<G>;
+  const int lane = threadIdx.x & 63;
+  const int lc = lane & 7, tt = lane >> 3;
+  const int vo = lane >> 5;
+  const bool tail = nvalid < kSub;  // wave-uniform
 
-    // Scores of token kt for the G heads.
-    float sc[G];
+  // Raw scores q·k of tokens tt and 8 + tt for every head.
+  float sc[2][G];
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float a = 0.f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) a = dot8(q[g][r], kr[r], a);
+      for (int x = 0; x < D / 64; ++x) a = dot8(q[g][x], r.k[pp][x], a);
       a += dpp_f32<kDppQuadXor1>(a);
       a += dpp_f32<kDppQuadXor2>(a);
-      sc[g] = a;
+      a += dpp_f32<kDppRowHalfMirror>(a);
+      sc[pp][g] = a;
     }
-    const int nvalid = tok1 - t0;  // tokens of this step inside the unit (>= 1)
-    const bool tail = nvalid < kSub;
+  if (tail) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) sc[g] = (kt < nvalid) ? sc[g] * p.scale_log2 : kNegInf;
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+      for (int g = 0; g < G; ++g) sc[pp][g] = (8 * pp + tt < nvalid) ? sc[pp][g] : kNegInf;
+  }
+  float own[2][O];
+#pragma unroll
+  for (int j = 0; j < O; ++j) {
+    const int mine = own_head<G>(lc, j);
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      float v = kNegInf;
+#pragma unroll
+      for (int g = 0; g < G; ++g) v = (g == mine) ? sc[pp][g] : v;
+      own[pp][j] = v;
+    }
+  }
 
-    // Online softmax per octet.
-    float alpha[G], pr[G];
+  // The running max is raised only when some score exceeds it by the slack; otherwise the
+  // probabilities below stay under 2^slack and nothing is rescaled.
+  bool raise = false;
+#pragma unroll
+  for (int j = 0; j < O; ++j) raise |= fmaxf(own[0][j], own[1][j]) > st.own_thr[j];
+  if (__ballot(raise)) {
+    float alpha[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float x = sc[g];
-      x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
+      float x = fmaxf(sc[0][g], sc[1][g]);
       x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
       x = fmaxf(x, xor16_f32(x));
-      const float mn = fmaxf(m[g], x);
-      const float ms = (mn == kNegInf) ? 0.f : mn;
-      alpha[g] = fast_exp2(m[g] - ms);
-      pr[g] = fast_exp2(sc[g] - ms);
-      m[g] = mn;
-      l[g] = l[g] * alpha[g] + pr[g];
-    }
-    if (kj == 0) {
+      x = fmaxf(x, __shfl_xor(x, 32, 64));
+      const float mn = uniform_f(fmaxf(st.m[g], x));
+      alpha[g] = 1.f;
+      if (mn != kNegInf && mn != st.m[g]) {
+        alpha[g] = fast_exp2((st.m[g] - mn) * c);  // 0 when the old max is -inf
 #pragma unroll
-      for (int g = 0; g < G; ++g) p_lds[wave][kt >> 3][g][kt & 7] = to_bf16(pr[g]);
-    }
-    wave_lds_sync();
-
-    if (tail) {  // zero V of tokens past the end: 0 * NaN must not reach the accumulators
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        uint32_t w[4] = {vr[k].x, vr[k].y, vr[k].z, vr[k].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int u = 8 * vo + 2 * e;
-          if (u >= nvalid) w[e] = 0u;
-          else if (u + 1 >= nvalid) w[e] &= 0xFFFFu;
-        }
-        vr[k] = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int y = 0; y < R; ++y) st.acc[g][y] *= alpha[g];
+        st.m[g] = mn;
+        st.nmc[g] = -mn * c;
+        st.thr[g] = mn + slack_raw;
       }
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint4 pp = *(const uint4*)&p_lds[wave][vo][g][0];
+    for (int j = 0; j < O; ++j) {
+      const int mine = own_head<G>(lc, j);
+      float a = 1.f, n = 0.f, t = kNegInf;
 #pragma unroll
-      for (int k = 0; k < R; ++k) acc[g][k] = dot8(pp, vr[k], acc[g][k] * alpha[g]);
+      for (int g = 0; g < G; ++g) {
+        a = (g == mine) ? alpha[g] : a;
+        n = (g == mine) ? st.nmc[g] : n;
+        t = (g == mine) ? st.thr[g] : t;
+      }
+      st.l[j] *= a;
+      st.own_nmc[j] = n;
+      st.own_thr[j] = (mine < 0) ? __builtin_inff() : t;
     }
-    wave_lds_sync();
   }
+#pragma unroll
+  for (int j = 0; j < O; ++j) {
+    const int mine = own_head<G>(lc, j);
+    const float p0 = fast_exp2(__builtin_fmaf(own[0][j], c, st.own_nmc[j]));
+    const float p1 = fast_exp2(__builtin_fmaf(own[1][j], c, st.own_nmc[j]));
+    st.l[j] += p0 + p1;
+    if (mine >= 0) {
+      p_sh[0][mine][tt] = to_bf16(p0);
+      p_sh[1][mine][tt] = to_bf16(p1);
+    }
+  }
+  wave_lds_sync();
 
-  // Sum l over the quads of each octet (every lane of a quad holds the same partial).
+  uint4 v[R];
+#pragma unroll
+  for (int x = 0; x < R; ++x) v[x] = r.v[x];
+  if (tail) {  // zero V of tokens past the end: 0 * NaN must not reach acc
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 8 * vo + 2 * e;
+      const uint32_t keep = (t + 1 < nvalid) ? 0xFFFFFFFFu : ((t < nvalid) ? 0xFFFFu : 0u);
+#pragma unroll
+      for (int x = 0; x < R; ++x) {
+        if (e == 0) v[x].x &= keep;
+        if (e == 1) v[x].y &= keep;
+        if (e == 2) v[x].z &= keep;
+        if (e == 3) v[x].w &= keep;
+      }
+    }
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float x = l[g];
-    x += dpp_f32<kDppRowRor4>(x);
-    x += dpp_f32<kDppRowRor8>(x);
-    x += xor16_f32(x);
-    l[g] = x;
-  }
-  if (vd == 0) {
+    const uint4 pp = *(const uint4*)&p_sh[vo][g][0];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      st_m[wave][vo][g] = m[g];
-      st_l[wave][vo][g] = l[g];
+    for (int x = 0; x < R; ++x) st.acc[g][x] = dot8(pp, v[x], st.acc[g][x]);
+  }
+  wave_lds_sync();
+}
+
+// Steps j0 .. j0+take-1 of unit (s, h) by virtual worker w.  x is the global index of step j0.
+// Depth is the number of steps whose loads are in flight while one step is computed.
+template <int D, int G, int Depth>
+__device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h, int j0, int take,
+                                             int n_s, long long w, long long x, const Plan& plan,
+                                             uint16_t (*p_sh)[G][8]) {
+  constexpr int R = D / kSlice;
+  constexpr int O = kOwn<G>;
+  const int lane = threadIdx.x & 63;
+  const int lc = lane & 7;
+  const int Hq = p.num_q_heads;
+  const int L = uniform(clamped_len(p, s));
+  const int u = s * p.num_kv_heads + h;
+  const bool whole = (j0 == 0) && (take == n_s);
+  if (j0 == 0 && lane == 0) p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1));
+
+  // This lane's head-dim slice of the G query rows sharing KV head h.
+  uint4 q[G][D / 64];
+  {
+    const uint16_t* qg = p.query + ((size_t)s * Hq + (size_t)h * G) * D + lc * (D / 8);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int y = 0; y < D / 64; ++y) q[g][y] = *(const uint4*)(qg + g * D + 8 * y);
+  }
+
+  const int bs = p.block_size;
+  const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int tok_end = min(L, (j0 + take) * kSub);
+  const int blk_last = (tok_end - 1) / bs;
+  int win = (j0 * kSub) / bs;
+  int ids;
+  {
+    const int id = (win + lane <= blk_last) ? bt[win + lane] : 0;
+    ids = min(max(id, 0), (int)(p.num_blocks - 1));
+  }
+  const size_t tile = (size_t)bs * D;
+  const size_t block_elems = (size_t)p.num_kv_heads * tile;
+  const size_t head_off = (size_t)h * tile;
+
+  PieceState<D, G> st;
+  const float c = p.scale_log2;
+  const float slack_raw = kRescaleSlack / c;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.m[g] = kNegInf;
+    st.nmc[g] = 0.f;
+    st.thr[g] = kNegInf;
+#pragma unroll
+    for (int y = 0; y < R; ++y) st.acc[g][y] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < O; ++j) {
+    st.own_nmc[j] = 0.f;
+    st.own_thr[j] = own_head<G>(lc, j) >= 0 ? kNegInf : __builtin_inff();
+    st.l[j] = 0.f;
+  }
+
+  // Prefetch loads are issued unconditionally (past the last step they repeat the last step's
+  // addresses, which hit in cache): a load issued on only some paths would make the compiler wait
+  // for every outstanding load before each step.
+  const int iend = j0 + take;
+  const int ilast = iend - 1;
+  int i = j0;
+  if constexpr (Depth == 0) {  // no prefetch: fewer registers, more resident waves
+    while (true) {
+      StepRegs<D> ra;
+      load_step<D>(ra, i, p, bt, blk_last, win, ids, head_off, block_elems);
+      compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      if (++i >= iend) break;
+    }
+  } else if constexpr (Depth == 1) {
+    StepRegs<D> ra, rb;
+    load_step<D>(ra, i, p, bt, blk_last, win, ids, head_off, block_elems);
+    while (true) {
+      load_step<D>(rb, min(i + 1, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      if (++i >= iend) break;
+      load_step<D>(ra, min(i + 1, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      compute_step<D, G>(rb, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      if (++i >= iend) break;
+    }
+  } else {  // two steps in flight while one is computed
+    StepRegs<D> r0, r1, r2;
+    load_step<D>(r0, i, p, bt, blk_last, win, ids, head_off, block_elems);
+    load_step<D>(r1, min(i + 1, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+    while (true) {
+      load_step<D>(r2, min(i + 2, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      compute_step<D, G>(r0, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      if (++i >= iend) break;
+      load_step<D>(r0, min(i + 2, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      compute_step<D, G>(r1, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      if (++i >= iend) break;
+      load_step<D>(r1, min(i + 2, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      compute_step<D, G>(r2, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      if (++i >= iend) break;
     }
   }
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int k = 0; k < R; ++k) st_acc[wave][vo][g][vd + 32 * k] = acc[g][k];
-  __syncthreads();
 
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int g = idx / D, d = idx % D;
-    float M = kNegInf;
+  // Finish the piece.  l: sum each own head's partial over the eight token groups; lane g % 8
+  // then holds head g's total.  acc: both octet halves share m, so they simply add.
+  const int vd = lane & 31, vo = lane >> 5;
+  float lsum[O];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+  for (int j = 0; j < O; ++j) {
+    float y = st.l[j];
+    y += dpp_f32<kDppRowRor8>(y);
+    y += xor16_f32(y);
+    y += __shfl_xor(y, 32, 64);
+    lsum[j] = y;
+  }
+  float* slot = p.partials + (size_t)(w + u) * (G * (2 + D));
+  uint16_t* orow = p.out + ((size_t)s * Hq + (size_t)h * G) * D;
 #pragma unroll
-      for (int o = 0; o < 2; ++o) M = fmaxf(M, st_m[w][o][g]);
-    const float Ms = (M == kNegInf) ? 0.f : M;
-    float Lt = 0.f, A = 0.f;
+  for (int g = 0; g < G; ++g) {
+    const float lt = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lsum[g / 8]), g % 8));
+    if (!whole && lane == 0) {
+      slot[g] = st.m[g] * c;  // the merge works in the log2 domain
+      slot[G + g] = lt;
+    }
+    // Half 0 finishes rows vd + 32k for k < R/2, half 1 the rest; each sends the other half's.
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-      for (int o = 0; o < 2; ++o) {
-        const float c = fast_exp2(st_m[w][o][g] - Ms);
-        Lt += st_l[w][o][g] * c;
-        A += st_acc[w][o][g][d] * c;
-      }
-    const size_t row = (size_t)s * Hq + (size_t)h * G + g;
-    if (n_parts == 1) {
-      p.out[row * D + d] = to_bf16(Lt > 0.f ? A / Lt : 0.f);
-    } else {
-      const size_t u = row * p.max_parts + part_idx;
-      p.ws_acc[u * D + d] = A;
-      if (d == 0) {
-        p.ws_ml[2 * u] = M;
-        p.ws_ml[2 * u + 1] = Lt;
-      }
+    for (int k = 0; k < R / 2; ++k) {
+      const float mine = vo ? st.acc[g][k + R / 2] : st.acc[g][k];
+      const float send = vo ? st.acc[g][k] : st.acc[g][k + R / 2];
+      const float a = mine + __shfl_xor(send, 32, 64);
+      const int d = vd + 32 * (k + (vo ? R / 2 : 0));
+      if (whole) orow[g * D + d] = to_bf16(a / lt);
+      else slot[2 * G + g * D + d] = a;
     }
   }
 }
 
-// Combine the partitions of each (sequence, query head): rescale every partition's partial sums
-// to the common maximum and divide once.
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-  constexpr int HPB = 256 / D;  // heads per block
-  const int s = blockIdx.x;
-  const int hq = blockIdx.y * HPB + threadIdx.x / D;
-  const int d = threadIdx.x % D;
-  if (hq >= p.num_q_heads) return;
-  const int L = min(max(p.seq_lens[s], 0), p.len_cap);
-  const int n_parts = (L + p.part_tokens - 1) / p.part_tokens;
-  if (n_parts <= 1) return;  // written directly by the partition kernel
-  const size_t row = (size_t)s * p.num_q_heads + hq;
-  const float* ml = p.ws_ml + 2 * row * p.max_parts;
-  const float* acc = p.ws_acc + row * p.max_parts * D + d;
-  float M = kNegInf;
-  for (int j = 0; j < n_parts; ++j) M = fmaxf(M, ml[2 * j]);
-  float Lt = 0.f, A = 0.f;
-  for (int j = 0; j < n_parts; ++j) {
-    const float c = fast_exp2(ml[2 * j] - M);
-    Lt += ml[2 * j + 1] * c;
-    A += acc[(size_t)j * D] * c;
+// Steps of virtual worker v, unit by unit.  (s, off) locate its first step: sequence s and offset
+// within that sequence's num_kv_heads * n_s steps.
+template <int D, int G, int Depth>
+__device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& plan, long long v,
+                                           int s, long long off, uint16_t (*p_sh)[G][8]) {
+  const int B = p.num_seqs, Hkv = p.num_kv_heads;
+  long long x = plan.start(v);
+  const long long x1 = plan.start(v + 1);
+  if (x >= x1 || s < 0 || s >= B) return;
+  int n_s = steps_of(p, s);
+  if (n_s == 0) return;  // unreachable: every step lies in a sequence with steps
+  int h = (int)(off / n_s);
+  int j = (int)(off % n_s);
+  while (true) {
+    const int take = (int)min((long long)(n_s - j), x1 - x);
+    decode_piece<D, G, Depth>(p, s, h, j, take, n_s, v, x, plan, p_sh);
+    x += take;
+    if (x >= x1) break;
+    j = 0;
+    if (++h == Hkv) {
+      h = 0;
+      do {
+        ++s;
+        n_s = (s < B) ? steps_of(p, s) : 0;
+      } while (s < B && n_s == 0);
+      if (s >= B) break;
+    }
   }
-  p.out[row * D + d] = to_bf16(A / Lt);
+}
+
+template <int D, int G, int Depth>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int B = p.num_seqs;
+  const int Hkv = p.num_kv_heads;
+
+  __shared__ long long sh_sum[kWaves];
+  __shared__ int sh_scan[kWaves];
+  __shared__ int sh_start_s[kWaves];
+  __shared__ long long sh_start_off[kWaves];
+  __shared__ __attribute__((aligned(16))) uint16_t p_lds[kWaves][2][G][8];
+  extern __shared__ int seq_prefix[];  // [B+1] steps per KV head before each sequence (dynamic mode)
+
+  // Total steps of the batch.
+  long long mine = 0;
+  for (int s = threadIdx.x; s < B; s += kThreads) mine += steps_of(p, s);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  if (lane == 0) sh_sum[wave] = mine;
+  if (threadIdx.x < kWaves) sh_start_s[threadIdx.x] = -1;
+  __syncthreads();
+  long long per_head = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) per_head += sh_sum[k];
+  Plan plan;
+  plan.T = per_head * Hkv;
+  if (plan.T == 0) return;  // block-uniform
+  plan.ns = min((long long)p.num_workers, (plan.T + kMinStepsPerWave - 1) / kMinStepsPerWave);
+  const bool dynamic = p.dyn_cap > 0 && plan.ns == p.num_workers;
+  if (dynamic) {
+    plan.S = max(plan.ns, plan.T * p.static_frac_q10 / 1024);
+    const long long rest = plan.T - plan.S;
+    plan.C = max((long long)p.chunk_steps, (rest + p.dyn_cap - 1) / p.dyn_cap);
+    plan.nd = (rest + plan.C - 1) / plan.C;
+  } else {
+    plan.S = plan.T;
+    plan.C = 1;
+    plan.nd = 0;
+  }
+  const long long wbase = (long long)blockIdx.x * kWaves;
+
+  // Prefix sums over sequences: locate where each static worker of this block starts, and keep
+  // the prefix in LDS for the dynamic chunks.
+  long long base = 0;
+  for (int c = 0; c < B; c += kThreads) {
+    const int s = c + threadIdx.x;
+    const int n = s < B ? steps_of(p, s) : 0;
+    const int incl = wave_inclusive_scan(n);
+    if (lane == 63) sh_scan[wave] = incl;
+    __syncthreads();
+    int before = 0, chunk = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      before += (k < wave) ? sh_scan[k] : 0;
+      chunk += sh_scan[k];
+    }
+    const long long excl = base + before + incl - n;
+    if (dynamic && s < B) seq_prefix[s] = (int)excl;
+    const long long lo = excl * Hkv;
+    const long long hi = (excl + n) * Hkv;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const long long wk = wbase + k;
+      const long long x0 = plan.start(wk);
+      if (wk < plan.ns && x0 >= lo && x0 < hi) {
+        sh_start_s[k] = s;
+        sh_start_off[k] = x0 - lo;
+      }
+    }
+    base += chunk;
+    __syncthreads();
+  }
+  if (dynamic && threadIdx.x == 0) seq_prefix[B] = (int)base;
+  __syncthreads();
+
+  const long long w = wbase + wave;
+  if (w >= plan.ns) return;  // no barriers below
+  run_worker<D, G, Depth>(p, plan, w, sh_start_s[wave], sh_start_off[wave], p_lds[wave]);
+  if (!dynamic) return;
+  while (true) {
+    unsigned d = 0;
+    if (lane == 0) d = atomicAdd(p.counter, 1u);
+    d = (unsigned)__shfl((int)d, 0, 64);
+    if ((long long)d >= plan.nd) break;
+    // Locate the chunk's first step: the last sequence whose prefix is <= x / Hkv.
+    const long long x0 = plan.start(plan.ns + d);
+    const long long xh = x0 / Hkv;
+    int lo = 0, hi = B;  // invariant: seq_prefix[lo] <= xh < seq_prefix[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seq_prefix[mid] <= xh) lo = mid;
+      else hi = mid;
+    }
+    run_worker<D, G, Depth>(p, plan, plan.ns + d, lo, x0 - (long long)seq_prefix[lo] * Hkv,
+                            p_lds[wave]);
+  }
+}
+
+// Combine the pieces of every unit that spans several waves; write zeros for empty sequences.
+// One pass over the pieces with an online rescale; each thread owns up to four outputs, whose
+// loads for one piece are independent of each other.
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
+  constexpr int PER = (G * D + 255) / 256;
+  const int u = blockIdx.x;
+  const int s = u / p.num_kv_heads;
+  const int h = u % p.num_kv_heads;
+  if (u == 0 && threadIdx.x == 0) *p.counter = 0u;  // ready for the next call
+  uint16_t* orow = p.out + ((size_t)s * p.num_q_heads + (size_t)h * G) * D;
+  if (clamped_len(p, s) == 0) {
+    for (int i = threadIdx.x; i < G * D; i += 256) orow[i] = 0;
+    return;
+  }
+  int2 info = p.unit_info[u];
+  info.x = max(info.x, 0);
+  info.y = min(info.y, p.num_workers + p.dyn_cap - 1);
+  if (info.x >= info.y) return;  // written by its only wave
+  float M[PER], lt[PER], a[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    M[k] = kNegInf;
+    lt[k] = 0.f;
+    a[k] = 0.f;
+  }
+  for (int w = info.x; w <= info.y; ++w) {
+    const float* slot = p.partials + (size_t)(w + u) * (G * (2 + D));
+    float mv[PER], lv[PER], av[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      const int g = min(i, G * D - 1) / D;
+      mv[k] = slot[g];
+      lv[k] = slot[G + g];
+      av[k] = slot[2 * G + min(i, G * D - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const float mn = fmaxf(M[k], mv[k]);
+      const float c_old = fast_exp2(M[k] - mn);  // M = -inf on the first piece: c_old = 0
+      const float c_new = fast_exp2(mv[k] - mn);
+      lt[k] = lt[k] * c_old + lv[k] * c_new;
+      a[k] = a[k] * c_old + av[k] * c_new;
+      M[k] = mn;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < G * D) orow[i] = to_bf16(a[k] / lt[k]);
+  }
+}
+
+// Prefetch depth of the decode kernel: PA_DECODE_PREFETCH=0, 1 or 2 (default 1).
+int prefetch_depth() {
+  const char* e = std::getenv("PA_DECODE_PREFETCH");
+  const int v = e ? std::atoi(e) : 1;
+  return (v == 0 || v == 2) ? v : 1;
+}
+
+template <int D, int G>
+const void* kernel_ptr() {
+  switch (prefetch_depth()) {
+    case 0: return reinterpret_cast<const void*>(&decode_kernel<D, G, 0>);
+    case 1: return reinterpret_cast<const void*>(&decode_kernel<D, G, 1>);
+    default: return reinterpret_cast<const void*>(&decode_kernel<D, G, 2>);
+  }
 }
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
   {
     TraceScope t("decode_partition", stream);
-    dim3 grid(p.max_parts, p.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<D, G>), grid, dim3(kThreads), 0, stream, p);
+    const dim3 grid(p.num_workers / kWaves), block(kThreads);
+    const size_t lds = p.dyn_cap > 0 ? (size_t)(p.num_seqs + 1) * 4 : 0;
+    switch (prefetch_depth()) {
+      case 0: hipLaunchKernelGGL((decode_kernel<D, G, 0>), grid, block, lds, stream, p); break;
+      case 1: hipLaunchKernelGGL((decode_kernel<D, G, 1>), grid, block, lds, stream, p); break;
+      default: hipLaunchKernelGGL((decode_kernel<D, G, 2>), grid, block, lds, stream, p); break;
+    }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.max_parts <= 1) return e;
+  if (e != hipSuccess) return e;
   {
     TraceScope t("decode_merge", stream);
-    constexpr int HPB = 256 / D;
-    dim3 grid(p.num_seqs, (p.num_q_heads + HPB - 1) / HPB);
-    hipLaunchKernelGGL((decode_merge_kernel<D>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(p.num_seqs * p.num_kv_heads), dim3(256),
+                       0, stream, p);
   }
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const DecodeParams& p, int G, hipStream_t stream) {
-  switch (G) {
-    case 1: return launch_dg<D, 1>(p, stream);
-    case 2: return launch_dg<D, 2>(p, stream);
-    case 4: return launch_dg<D, 4>(p, stream);
-    case 8: if constexpr (D <= 128) return launch_dg<D, 8>(p, stream); break;
-    case 16: if constexpr (D <= 64) return launch_dg<D, 16>(p, stream); break;
-    default: break;
+// Dispatch over the supported (head_dim, group) pairs; `fallback` for any other pair.
+template <typename Ret, typename F>
+Ret dispatch(int D, int G, Ret fallback, F&& f) {
+  switch (D) {
+    case 64:
+      switch (G) {
+        case 1: return f.template operator()<64, 1>();
+        case 2: return f.template operator()<64, 2>();
+        case 4: return f.template operator()<64, 4>();
+        case 8: return f.template operator()<64, 8>();
+        case 16: return f.template operator()<64, 16>();
+      }
+      break;
+    case 128:
+      switch (G) {
+        case 1: return f.template operator()<128, 1>();
+        case 2: return f.template operator()<128, 2>();
+        case 4: return f.template operator()<128, 4>();
+        case 8: return f.template operator()<128, 8>();
+      }
+      break;
+    case 256:
+      switch (G) {
+        case 1: return f.template operator()<256, 1>();
+        case 2: return f.template operator()<256, 2>();
+        case 4: return f.template operator()<256, 4>();
+      }
+      break;
   }
-  return hipErrorInvalidValue;
+  return fallback;
 }
 
 }  // namespace
 
-int decode_partition_tokens() {
-  static const int part = [] {
-    int v = 512;
-    if (const char* e = std::getenv("PA_DECODE_PART")) {
-      const int x = std::atoi(e);
-      if (x >= 64 && x <= 1024 && x % 32 == 0) v = x;
+int decode_workers(int head_dim, int group) {
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, int> cache;  // (device, variant) -> resident workgroups
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int blocks = 0;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    const auto key = std::make_pair(dev, (head_dim * 64 + group) * 4 + prefetch_depth());
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      blocks = it->second;
+    } else {
+      int cus = 0, per_cu = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+      const void* fn = dispatch(head_dim, group, (const void*)nullptr,
+                                []<int D, int G>() { return kernel_ptr<D, G>(); });
+      if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads,
+                                                              kPrefixLdsBytes) != hipSuccess)
+        return 0;
+      blocks = cus * std::max(per_cu, 1);
+      cache[key] = blocks;
     }
-    return v;
-  }();
-  return part;
+  }
+  // Tuning and test override, read on every call: the total number of worker waves.
+  if (const char* e = std::getenv("PA_DECODE_WORKERS")) {
+    const int v = std::atoi(e);
+    if (v >= kWaves) return std::min(v / kWaves, blocks) * kWaves;
+  }
+  return blocks * kWaves;
+}
+
+DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group) {
+  DecodeWorkspace ws{};
+  ws.workers = decode_workers(head_dim, group);
+  if (ws.workers <= 0 || num_seqs <= 0) return ws;
+  // Dynamic chunks need the per-sequence prefix in LDS: batches up to kMaxPrefixSeqs.
+  ws.dyn_cap = num_seqs <= kMaxPrefixSeqs ? kDynSlotsPerWorker * ws.workers : 0;
+  const size_t units = (size_t)num_seqs * num_kv_heads;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  ws.counter_off = 0;
+  ws.info_off = 256;
+  ws.partials_off = ws.info_off + up(units * sizeof(int2));
+  ws.bytes = ws.partials_off +
+             ((size_t)ws.workers + ws.dyn_cap + units) * group * (2 + head_dim) * sizeof(float);
+  return ws;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  if (p.num_workers < kWaves || p.num_workers % kWaves) return hipErrorInvalidConfiguration;
+  if (p.dyn_cap > 0 && (p.num_seqs > kMaxPrefixSeqs || p.chunk_steps < 1 ||
+                        p.static_frac_q10 < 512 || p.static_frac_q10 > 1024))
+    return hipErrorInvalidConfiguration;
   const int G = p.num_q_heads / p.num_kv_heads;
-  switch (p.head_dim) {
-    case 64: return launch_d<64>(p, G, stream);
-    case 128: return launch_d<128>(p, G, stream);
-    case 256: return launch_d<256>(p, G, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return dispatch(p.head_dim, G, hipErrorInvalidValue,
+                  [&]<int D, int GG>() { return launch_dg<D, GG>(p, stream); });
 }
 
 }  // namespace pa

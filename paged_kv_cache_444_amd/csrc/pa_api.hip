@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -72,7 +73,8 @@ pa_status_t check_attention_shape(int32_t num_q_heads, int32_t num_kv_heads, int
   if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_seq*block_size %lld",
                 max_seq_len, (long long)max_blocks_per_seq * block_size);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "scale must be finite and positive");
   return PA_OK;
 }
 
@@ -192,18 +194,29 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_
   return hip_status(pa::launch_reshape(p, static_cast<hipStream_t>(stream)), "reshape_and_cache");
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_seq_len) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
-  const int part = pa::decode_partition_tokens();
-  const size_t P = (size_t)((max_seq_len + part - 1) / part);
-  if (P <= 1) return 0;
-  const size_t rows = (size_t)num_seqs * num_q_heads * P;
-  return align_up(rows * 2 * sizeof(float), 256) + rows * head_dim * sizeof(float);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len) {
+  (void)max_seq_len;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return 0;
+  const int g = num_q_heads / num_kv_heads;
+  if (!supported_head_dim(head_dim) || !supported_group(g, head_dim)) return 0;
+  return pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g).bytes;
 }
 
+namespace {
+// Decode tunables, read on every call (for sweeps): share of the steps split statically and the
+// smallest dynamic chunk.
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* e = std::getenv(name);
+  if (!e) return dflt;
+  const int v = std::atoi(e);
+  return (v >= lo && v <= hi) ? v : dflt;
+}
+}  // namespace
+
 pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
-                      const void* value_cache, const int32_t* block_tables,
+                      const void* value_cache, int64_t num_blocks, const int32_t* block_tables,
                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
@@ -212,6 +225,8 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
   pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
                                          max_blocks_per_seq, max_seq_len, scale);
   if (st != PA_OK) return st;
+  if (num_blocks <= 0 || num_blocks > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks %lld out of range", (long long)num_blocks);
   if (num_seqs == 0) return ok();
   if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens)
     return fail(PA_ERR_NULL_POINTER, "null pointer argument");
@@ -219,13 +234,15 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
       !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4))
     return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for bf16 arrays)");
   if (out == query) return fail(PA_ERR_INVALID_ARG, "out must not alias query");
-  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
-  if (need > 0 && !aligned(workspace, 16))
-    return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const int g = num_q_heads / num_kv_heads;
+  const pa::DecodeWorkspace wl = pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g);
+  if (wl.workers <= 0)
+    return fail(PA_ERR_HIP, "cannot query the device for the decode launch shape");
+  if (!workspace || workspace_bytes < wl.bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                wl.bytes);
+  if (!aligned(workspace, 16)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
 
-  const int part = pa::decode_partition_tokens();
   pa::DecodeParams p{};
   p.out = static_cast<uint16_t*>(out);
   p.query = static_cast<const uint16_t*>(query);
@@ -233,23 +250,23 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
   p.vpool = static_cast<const uint16_t*>(value_cache);
   p.block_tables = block_tables;
   p.seq_lens = seq_lens;
+  p.num_blocks = num_blocks;
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.head_dim = head_dim;
   p.block_size = block_size;
   p.max_blocks_per_seq = max_blocks_per_seq;
-  p.part_tokens = part;
-  p.max_parts = max_seq_len > 0 ? (max_seq_len + part - 1) / part : 1;
-  p.len_cap = (int)std::min<int64_t>((int64_t)p.max_parts * part,
-                                     (int64_t)max_blocks_per_seq * block_size);
+  p.num_workers = wl.workers;
+  p.dyn_cap = wl.dyn_cap;
+  p.chunk_steps = env_int("PA_DECODE_CHUNK", 4, 1, 256);
+  p.static_frac_q10 = env_int("PA_DECODE_STATIC_Q10", 1024, 512, 1024);
+  p.len_cap = max_seq_len;
   p.scale_log2 = scale * 1.4426950408889634f;
-  if (need > 0) {
-    const size_t rows = (size_t)num_seqs * num_q_heads * p.max_parts;
-    p.ws_ml = static_cast<float*>(workspace);
-    p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        align_up(rows * 2 * sizeof(float), 256));
-  }
+  char* base = static_cast<char*>(workspace);
+  p.counter = reinterpret_cast<unsigned*>(base + wl.counter_off);
+  p.unit_info = reinterpret_cast<int2*>(base + wl.info_off);
+  p.partials = reinterpret_cast<float*>(base + wl.partials_off);
   return hip_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)), "decode");
 }
 

@@ -21,6 +21,7 @@ constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowHalfMirror = 0x141;  // lane i of each 8-lane half-row reads lane 7 - i
 
 template <int Ctrl>
 __device__ __forceinline__ float dpp_f32(float x) {

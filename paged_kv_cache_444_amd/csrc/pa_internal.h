@@ -7,10 +7,11 @@
 
 namespace pa {
 
-// Tokens of one sequence handled by one decode work unit (a "partition").  A multiple of 32 so
-// partitions start on block boundaries for both block sizes; at most 64 blocks per partition.
-int decode_partition_tokens();
-
+// Decode work is cut into "steps" of 16 tokens of one (sequence, KV head) pair.  The pairs
+// ("units", numbered s*num_kv_heads + h) are laid end to end and every worker wave takes an equal
+// contiguous range of the concatenated steps, so the load is balanced whatever the length mix.
+// A unit finished inside one wave is written to the output directly; the pieces of a unit that
+// spans several waves go to per-piece partial slots and decode_merge combines them.
 struct DecodeParams {
   uint16_t* out;
   const uint16_t* query;
@@ -18,16 +19,29 @@ struct DecodeParams {
   const uint16_t* vpool;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* ws_ml;   // [B][Hq][P] (m, l) pairs
-  float* ws_acc;  // [B][Hq][P][D]
+  unsigned* counter;  // dynamic chunks handed out so far; zero between calls
+  int2* unit_info;    // [num_seqs*num_kv_heads] (first worker, last worker) of each unit
+  float* partials;    // [num_workers + dyn_cap + units][G][2 + D]: m[G], l[G], acc[G][D]
+  int64_t num_blocks;
   int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
-  int part_tokens, max_parts;
-  // Lengths are clamped to this (min of max_parts*part_tokens and the table width) so a length
-  // beyond the caller's bound cannot take a kernel outside the table or the workspace.
+  int num_workers;     // waves launched (grid size * waves per workgroup)
+  int dyn_cap;         // most dynamic chunks the workspace holds (0: static split only)
+  int chunk_steps;     // smallest dynamic chunk, in steps
+  int static_frac_q10; // share of the steps split statically, in 1/1024
+  // Lengths are clamped to this (min of max_seq_len and the table width) so a length beyond the
+  // caller's bound cannot take a kernel outside the table.
   int len_cap;
   float scale_log2;  // softmax scale times log2(e)
 };
 
+// Waves the decode kernel is launched with for this shape on the current device.
+int decode_workers(int head_dim, int group);
+// Workspace layout of pa_decode: the chunk counter, then unit_info, then the partial slots.
+struct DecodeWorkspace {
+  size_t counter_off, info_off, partials_off, bytes;
+  int workers, dyn_cap;
+};
+DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 struct ReshapeParams {

@@ -133,6 +133,61 @@ def test_decode_max_length_and_scale():
     assert_close(upcast(host_u16(out)), ref, "decode at 8192 tokens, scale 0.3")
 
 
+def test_decode_many_short_sequences_and_wide_batch():
+    """Several hundred sequences (more than one 256-wide scan chunk), lengths 0..70, so that one
+    wave's range crosses many units and most units sit inside a single wave."""
+    lens = np.random.default_rng(24).integers(0, 71, size=700).tolist()
+    case = build_case(Spec(name="short", num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                           seed=(24,), decode_lens=lens))
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    got = upcast(gpu_decode(case, kc, vc))
+    assert_close(got, oracle_decode(case, case.key_cache, case.value_cache), "700 short sequences")
+
+
+@pytest.mark.parametrize("workers", [4, 12, 64])
+def test_decode_few_workers_long_ranges(workers, monkeypatch):
+    """Few worker waves: each wave streams hundreds of steps, crossing the 64-block id window and
+    several unit boundaries; results must not depend on the worker count beyond rounding."""
+    case = build_case(Spec(name="few", num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                           seed=(25,), decode_lens=[3000, 1, 2049, 4100, 17, 1500]))
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    monkeypatch.setenv("PA_DECODE_WORKERS", str(workers))
+    got = upcast(gpu_decode(case, kc, vc))
+    assert_close(got, oracle_decode(case, case.key_cache, case.value_cache), f"{workers} workers")
+
+
+@pytest.mark.parametrize("static_q10,chunk", [(1024, 4), (768, 4), (512, 1), (640, 16)])
+def test_decode_static_and_dynamic_splits(static_q10, chunk, monkeypatch):
+    """The share of statically split steps and the dynamic chunk size change only how work is
+    handed out: every split must match the oracle, and one workspace is reused across calls."""
+    case = cached_named_case(2)
+    monkeypatch.setenv("PA_DECODE_STATIC_Q10", str(static_q10))
+    monkeypatch.setenv("PA_DECODE_CHUNK", str(chunk))
+    d = case.decode
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    q, bt, sl = dev_u16(d.query), dev_i32(d.block_tables), dev_i32(d.seq_lens)
+    ws = torch.zeros(pa.decode_workspace_bytes(d.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                               case.head_dim, d.max_seq_len),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        out = pa.decode(q, kc, vc, bt, sl, num_kv_heads=case.num_kv_heads, block_size=16,
+                        scale=float(case.scale), max_seq_len=d.max_seq_len, workspace=ws)
+        outs.append(host_u16(out))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])  # deterministic whatever wave takes which chunk
+    seqs = list(range(0, d.num_seqs, 9))
+    ref = oracle_decode(case, case.key_cache, case.value_cache, seqs=seqs)
+    assert_close(upcast(outs[0])[seqs], ref[seqs], f"decode static {static_q10}/1024, chunk {chunk}")
+
+
+def test_decode_workspace_sizes_on_device():
+    n = pa.decode_workspace_bytes(128, 64, 8, 128, 8192)
+    assert n >= 128 * 8 * 8 * (128 + 2) * 4  # at least one partial slot per unit
+    assert pa.decode_workspace_bytes(128, 64, 8, 128, 16) == n  # independent of lengths
+    assert pa.decode_workspace_bytes(256, 64, 8, 128, 8192) > n
+
+
 # ------------------------------------------------------------------------- invariants on the GPU
 
 def _small(seed=30, **kw):
@@ -230,4 +285,4 @@ def test_abi_rejects_bad_arguments_without_touching_buffers():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), before.view(torch.int16))
     lib = pa.load_library()
-    assert lib.pa_decode(0, 0, 0, 0, 0, 0, 1, 8, 2, 128, 16, 4, 64, 0.1, 0, 0, 0) == 1
+    assert lib.pa_decode(0, 0, 0, 0, 1000, 0, 0, 1, 8, 2, 128, 16, 4, 64, 0.1, 0, 0, 0) == 1

@@ -126,9 +126,14 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
                       int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pa_prefill_chunk needs for this batch shape. */
-size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
-                                  int32_t head_dim, int32_t max_seq_len);
+/*
+ * Bytes of workspace pa_prefill_chunk needs for this batch shape on the current device; 0 means
+ * none (workspace may then be NULL).  Long contexts are split into key ranges whose partial softmax
+ * states are combined afterwards; the workspace holds those states.  It needs no initialisation.
+ */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_seq_len);
 
 /*
  * pa_prefill_chunk — causal attention of a chunk of query tokens per sequence over the
@@ -137,27 +142,34 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num
  * Source: long prompts are processed in fixed-size chunks (512 tokens by default) that attend to
  * everything cached before them and are batched with decode tokens ("Serving engine internals",
  * section "Chunked prefill protects the TTFT tail"); the mask is Step 2's causal mask aligned to
- * the end of the key range, so chunk row i (0-based) of a sequence of L cached tokens with q_len
- * chunk rows sees keys 0 .. L - q_len + i.
+ * the end of the key range ("Inference optimization", Build it, Step 2), so chunk row t (0-based)
+ * of a sequence of L cached tokens with q_len chunk rows sees keys 0 .. L - q_len + t.
  *
- *   out            bf16 [total_q][num_q_heads][head_dim]
+ *   out            bf16 [total_q][num_q_heads][head_dim] (written; must not alias inputs)
  *   query          bf16 [total_q][num_q_heads][head_dim]; sequence i owns rows
  *                  query_start_loc[i] .. query_start_loc[i+1]-1
+ *   key_cache, value_cache, num_blocks  as for pa_decode (ids are clamped into the pool)
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]; entries for keys < L are read
  *   query_start_loc int32 [num_seqs+1], non-decreasing, query_start_loc[num_seqs] == total_q
  *   seq_lens       int32 [num_seqs]; L_i = prior context + chunk length; the chunk's own K/V must
- *                  already be in the cache (pa_reshape_and_cache first); L_i >= q_len_i
- *   max_q_len      host-side upper bound of the chunk lengths
+ *                  already be in the cache (pa_reshape_and_cache first); q_len_i <= L_i <=
+ *                  max_seq_len (other values give unspecified results, never an access outside
+ *                  the buffers)
+ *   max_q_len      host-side upper bound of the chunk lengths (<= max_seq_len)
  *   max_seq_len    host-side upper bound of seq_lens (<= max_blocks_per_seq*block_size)
+ *   scale          softmax scale (> 0)
  *   workspace      at least pa_prefill_workspace_bytes(...) bytes
- * Same head_dim / group limits as pa_decode.
+ * Both contractions run on bf16 matrix cores with fp32 accumulation; output rounded to bf16
+ * (nearest even).  Same head_dim / group limits as pa_decode.
  */
 pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache,
-                             const void* value_cache, const int32_t* block_tables,
-                             const int32_t* query_start_loc, const int32_t* seq_lens,
-                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                             int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
-                             float scale, void* workspace, size_t workspace_bytes, void* stream);
+                             const void* value_cache, int64_t num_blocks,
+                             const int32_t* block_tables, const int32_t* query_start_loc,
+                             const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
+                             int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int32_t max_seq_len, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * Kernel timing (tracing).  While enabled, every kernel the library launches is bracketed by a

@@ -47,9 +47,9 @@ _SIGNATURES = {
     "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pa_decode": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                          ctypes.c_float, _P, _SZ, _P]),
-    "pa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
-    "pa_prefill_chunk": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
-                                _I32, _I32, _I32, ctypes.c_float, _P, _SZ, _P]),
+    "pa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_prefill_chunk": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                _I32, _I32, _I32, _I32, ctypes.c_float, _P, _SZ, _P]),
     "pa_trace_enable": (_I32, [_I32]),
     "pa_trace_read": (_I32, [ctypes.c_char_p, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double)]),
 }
@@ -102,10 +102,9 @@ def pool_shape(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: in
 
 
 def _num_blocks(pool: torch.Tensor, num_kv_heads: int, block_size: int, head_dim: int) -> int:
-    per = num_kv_heads * block_size * head_dim
-    if pool.numel() % per:
-        raise ValueError("pool size is not a whole number of blocks")
-    return pool.numel() // per
+    """Whole blocks the pool holds for this shape (the library validates the shape itself)."""
+    per = max(num_kv_heads * block_size * head_dim, 1)
+    return max(pool.numel() // per, 1)
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
@@ -130,10 +129,11 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
                                                         max_seq_len))
 
 
-def prefill_workspace_bytes(num_seqs: int, total_q: int, num_q_heads: int, head_dim: int,
-                            max_seq_len: int) -> int:
-    return int(load_library().pa_prefill_workspace_bytes(num_seqs, total_q, num_q_heads, head_dim,
-                                                         max_seq_len))
+def prefill_workspace_bytes(num_seqs: int, total_q: int, max_q_len: int, num_q_heads: int,
+                            num_kv_heads: int, head_dim: int, max_seq_len: int) -> int:
+    """Workspace bytes pa_prefill_chunk needs on the current device (0: none)."""
+    return int(load_library().pa_prefill_workspace_bytes(num_seqs, total_q, max_q_len, num_q_heads,
+                                                         num_kv_heads, head_dim, max_seq_len))
 
 
 def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> tuple:
@@ -187,10 +187,11 @@ def prefill_chunk(query: torch.Tensor, key_cache: torch.Tensor, value_cache: tor
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(query)
-    ws, ws_bytes = _workspace(prefill_workspace_bytes(n, total_q, Hq, D, max_seq_len), workspace,
-                              query.device)
+    ws, ws_bytes = _workspace(prefill_workspace_bytes(n, total_q, max_q_len, Hq, num_kv_heads, D,
+                                                      max_seq_len), workspace, query.device)
+    nb = _num_blocks(key_cache, num_kv_heads, block_size, D)
     _check(lib.pa_prefill_chunk(_bf16(out, "out"), _bf16(query, "query"), _bf16(key_cache, "key_cache"),
-                                _bf16(value_cache, "value_cache"),
+                                _bf16(value_cache, "value_cache"), nb,
                                 _ints(block_tables, torch.int32, "block_tables"),
                                 _ints(query_start_loc, torch.int32, "query_start_loc"),
                                 _ints(seq_lens, torch.int32, "seq_lens"), n, total_q, max_q_len, Hq,

@@ -270,29 +270,86 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
   return hip_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)), "decode");
 }
 
-size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
-                                  int32_t head_dim, int32_t max_seq_len) {
-  (void)num_seqs;
-  (void)total_q;
-  (void)num_q_heads;
-  (void)head_dim;
-  (void)max_seq_len;
-  return 0;
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_seq_len) {
+  if (num_seqs <= 0 || total_q <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads)
+    return 0;
+  const int g = num_q_heads / num_kv_heads;
+  if (!supported_head_dim(head_dim) || !supported_group(g, head_dim)) return 0;
+  const pa::PrefillSplit sp =
+      pa::prefill_split(num_seqs, max_q_len, num_kv_heads, g, head_dim, max_seq_len);
+  if (sp.splits <= 1) return 0;
+  const size_t rows = (size_t)total_q * num_q_heads * sp.splits;
+  return align_up(rows * 2 * sizeof(float), 256) + rows * head_dim * sizeof(float);
 }
 
 pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache,
-                             const void* value_cache, const int32_t* block_tables,
-                             const int32_t* query_start_loc, const int32_t* seq_lens,
-                             int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                             int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
-                             float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)out; (void)query; (void)key_cache; (void)value_cache; (void)block_tables;
-  (void)query_start_loc; (void)seq_lens; (void)num_seqs; (void)total_q; (void)max_q_len;
-  (void)num_q_heads; (void)num_kv_heads; (void)head_dim; (void)block_size;
-  (void)max_blocks_per_seq; (void)max_seq_len; (void)scale; (void)workspace;
-  (void)workspace_bytes; (void)stream;
-  return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk is not built yet");
+                             const void* value_cache, int64_t num_blocks,
+                             const int32_t* block_tables, const int32_t* query_start_loc,
+                             const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
+                             int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int32_t max_seq_len, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size (num_seqs %d, total_q %d, max_q_len %d)",
+                num_seqs, total_q, max_q_len);
+  pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
+                                         max_blocks_per_seq, max_seq_len, scale);
+  if (st != PA_OK) return st;
+  if (num_blocks <= 0 || num_blocks > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks %lld out of range", (long long)num_blocks);
+  if (max_q_len > max_seq_len)
+    return fail(PA_ERR_INVALID_ARG, "max_q_len %d exceeds max_seq_len %d", max_q_len, max_seq_len);
+  if (num_seqs == 0 || total_q == 0) return ok();
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !query_start_loc ||
+      !seq_lens)
+    return fail(PA_ERR_NULL_POINTER, "null pointer argument");
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(query_start_loc, 4) ||
+      !aligned(seq_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for bf16 arrays)");
+  if (out == query) return fail(PA_ERR_INVALID_ARG, "out must not alias query");
+  const int g = num_q_heads / num_kv_heads;
+  const size_t need = pa_prefill_workspace_bytes(num_seqs, total_q, max_q_len, num_q_heads,
+                                                 num_kv_heads, head_dim, max_seq_len);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  const pa::PrefillSplit sp =
+      pa::prefill_split(num_seqs, max_q_len, num_kv_heads, g, head_dim, max_seq_len);
+  pa::PrefillParams p{};
+  p.out = static_cast<uint16_t*>(out);
+  p.query = static_cast<const uint16_t*>(query);
+  p.kpool = static_cast<const uint16_t*>(key_cache);
+  p.vpool = static_cast<const uint16_t*>(value_cache);
+  p.block_tables = block_tables;
+  p.query_start_loc = query_start_loc;
+  p.seq_lens = seq_lens;
+  p.num_blocks = num_blocks;
+  p.num_seqs = num_seqs;
+  p.total_q = total_q;
+  p.max_q_len = max_q_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
+  p.splits = need > 0 ? sp.splits : 1;
+  p.split_keys = need > 0 ? sp.split_keys : max_seq_len;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  if (need > 0) {
+    const size_t rows = (size_t)total_q * num_q_heads * p.splits;
+    p.ws_ml = static_cast<float*>(workspace);
+    p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align_up(rows * 2 * sizeof(float), 256));
+  }
+  return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill_chunk");
 }
 
 }  // extern "C"

@@ -65,14 +65,21 @@ struct PrefillParams {
   const int32_t* block_tables;
   const int32_t* query_start_loc;
   const int32_t* seq_lens;
-  float* ws_ml;   // [total_q][Hq][splits] (m, l)
+  float* ws_ml;   // [total_q][Hq][splits] (m, l), m in the log2 domain
   float* ws_acc;  // [total_q][Hq][splits][D]
+  int64_t num_blocks;
   int num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size;
-  int max_blocks_per_seq, max_seq_len, splits;
+  int max_blocks_per_seq, max_seq_len;
+  int splits, split_keys;  // context split: `splits` key ranges of split_keys keys (multiple of 32)
   float scale_log2;
 };
 
-int prefill_splits(int num_seqs, int max_q_len, int num_kv_heads, int group, int max_seq_len);
+// Context split chosen for a prefill launch (it sizes the workspace).
+struct PrefillSplit {
+  int splits, split_keys;
+};
+PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int group, int head_dim,
+                           int max_seq_len);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
 // Kernel timing: when tracing is on, launches are bracketed by events on their stream.

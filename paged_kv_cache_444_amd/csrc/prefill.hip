@@ -1,0 +1,392 @@
+// Chunked-prefill attention for gfx950 on matrix cores.
+//
+// What is computed: a chunk of q_len query tokens of a sequence attends causally to the
+// sequence's whole paged context, including the chunk's own keys, which pa_reshape_and_cache has
+// already written ("Serving engine internals" lesson, section on chunked prefill: long prompts are
+// processed as fixed-size chunks batched with decode tokens).  The attention is the "Inference
+// optimization" lesson's Build it, Step 2: max-subtracted softmax(q·kᵀ·scale)·v with the causal
+// mask aligned to the end of the key range, so chunk row t (0-based) of a sequence of L cached
+// tokens sees keys 0 .. L - q_len + t.  Prefill is compute-bound (same lesson, "Prefill vs
+// decode"), so both contractions run on v_mfma_f32_16x16x32_bf16.
+//
+// Tiling.  A workgroup of four waves owns 64*RT query rows of one KV head, where a row is a
+// (query token, head-in-group) pair: the G query heads that share a KV head share every K/V tile,
+// so they are packed into the rows of one tile (row r = token r / G, head r % G).  Each wave owns
+// RT tiles of 16 rows.  The keys are walked in tiles of 32 (two 16-token sub-blocks); each tile's
+// K and V are copied from the pool into LDS in the pool's own layout (double buffered) and every
+// wave computes
+//   Sᵀ[key][row] = K·Qᵀ      A = K from LDS (16 keys x 32 dims per instruction), B = Q rows kept
+//                            in registers for the whole walk;
+//   Oᵀ[dim][row] += Vᵀ·Pᵀ    A = V from LDS, B = the bf16 probabilities.
+// With the transposed product the score tile comes out of the matrix core exactly in the lane
+// layout the second product needs as its B operand (lane l holds keys 4*(l/16)+i of row l%16), so
+// probabilities never leave registers.  The softmax is online per row in the log2 domain; masking
+// is applied only on tiles that reach past the first token's diagonal, by selection (NaN-safe),
+// and V rows of keys at or past L are zeroed in LDS so that 0 * NaN cannot enter the accumulator.
+//
+// Context split.  Long contexts are cut into `splits` key ranges (multiples of 32 keys) so the
+// launch has enough workgroups; each range's (m, l, acc) per row goes to the workspace and
+// prefill_merge combines them in split order.  With one split the output is written directly.
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+#include <algorithm>
+#include <cstdlib>
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPWaves = 4;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kKeyTile = 32;
+
+// 16-row MFMA tiles per wave: two, except for head_dim 256 whose accumulators need the room.
+template <int D>
+constexpr int kRowTiles = (D == 256) ? 1 : 2;
+
+__device__ __forceinline__ f32x4_t mfma(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float xor32_f32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Copy of one 32-key tile (two sub-blocks) of K and V for KV head h into LDS, staged through
+// registers: each thread moves D/32 16-byte pieces.  Piece idx covers chunk idx / (2D) (K of
+// sub-block 0, K of sub-block 1, V of sub-block 0, V of sub-block 1), element 8*(idx % (2D)).
+template <int D>
+struct TileRegs {
+  uint4 v[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillParams& p, const int* bt,
+                                          int h, int tile, int L) {
+  constexpr int kPieces = D / 32;
+  const int bs = p.block_size;
+  const size_t tile_elems = (size_t)bs * D;
+  const size_t block_elems = (size_t)p.num_kv_heads * tile_elems;
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    const int idx = threadIdx.x + kPThreads * k;
+    const int chunk = idx / (2 * D);
+    const int within = idx % (2 * D);
+    const int sub = chunk & 1;
+    const int key0 = tile * kKeyTile + 16 * sub;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (key0 < L) {
+      int id = bt[key0 / bs];
+      id = min(max(id, 0), (int)(p.num_blocks - 1));
+      const size_t off = (size_t)id * block_elems + (size_t)h * tile_elems +
+                         (size_t)(key0 % bs) * D + 8 * (size_t)within;
+      const uint16_t* pool = (chunk < 2) ? p.kpool : p.vpool;
+      val = *(const uint4*)(pool + off);
+      if (chunk >= 2 && key0 + 16 > L) {
+        // V rows: element (d, t) at d*16 + t; this piece holds tokens 8*(within&1) .. +7.
+        const int t0 = key0 + 8 * (within & 1);
+        uint32_t w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = t0 + 2 * e;
+          const uint32_t keep = (t + 1 < L) ? 0xFFFFFFFFu : ((t < L) ? 0xFFFFu : 0u);
+          w[e] &= keep;
+        }
+        val = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    r.v[k] = val;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* lds) {
+  // LDS tile: K sub-blocks 0 and 1 ([16*D] each), then V sub-blocks 0 and 1.
+#pragma unroll
+  for (int k = 0; k < D / 32; ++k) {
+    const int idx = threadIdx.x + kPThreads * k;
+    *(uint4*)(lds + 8 * (size_t)idx) = r.v[k];
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
+  constexpr int RT = kRowTiles<D>;
+  constexpr int KS = D / 32;       // k-steps of the score product
+  constexpr int DT = D / 16;       // 16-dim tiles of the output
+  constexpr int ROWS = kPWaves * 16 * RT;
+  constexpr int TQ = ROWS / G;     // query tokens per workgroup
+  constexpr int TILE_ELEMS = 4 * 16 * D;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][TILE_ELEMS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int s = blockIdx.z;
+  const int h = blockIdx.y / p.splits;
+  const int split = blockIdx.y % p.splits;
+  const int qs = p.query_start_loc[s];
+  const int q_len = p.query_start_loc[s + 1] - qs;
+  const int q0 = blockIdx.x * TQ;
+  if (q_len <= 0 || q0 >= q_len) return;  // block-uniform
+  const int L = min(max(p.seq_lens[s], 0), p.max_seq_len);
+  const int ctx = max(L - q_len, 0);
+  const int tq = min(TQ, q_len - q0);
+  const int kv_end = min(L, ctx + q0 + tq);
+  const int kb = split * p.split_keys;
+  const int ke = min(kv_end, kb + p.split_keys);
+  const int Hq = p.num_q_heads;
+  const float c = p.scale_log2;
+
+  // Rows of this lane: column n = lane % 16 of each of the wave's row tiles.
+  int row_tok[RT], row_lim[RT];
+  bool row_ok[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = wave * 16 * RT + 16 * rt + (lane & 15);
+    row_tok[rt] = q0 + r / G;
+    // Rows past the chunk, or past the query array if query_start_loc is malformed, are skipped.
+    row_ok[rt] = (r / G) < tq && qs + row_tok[rt] < p.total_q && qs >= 0;
+    row_lim[rt] = min(ctx + row_tok[rt], L - 1);  // last visible key
+  }
+
+  // Q operand: rows as B, 32 dims per k-step, lane holds dims 8*(lane/16) .. +7.
+  uint4 qb[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = wave * 16 * RT + 16 * rt + (lane & 15);
+    // Rows past the chunk read its last row (always inside the query array) and are zeroed.
+    const int tok = min(min(qs + q0 + r / G, qs + q_len - 1), p.total_q - 1);
+    const size_t qrow = (size_t)max(tok, 0) * Hq + (size_t)h * G + r % G;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = *(const uint4*)(p.query + qrow * D + 32 * ks + 8 * (lane >> 4));
+      qb[rt][ks] = row_ok[rt] ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  f32x4_t acc[DT][RT];
+  float m[RT], l[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = kNegInf;
+    l[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int t_first = kb / kKeyTile;
+  const int t_end = (ke + kKeyTile - 1) / kKeyTile;  // empty range: t_end <= t_first
+  const int diag = ctx + q0;  // keys above this need a per-row mask
+  if (t_first < t_end) {
+    TileRegs<D> regs;
+    load_tile<D>(regs, p, bt, h, t_first, L);
+    store_tile<D>(regs, lds[0]);
+    __syncthreads();
+    int cur = 0;
+    for (int t = t_first; t < t_end; ++t) {
+      const bool more = t + 1 < t_end;  // block-uniform
+      if (more) load_tile<D>(regs, p, bt, h, t + 1, L);
+      const uint16_t* kl = lds[cur];
+      const uint16_t* vl = lds[cur] + 2 * 16 * D;
+
+      // Scores for keys 32t + 16kt + 4*(lane/16) + i.
+      f32x4_t sc[2][RT];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) sc[kt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 ka =
+              *(const uint4*)(kl + kt * 16 * D + ks * 512 + (lane & 15) * 32 + 8 * (lane >> 4));
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) sc[kt][rt] = mfma(ka, qb[rt][ks], sc[kt][rt]);
+        }
+      }
+      const bool masked = t * kKeyTile + kKeyTile - 1 > diag;  // block-uniform
+      uint4 pb[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float x[8];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = sc[kt][rt][i] * c;
+            if (masked) {
+              const int key = t * kKeyTile + 16 * kt + 4 * (lane >> 4) + i;
+              v = (key <= row_lim[rt]) ? v : kNegInf;
+            }
+            x[4 * kt + i] = v;
+          }
+        float mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+        mx = fmaxf(mx, xor16_f32(mx));
+        mx = fmaxf(mx, xor32_f32(mx));
+        const float mn = fmaxf(m[rt], mx);
+        const float ms = (mn == kNegInf) ? 0.f : mn;
+        const float alpha = fast_exp2(m[rt] - ms);
+        m[rt] = mn;
+        float ps = 0.f;
+        float pr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pr[i] = fast_exp2(x[i] - ms);
+          ps += pr[i];
+        }
+        l[rt] = l[rt] * alpha + ps;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt][rt] *= alpha;
+        // B operand of the second product: item j < 4 is key 4*(lane/16)+j of sub-block 0,
+        // item j >= 4 the same key of sub-block 1 (the A operand below uses the same order).
+        pb[rt] = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                            pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + (lane & 15);
+        const uint2 v0 = *(const uint2*)(vl + d * 16 + 4 * (lane >> 4));
+        const uint2 v1 = *(const uint2*)(vl + 16 * D + d * 16 + 4 * (lane >> 4));
+        const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[dt][rt] = mfma(va, pb[rt], acc[dt][rt]);
+      }
+      if (more) store_tile<D>(regs, lds[cur ^ 1]);
+      __syncthreads();
+      cur ^= 1;
+    }
+  }
+
+  // Finish: row sums over the four lane groups, then normalise or hand the split's state over.
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float lt = l[rt];
+    lt += xor16_f32(lt);
+    lt += xor32_f32(lt);
+    if (!row_ok[rt]) continue;
+    const int r = wave * 16 * RT + 16 * rt + (lane & 15);
+    const size_t orow = (size_t)(qs + row_tok[rt]) * Hq + (size_t)h * G + r % G;
+    if (p.splits == 1) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4_t a = acc[dt][rt];
+        const uint2 o = make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv),
+                                   pack_bf16x2(a[2] * inv, a[3] * inv));
+        *(uint2*)(p.out + orow * D + 16 * dt + 4 * (lane >> 4)) = o;
+      }
+    } else {
+      const size_t u = orow * p.splits + split;
+      if (lane < 16) {
+        p.ws_ml[2 * u] = m[rt];  // log2 domain; -inf for an empty or fully masked range
+        p.ws_ml[2 * u + 1] = lt;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *(f32x4_t*)(p.ws_acc + u * D + 16 * dt + 4 * (lane >> 4)) = acc[dt][rt];
+    }
+  }
+}
+
+// Combine the context splits of every (query row, head) in split order.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
+  constexpr int HPB = 256 / D;  // heads per block
+  const int row = blockIdx.x;
+  const int hq = blockIdx.y * HPB + threadIdx.x / D;
+  const int d = threadIdx.x % D;
+  if (hq >= p.num_q_heads) return;
+  const size_t u0 = ((size_t)row * p.num_q_heads + hq) * p.splits;
+  float M = kNegInf, lt = 0.f, a = 0.f;
+  for (int j = 0; j < p.splits; ++j) {
+    const float mj = p.ws_ml[2 * (u0 + j)];
+    if (mj == kNegInf) continue;  // empty range for this row
+    const float mn = fmaxf(M, mj);
+    const float c_old = fast_exp2(M - mn);
+    const float c_new = fast_exp2(mj - mn);
+    lt = lt * c_old + p.ws_ml[2 * (u0 + j) + 1] * c_new;
+    a = a * c_old + p.ws_acc[(u0 + j) * D + d] * c_new;
+    M = mn;
+  }
+  p.out[((size_t)row * p.num_q_heads + hq) * D + d] = to_bf16(lt > 0.f ? a / lt : 0.f);
+}
+
+template <int D, int G>
+hipError_t launch_dg(const PrefillParams& p, hipStream_t stream) {
+  constexpr int TQ = kPWaves * 16 * kRowTiles<D> / G;
+  {
+    TraceScope t("prefill_chunk", stream);
+    const dim3 grid((p.max_q_len + TQ - 1) / TQ, p.num_kv_heads * p.splits, p.num_seqs);
+    hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kPThreads), 0, stream, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  {
+    TraceScope t("prefill_merge", stream);
+    constexpr int HPB = 256 / D;
+    const dim3 grid(p.total_q, (p.num_q_heads + HPB - 1) / HPB);
+    hipLaunchKernelGGL((prefill_merge_kernel<D>), grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PrefillParams& p, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_dg<D, 1>(p, stream);
+    case 2: return launch_dg<D, 2>(p, stream);
+    case 4: return launch_dg<D, 4>(p, stream);
+    case 8: if constexpr (D <= 128) return launch_dg<D, 8>(p, stream); break;
+    case 16: if constexpr (D <= 64) return launch_dg<D, 16>(p, stream); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return cus > 0 ? cus : 256;
+}
+
+}  // namespace
+
+PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int group, int head_dim,
+                           int max_seq_len) {
+  PrefillSplit r{1, std::max(max_seq_len, 1)};
+  if (num_seqs <= 0 || max_q_len <= 0 || max_seq_len <= 0) return r;
+  const int rows = kPWaves * 16 * (head_dim == 256 ? 1 : 2);
+  const int tq = rows / group;
+  const long long base = (long long)((max_q_len + tq - 1) / tq) * num_kv_heads * num_seqs;
+  // Enough workgroups for four per CU, each range at least 256 keys, at most 16 ranges.
+  long long want = (4LL * cu_count() + base - 1) / base;
+  if (const char* e = std::getenv("PA_PREFILL_SPLITS")) want = std::atoi(e);
+  want = std::min<long long>(std::max<long long>(want, 1), 16);
+  want = std::min<long long>(want, std::max(1, max_seq_len / 256));
+  if (want <= 1) return r;
+  int keys = (int)((max_seq_len + want - 1) / want);
+  keys = (keys + kKeyTile - 1) / kKeyTile * kKeyTile;
+  r.split_keys = keys;
+  r.splits = (max_seq_len + keys - 1) / keys;
+  return r;
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  if (p.splits < 1 || (p.splits > 1 && p.split_keys % kKeyTile)) return hipErrorInvalidValue;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  switch (p.head_dim) {
+    case 64: return launch_d<64>(p, G, stream);
+    case 128: return launch_d<128>(p, G, stream);
+    case 256: return launch_d<256>(p, G, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -13,8 +13,13 @@ previous step filled.  Prints one JSON line.
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same batch (a correctness tool,
                not an optimised CPU kernel)
 
+  mixed_step   the chunked-prefill mixed step of the same model shape (one 512-token chunk over
+               31,744 cached tokens, batched with 127 decode sequences): per-kernel times and the
+               prefill kernel's MFMA roofline (causal FLOPs / its event-timed duration against the
+               2.5 PFLOP/s dense bf16 peak)
+
 `--mode copy` instead times a plain device-to-device copy of a known size: the calibration run for
-the FETCH_SIZE / WRITE_SIZE hardware counters.
+the FETCH_SIZE / WRITE_SIZE hardware counters.  `--mode mixed` runs only the mixed step.
 """
 
 from __future__ import annotations
@@ -31,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "pa_decode achieved HBM GB/s (% of peak) + seqs/s, 70B-shape B=128"
 
 
@@ -42,6 +48,42 @@ def decode_bytes(seq_lens, Hq, Hkv, D, bs):
     qo = len(L) * 2 * Hq * D * 2
     tables = int(((L + bs - 1) // bs).sum()) * 4 + len(L) * 4
     return kv + qo + tables
+
+
+def prefill_flops(query_start_loc, seq_lens, Hq, D):
+    """Causal attention FLOPs of a prefill chunk: one multiply-add (2 FLOPs) per head dimension for
+    q·k and one for p·v, per visible (query row, key) pair and head:
+    4 * D * Hq * (sum over rows of the keys each row sees)."""
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    total = 0
+    for i, L in enumerate(np.asarray(seq_lens, dtype=np.int64)):
+        q = int(qsl[i + 1] - qsl[i])
+        ctx = int(L) - q
+        total += q * ctx + q * (q + 1) // 2
+    return 4 * D * Hq * total
+
+
+def reshape_bytes(T, Hkv, D):
+    """Algorithmic bytes of reshape_and_cache: K and V rows read and written, slots read."""
+    return 4 * T * Hkv * D * 2 + 8 * T
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` measured with FETCH_SIZE / WRITE_SIZE (profiles/traffic.json),
+    or None when the kernel's sources changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def parse():
@@ -56,7 +98,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over the whole batch until this much CPU time is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["decode", "copy"], default="decode")
+    ap.add_argument("--mode", choices=["decode", "copy", "mixed"], default="decode")
+    ap.add_argument("--mixed-steps", type=int, default=30)
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-step measurement")
     ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
 
@@ -96,6 +140,9 @@ def main():
 
     if args.mode == "copy":
         run_copy(args)
+        return
+    if args.mode == "mixed":
+        print(json.dumps(run_mixed(args)), flush=True)
         return
 
     import paged_kv_cache_444_amd as pa
@@ -164,6 +211,13 @@ def main():
     main_ms = ms_main / max(n_main, 1)
     main_gbs = nbytes / (main_ms * 1e-3) / 1e9
 
+    n_pools = len(pools)
+    mixed = None
+    if not args.no_mixed:
+        del pools, kc0, vc0
+        torch.cuda.empty_cache()
+        mixed = run_mixed(args)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
@@ -188,7 +242,7 @@ def main():
             "workload": case.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "block_size": bs, "mean_seq_len": round(float(d.seq_lens.mean()), 1),
             "max_seq_len": max_len, "algorithmic_bytes": nbytes, "pool_blocks": case.num_blocks,
-            "pool_copies_cycled": len(pools),
+            "pool_copies_cycled": n_pools,
             "decode_workers": int(os.environ.get("PA_DECODE_WORKERS", "0")) or "default",
             "decode_prefetch": int(os.environ.get("PA_DECODE_PREFETCH", "1")),
             "decode_static_q10": int(os.environ.get("PA_DECODE_STATIC_Q10", "1024")),
@@ -197,13 +251,86 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "decode_kernel", "achieved": round(main_gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(main_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None, "launch_us": round(main_ms * 1e3, 2),
+            "traffic": measured_traffic("decode_kernel"), "launch_us": round(main_ms * 1e3, 2),
             "merge_launch_us": round(ms_merge / max(n_merge, 1) * 1e3, 2),
         },
         "warm_single_pool_us_per_step": None if warm_us is None else round(warm_us, 2),
+        "mixed_step": mixed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def run_mixed(args):
+    """Chunked-prefill mixed step of the 70B shape: reshape of the chunk's K/V, the prefill chunk,
+    then decode of the 127 other sequences, all resident in HBM, on one stream."""
+    import torch
+
+    import paged_kv_cache_444_amd as pa
+    from workloads import named_case
+
+    log("generating the mixed chunked-prefill workload")
+    case = named_case(4)
+    Hq, Hkv, D, bs = case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+    pf, dc, rs = case.prefill, case.decode, case.reshape
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    kc, vc = dev(case.key_cache), dev(case.value_cache)
+    rk, rv, slots = dev(rs.key), dev(rs.value), torch.from_numpy(rs.slot_mapping).cuda()
+    pq, pbt = dev(pf.query), torch.from_numpy(pf.block_tables).cuda()
+    pqsl, psl = torch.from_numpy(pf.query_start_loc).cuda(), torch.from_numpy(pf.seq_lens).cuda()
+    dq, dbt, dsl = dev(dc.query), torch.from_numpy(dc.block_tables).cuda(), torch.from_numpy(dc.seq_lens).cuda()
+    pout, dout = torch.empty_like(pq), torch.empty_like(dq)
+    pws = torch.zeros(max(pa.prefill_workspace_bytes(pf.num_seqs, pf.total_q, pf.max_q_len, Hq, Hkv, D,
+                                                     pf.max_seq_len), 1), dtype=torch.uint8, device="cuda")
+    dws = torch.zeros(max(pa.decode_workspace_bytes(dc.num_seqs, Hq, Hkv, D, dc.max_seq_len), 1),
+                      dtype=torch.uint8, device="cuda")
+    scale = float(case.scale)
+
+    def step():
+        pa.reshape_and_cache(rk, rv, kc, vc, slots, num_kv_heads=Hkv, head_dim=D, block_size=bs)
+        pa.prefill_chunk(pq, kc, vc, pbt, pqsl, psl, num_kv_heads=Hkv, block_size=bs,
+                         max_q_len=pf.max_q_len, max_seq_len=pf.max_seq_len, scale=scale, out=pout,
+                         workspace=pws)
+        pa.decode(dq, kc, vc, dbt, dsl, num_kv_heads=Hkv, block_size=bs, scale=scale,
+                  max_seq_len=dc.max_seq_len, out=dout, workspace=dws)
+
+    names = ("reshape_and_cache", "prefill_chunk", "prefill_merge", "decode_partition", "decode_merge")
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    pa.trace_enable(True)
+    for n in names:
+        pa.trace_read(n)
+    t0 = time.perf_counter()
+    for _ in range(args.mixed_steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.mixed_steps
+    per = {}
+    for n in names:
+        k, ms = pa.trace_read(n)
+        per[n] = round(ms / k * 1e3, 2) if k else None
+    pa.trace_enable(False)
+    flops = prefill_flops(pf.query_start_loc, pf.seq_lens, Hq, D)
+    pre_us = per["prefill_chunk"]
+    tflops = flops / (pre_us * 1e-6) / 1e12
+    dbytes = decode_bytes(dc.seq_lens, Hq, Hkv, D, bs)
+    rbytes = reshape_bytes(len(rs.slot_mapping), Hkv, D)
+    log(f"mixed step {ms_step * 1e3:.1f} us")
+    return {
+        "workload": case.name, "us_per_step": round(ms_step * 1e3, 2), "steps": args.mixed_steps,
+        "kernel_us": per,
+        "prefill_roofline": {"bound": "mfma", "kernel": "prefill_chunk",
+                             "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "flops_per_launch": flops},
+        "decode_gbs": round(dbytes / (per["decode_partition"] * 1e-6) / 1e9, 1),
+        "reshape_gbs": round(rbytes / (per["reshape_and_cache"] * 1e-6) / 1e9, 1),
+        "reshape_bytes": rbytes, "decode_bytes": dbytes,
+    }
 
 
 def cpu_baseline(case, budget_s):

@@ -701,7 +701,7 @@ int decode_workers(int head_dim, int group) {
     }
   }
   // Tuning and test override, read on every call: the total number of worker waves.
-  if (const char* e = std::getenv("PA_DECODE_WORKERS")) {
+  if (const char* e = std::getenv("PA_DECODE_WORKERS"); e && *e) {
     const int v = std::atoi(e);
     if (v >= kWaves) return std::min(v / kWaves, blocks) * kWaves;
   }

@@ -209,7 +209,7 @@ namespace {
 // smallest dynamic chunk.
 int env_int(const char* name, int dflt, int lo, int hi) {
   const char* e = std::getenv(name);
-  if (!e) return dflt;
+  if (!e || !*e) return dflt;
   const int v = std::atoi(e);
   return (v >= lo && v <= hi) ? v : dflt;
 }

@@ -43,6 +43,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kPWaves = 4;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kKeyTile = 32;
+// log2-domain slack before the running max is raised: probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.0f;
 
 // 16-row MFMA tiles per wave: two, except for head_dim 256 whose accumulators need the room.
 template <int D>
@@ -167,11 +169,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     }
   }
 
+  // Online-softmax state per row (the same in the four lanes sharing a row): m is the running
+  // maximum of raw scores, nmc = -m * scale * log2(e) (0 while m is -inf), thr = m + slack.
   f32x4_t acc[DT][RT];
-  float m[RT], l[RT];
+  float m[RT], nmc[RT], thr[RT], l[RT];
+  const float slack_raw = kRescaleSlack / c;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m[rt] = kNegInf;
+    nmc[rt] = 0.f;
+    thr[rt] = kNegInf;
     l[rt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -211,37 +218,47 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       uint4 pb[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        float x[8];
+        float x[8];  // raw scores; -inf where masked
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float v = sc[kt][rt][i] * c;
+            float v = sc[kt][rt][i];
             if (masked) {
               const int key = t * kKeyTile + 16 * kt + 4 * (lane >> 4) + i;
               v = (key <= row_lim[rt]) ? v : kNegInf;
             }
             x[4 * kt + i] = v;
           }
-        float mx = x[0];
+        // The running max is raised (and acc rescaled) only when a score exceeds it by the slack,
+        // so probabilities stay below 2^slack and the accumulators are rarely touched.
+        bool raise = false;
 #pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = fmaxf(mx, xor16_f32(mx));
-        mx = fmaxf(mx, xor32_f32(mx));
-        const float mn = fmaxf(m[rt], mx);
-        const float ms = (mn == kNegInf) ? 0.f : mn;
-        const float alpha = fast_exp2(m[rt] - ms);
-        m[rt] = mn;
-        float ps = 0.f;
-        float pr[8];
+        for (int i = 0; i < 8; ++i) raise |= x[i] > thr[rt];
+        if (__ballot(raise)) {
+          float mx = x[0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+          mx = fmaxf(mx, xor16_f32(mx));
+          mx = fmaxf(mx, xor32_f32(mx));
+          const float mn = fmaxf(m[rt], mx);  // raw units
+          if (mn != kNegInf && mn != m[rt]) {
+            const float alpha = fast_exp2((m[rt] - mn) * c);  // 0 when the old max is -inf
+            l[rt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt][rt] *= alpha;
+            m[rt] = mn;
+            nmc[rt] = -mn * c;
+            thr[rt] = mn + slack_raw;
+          }
+        }
+        float pr[8], ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          pr[i] = fast_exp2(x[i] - ms);
+          pr[i] = fast_exp2(__builtin_fmaf(x[i], c, nmc[rt]));
           ps += pr[i];
         }
-        l[rt] = l[rt] * alpha + ps;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt][rt] *= alpha;
+        l[rt] += ps;
         // B operand of the second product: item j < 4 is key 4*(lane/16)+j of sub-block 0,
         // item j >= 4 the same key of sub-block 1 (the A operand below uses the same order).
         pb[rt] = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
@@ -283,7 +300,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     } else {
       const size_t u = orow * p.splits + split;
       if (lane < 16) {
-        p.ws_ml[2 * u] = m[rt];  // log2 domain; -inf for an empty or fully masked range
+        p.ws_ml[2 * u] = m[rt] * c;  // log2 domain; -inf for an empty or fully masked range
         p.ws_ml[2 * u + 1] = lt;
       }
 #pragma unroll
@@ -293,27 +310,31 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   }
 }
 
-// Combine the context splits of every (query row, head) in split order.
+// Combine the context splits of every (query row, head) in split order.  A thread owns four
+// head-dim values of one (row, head); the split maxima are loaded first, then the sums.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
-  constexpr int HPB = 256 / D;  // heads per block
-  const int row = blockIdx.x;
-  const int hq = blockIdx.y * HPB + threadIdx.x / D;
-  const int d = threadIdx.x % D;
-  if (hq >= p.num_q_heads) return;
-  const size_t u0 = ((size_t)row * p.num_q_heads + hq) * p.splits;
-  float M = kNegInf, lt = 0.f, a = 0.f;
-  for (int j = 0; j < p.splits; ++j) {
-    const float mj = p.ws_ml[2 * (u0 + j)];
-    if (mj == kNegInf) continue;  // empty range for this row
-    const float mn = fmaxf(M, mj);
-    const float c_old = fast_exp2(M - mn);
-    const float c_new = fast_exp2(mj - mn);
-    lt = lt * c_old + p.ws_ml[2 * (u0 + j) + 1] * c_new;
-    a = a * c_old + p.ws_acc[(u0 + j) * D + d] * c_new;
-    M = mn;
+  constexpr int TPH = D / 4;  // threads per (row, head)
+  const size_t unit = (size_t)blockIdx.x * (256 / TPH) + threadIdx.x / TPH;  // row * Hq + head
+  if (unit >= (size_t)p.total_q * p.num_q_heads) return;
+  const int d = 4 * (threadIdx.x % TPH);
+  const size_t u0 = unit * p.splits;
+  float M = kNegInf;
+  for (int j = 0; j < p.splits; ++j) M = fmaxf(M, p.ws_ml[2 * (u0 + j)]);
+  float lt = 0.f;
+  f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+  if (M != kNegInf) {
+    for (int j = 0; j < p.splits; ++j) {
+      const float mj = p.ws_ml[2 * (u0 + j)];
+      if (mj == kNegInf) continue;  // empty range for this row
+      const float w = fast_exp2(mj - M);
+      lt += p.ws_ml[2 * (u0 + j) + 1] * w;
+      a += *(const f32x4_t*)(p.ws_acc + (u0 + j) * D + d) * w;
+    }
   }
-  p.out[((size_t)row * p.num_q_heads + hq) * D + d] = to_bf16(lt > 0.f ? a / lt : 0.f);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  *(uint2*)(p.out + unit * D + d) =
+      make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
 }
 
 template <int D, int G>
@@ -328,8 +349,9 @@ hipError_t launch_dg(const PrefillParams& p, hipStream_t stream) {
   if (e != hipSuccess || p.splits == 1) return e;
   {
     TraceScope t("prefill_merge", stream);
-    constexpr int HPB = 256 / D;
-    const dim3 grid(p.total_q, (p.num_q_heads + HPB - 1) / HPB);
+    constexpr int UPB = 256 / (D / 4);  // (row, head) units per block
+    const size_t units = (size_t)p.total_q * p.num_q_heads;
+    const dim3 grid((unsigned)((units + UPB - 1) / UPB));
     hipLaunchKernelGGL((prefill_merge_kernel<D>), grid, dim3(256), 0, stream, p);
   }
   return hipGetLastError();
@@ -367,7 +389,7 @@ PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int gr
   const long long base = (long long)((max_q_len + tq - 1) / tq) * num_kv_heads * num_seqs;
   // Enough workgroups for four per CU, each range at least 256 keys, at most 16 ranges.
   long long want = (4LL * cu_count() + base - 1) / base;
-  if (const char* e = std::getenv("PA_PREFILL_SPLITS")) want = std::atoi(e);
+  if (const char* e = std::getenv("PA_PREFILL_SPLITS"); e && *e) want = std::atoi(e);
   want = std::min<long long>(std::max<long long>(want, 1), 16);
   want = std::min<long long>(want, std::max(1, max_seq_len / 256));
   if (want <= 1) return r;

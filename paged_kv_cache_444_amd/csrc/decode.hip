@@ -131,7 +131,7 @@ __device__ __forceinline__ int own_head(int c, int j) {
 // of the unit, one per lane, starting at logical block `win`.
 template <int D>
 __device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodeParams& p,
-                                          const int* bt, int blk_last, int& win, int& ids,
+                                          const int* bt, int& win, int& ids,
                                           size_t head_off, size_t block_elems) {
   constexpr int R = D / kSlice;
   constexpr int DL = D / 8;  // head-dim values per K-side lane
@@ -141,7 +141,7 @@ __device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodePar
   const int b = t0 >> (bs == 32 ? 5 : 4);
   if (b - win >= 64) {  // rare: refill the block-id window
     win = b;
-    const int id = (win + lane <= blk_last) ? bt[win + lane] : 0;
+    const int id = (win + lane < p.max_blocks_per_seq) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const int id = __builtin_amdgcn_readlane(ids, b - win);
@@ -315,11 +315,12 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   const int bs = p.block_size;
   const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int tok_end = min(L, (j0 + take) * kSub);
-  const int blk_last = (tok_end - 1) / bs;
   int win = (j0 * kSub) / bs;
   int ids;
   {
-    const int id = (win + lane <= blk_last) ? bt[win + lane] : 0;
+    // Read without waiting for the length: entries past the sequence's blocks are padding, and
+    // the steps below only ever use the sequence's own blocks.
+    const int id = (win + lane < p.max_blocks_per_seq) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const size_t tile = (size_t)bs * D;
@@ -353,33 +354,33 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   if constexpr (Depth == 0) {  // no prefetch: fewer registers, more resident waves
     while (true) {
       StepRegs<D> ra;
-      load_step<D>(ra, i, p, bt, blk_last, win, ids, head_off, block_elems);
+      load_step<D>(ra, i, p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else if constexpr (Depth == 1) {
     StepRegs<D> ra, rb;
-    load_step<D>(ra, i, p, bt, blk_last, win, ids, head_off, block_elems);
+    load_step<D>(ra, i, p, bt, win, ids, head_off, block_elems);
     while (true) {
-      load_step<D>(rb, min(i + 1, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      load_step<D>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D>(ra, min(i + 1, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      load_step<D>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(rb, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else {  // two steps in flight while one is computed
     StepRegs<D> r0, r1, r2;
-    load_step<D>(r0, i, p, bt, blk_last, win, ids, head_off, block_elems);
-    load_step<D>(r1, min(i + 1, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+    load_step<D>(r0, i, p, bt, win, ids, head_off, block_elems);
+    load_step<D>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
     while (true) {
-      load_step<D>(r2, min(i + 2, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      load_step<D>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(r0, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D>(r0, min(i + 2, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      load_step<D>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(r1, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D>(r1, min(i + 2, ilast), p, bt, blk_last, win, ids, head_off, block_elems);
+      load_step<D>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(r2, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
@@ -464,9 +465,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t p_lds[kWaves][2][G][8];
   extern __shared__ int seq_prefix[];  // [B+1] steps per KV head before each sequence (dynamic mode)
 
-  // Total steps of the batch.
-  long long mine = 0;
-  for (int s = threadIdx.x; s < B; s += kThreads) mine += steps_of(p, s);
+  // Total steps of the batch.  The first kThreads sequences' step counts stay in a register for
+  // the prefix sums below, so small batches read their lengths once.
+  const int n_first = (int)threadIdx.x < B ? steps_of(p, threadIdx.x) : 0;
+  long long mine = n_first;
+  for (int s = threadIdx.x + kThreads; s < B; s += kThreads) mine += steps_of(p, s);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
   if (lane == 0) sh_sum[wave] = mine;
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   long long base = 0;
   for (int c = 0; c < B; c += kThreads) {
     const int s = c + threadIdx.x;
-    const int n = s < B ? steps_of(p, s) : 0;
+    const int n = (c == 0) ? n_first : (s < B ? steps_of(p, s) : 0);
     const int incl = wave_inclusive_scan(n);
     if (lane == 63) sh_scan[wave] = incl;
     __syncthreads();
@@ -575,25 +578,34 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     lt[k] = 0.f;
     a[k] = 0.f;
   }
-  for (int w = info.x; w <= info.y; ++w) {
-    const float* slot = p.partials + (size_t)(w + u) * (G * (2 + D));
-    float mv[PER], lv[PER], av[PER];
+  // Four pieces per round: their loads are issued together, then combined in worker order.
+  constexpr int kRound = 4;
+  for (int w0 = info.x; w0 <= info.y; w0 += kRound) {
+    float mv[kRound][PER], lv[kRound][PER], av[kRound][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = threadIdx.x + 256 * k;
-      const int g = min(i, G * D - 1) / D;
-      mv[k] = slot[g];
-      lv[k] = slot[G + g];
-      av[k] = slot[2 * G + min(i, G * D - 1)];
+    for (int r = 0; r < kRound; ++r) {
+      const int w = min(w0 + r, info.y);
+      const float* slot = p.partials + (size_t)(w + u) * (G * (2 + D));
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = min(threadIdx.x + 256 * k, G * D - 1);
+        mv[r][k] = slot[i / D];
+        lv[r][k] = slot[G + i / D];
+        av[r][k] = slot[2 * G + i];
+      }
     }
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const float mn = fmaxf(M[k], mv[k]);
-      const float c_old = fast_exp2(M[k] - mn);  // M = -inf on the first piece: c_old = 0
-      const float c_new = fast_exp2(mv[k] - mn);
-      lt[k] = lt[k] * c_old + lv[k] * c_new;
-      a[k] = a[k] * c_old + av[k] * c_new;
-      M[k] = mn;
+    for (int r = 0; r < kRound; ++r) {
+      if (w0 + r > info.y) break;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const float mn = fmaxf(M[k], mv[r][k]);
+        const float c_old = fast_exp2(M[k] - mn);  // M = -inf on the first piece: c_old = 0
+        const float c_new = fast_exp2(mv[r][k] - mn);
+        lt[k] = lt[k] * c_old + lv[r][k] * c_new;
+        a[k] = a[k] * c_old + av[r][k] * c_new;
+        M[k] = mn;
+      }
     }
   }
 #pragma unroll

@@ -57,61 +57,53 @@ __device__ __forceinline__ f32x4_t mfma(const uint4& a, const uint4& b, f32x4_t 
 
 __device__ __forceinline__ float xor32_f32(float x) { return __shfl_xor(x, 32, 64); }
 
-// Copy of one 32-key tile (two sub-blocks) of K and V for KV head h into LDS, staged through
-// registers: each thread moves D/32 16-byte pieces.  Piece idx covers chunk idx / (2D) (K of
-// sub-block 0, K of sub-block 1, V of sub-block 0, V of sub-block 1), element 8*(idx % (2D)).
-template <int D>
-struct TileRegs {
-  uint4 v[D / 32];
-};
+// K/V tile pipeline.  kStages LDS stages each hold one 32-key tile as [K sub-block 0][K sub-block 1]
+// [V sub-block 0][V sub-block 1] (16*D elements each, in pool layout).  Wave w fetches region w
+// with D/32 direct global->LDS loads of 1 KB (lane l's 16 bytes land at 16*l), so every wave
+// issues the same number of loads per tile and a vmcnt wait releases exactly one tile without
+// touching registers.  Physical block ids come from an LDS copy of the table slice, so no other
+// vector-memory load is in flight inside the walk.
+constexpr int kStages = 3;
+constexpr int kMaxTableLds = 2048;  // block ids of one workgroup's key range
 
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const PrefillParams& p, const int* bt,
-                                          int h, int tile, int L) {
-  constexpr int kPieces = D / 32;
-  const int bs = p.block_size;
-  const size_t tile_elems = (size_t)bs * D;
-  const size_t block_elems = (size_t)p.num_kv_heads * tile_elems;
-#pragma unroll
-  for (int k = 0; k < kPieces; ++k) {
-    const int idx = threadIdx.x + kPThreads * k;
-    const int chunk = idx / (2 * D);
-    const int within = idx % (2 * D);
-    const int sub = chunk & 1;
-    const int key0 = tile * kKeyTile + 16 * sub;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (key0 < L) {
-      int id = bt[key0 / bs];
-      id = min(max(id, 0), (int)(p.num_blocks - 1));
-      const size_t off = (size_t)id * block_elems + (size_t)h * tile_elems +
-                         (size_t)(key0 % bs) * D + 8 * (size_t)within;
-      const uint16_t* pool = (chunk < 2) ? p.kpool : p.vpool;
-      val = *(const uint4*)(pool + off);
-      if (chunk >= 2 && key0 + 16 > L) {
-        // V rows: element (d, t) at d*16 + t; this piece holds tokens 8*(within&1) .. +7.
-        const int t0 = key0 + 8 * (within & 1);
-        uint32_t w[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = t0 + 2 * e;
-          const uint32_t keep = (t + 1 < L) ? 0xFFFFFFFFu : ((t < L) ? 0xFFFFu : 0u);
-          w[e] &= keep;
-        }
-        val = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
-    r.v[k] = val;
-  }
+// s_waitcnt with vmcnt(n) and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at lds + 16*l (M0 holds
+// the wave-uniform LDS address).  Written as inline assembly so the compiler does not treat every
+// later LDS access as dependent on it; the walk below waits for these loads explicitly.
+__device__ __forceinline__ void lds_dma_16(const uint16_t* src, lds_u16* dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* lds) {
-  // LDS tile: K sub-blocks 0 and 1 ([16*D] each), then V sub-blocks 0 and 1.
+__device__ __forceinline__ void issue_tile(const PrefillParams& p, const int* ids_lds, int blk0,
+                                           int h, int tile, int L, lds_u16* stage) {
+  constexpr int NP = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int r = threadIdx.x >> 6;  // region = wave
+  const int key0 = tile * kKeyTile + 16 * (r & 1);
+  const int bs = p.block_size;
+  // Keys at or past L fetch block 0 (always inside the pool): their V rows are zeroed before use
+  // and their scores are masked.
+  const int id = (key0 < L) ? ids_lds[min(max(key0 / bs - blk0, 0), kMaxTableLds - 1)] : 0;
+  const size_t tile_elems = (size_t)bs * D;
+  const uint16_t* src = ((r < 2) ? p.kpool : p.vpool) +
+                        ((size_t)id * p.num_kv_heads + h) * tile_elems +
+                        (size_t)(key0 % bs) * D + 8 * lane;
 #pragma unroll
-  for (int k = 0; k < D / 32; ++k) {
-    const int idx = threadIdx.x + kPThreads * k;
-    *(uint4*)(lds + 8 * (size_t)idx) = r.v[k];
-  }
+  for (int pc = 0; pc < NP; ++pc)
+    lds_dma_16(src + pc * 512, stage + r * 16 * D + pc * 512);
 }
 
 template <int D, int G>
@@ -122,7 +114,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   constexpr int ROWS = kPWaves * 16 * RT;
   constexpr int TQ = ROWS / G;     // query tokens per workgroup
   constexpr int TILE_ELEMS = 4 * 16 * D;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kStages][TILE_ELEMS];
+  __shared__ int ids_lds[kMaxTableLds];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -188,15 +181,48 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   const int t_first = kb / kKeyTile;
   const int t_end = (ke + kKeyTile - 1) / kKeyTile;  // empty range: t_end <= t_first
   const int diag = ctx + q0;  // keys above this need a per-row mask
+  // Table slice of this workgroup's keys [32*t_first, 32*t_end), clamped into the pool.
+  const int bs = p.block_size;
+  const int blk0 = (t_first * kKeyTile) / bs;
+  const int nblk = (t_first < t_end) ? min(kMaxTableLds, (min(t_end * kKeyTile, L) - 1) / bs - blk0 + 1)
+                                     : 0;
+  {
+    constexpr int kPer = kMaxTableLds / kPThreads;
+    int v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = threadIdx.x + kPThreads * k;
+      v[k] = (i < nblk) ? bt[blk0 + i] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = threadIdx.x + kPThreads * k;
+      ids_lds[i] = (i < nblk) ? min(max(v[k], 0), (int)(p.num_blocks - 1)) : 0;  // all valid ids
+    }
+  }
+  // Every ordinary vector-memory load (query rows, table slice) is complete before the walk, so
+  // the only loads in flight inside it are the tile loads counted by wait_vmcnt.
+  wait_vmcnt<0>();
+  __syncthreads();
   if (t_first < t_end) {
-    TileRegs<D> regs;
-    load_tile<D>(regs, p, bt, h, t_first, L);
-    store_tile<D>(regs, lds[0]);
-    __syncthreads();
-    int cur = 0;
+    constexpr int NP = D / 32;
+#pragma unroll
+    for (int k = 0; k < kStages - 1; ++k)
+      issue_tile<D>(p, ids_lds, blk0, h, min(t_first + k, t_end - 1), L, (lds_u16*)&lds[k][0]);
     for (int t = t_first; t < t_end; ++t) {
-      const bool more = t + 1 < t_end;  // block-uniform
-      if (more) load_tile<D>(regs, p, bt, h, t + 1, L);
+      const int cur = (t - t_first) % kStages;
+      wait_vmcnt<NP * (kStages - 2)>();  // this wave's part of tile t has landed
+      __syncthreads();                   // all parts landed; every wave is done with tile t-1
+      issue_tile<D>(p, ids_lds, blk0, h, min(t + kStages - 1, t_end - 1), L,
+                    (lds_u16*)&lds[(cur + kStages - 1) % kStages][0]);
+      if (t * kKeyTile + kKeyTile > L) {  // block-uniform: zero V rows of keys at or past L
+        uint16_t* vz = &lds[cur][2 * 16 * D];
+        for (int i = threadIdx.x; i < 2 * 16 * D; i += kPThreads) {
+          const int key = t * kKeyTile + 16 * (i / (16 * D)) + (i % 16);
+          if (key >= L) vz[i] = 0;
+        }
+        __syncthreads();
+      }
       const uint16_t* kl = lds[cur];
       const uint16_t* vl = lds[cur] + 2 * 16 * D;
 
@@ -273,10 +299,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[dt][rt] = mfma(va, pb[rt], acc[dt][rt]);
       }
-      if (more) store_tile<D>(regs, lds[cur ^ 1]);
-      __syncthreads();
-      cur ^= 1;
     }
+    wait_vmcnt<0>();  // no tile load may still be writing LDS when the workgroup ends
   }
 
   // Finish: row sums over the four lane groups, then normalise or hand the split's state over.
@@ -384,6 +408,9 @@ PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int gr
                            int max_seq_len) {
   PrefillSplit r{1, std::max(max_seq_len, 1)};
   if (num_seqs <= 0 || max_q_len <= 0 || max_seq_len <= 0) return r;
+  // One range's table slice must fit the LDS copy (kMaxTableLds entries of 16-token blocks).
+  const int max_keys = (kMaxTableLds - 2) * 16 / kKeyTile * kKeyTile;
+  const long long need = (max_seq_len + max_keys - 1) / max_keys;
   const int rows = kPWaves * 16 * (head_dim == 256 ? 1 : 2);
   const int tq = rows / group;
   const long long base = (long long)((max_q_len + tq - 1) / tq) * num_kv_heads * num_seqs;
@@ -392,6 +419,7 @@ PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int gr
   if (const char* e = std::getenv("PA_PREFILL_SPLITS"); e && *e) want = std::atoi(e);
   want = std::min<long long>(std::max<long long>(want, 1), 16);
   want = std::min<long long>(want, std::max(1, max_seq_len / 256));
+  want = std::max(want, need);
   if (want <= 1) return r;
   int keys = (int)((max_seq_len + want - 1) / want);
   keys = (keys + kKeyTile - 1) / kKeyTile * kKeyTile;

@@ -38,6 +38,7 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+#include <algorithm>
 #include <cstdlib>
 #include <map>
 #include <mutex>
@@ -57,6 +58,7 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr int kMaxPrefixSeqs = 4096;
 constexpr int kPrefixLdsBytes = (kMaxPrefixSeqs + 1) * 4;
 constexpr int kDynSlotsPerWorker = 2;
+constexpr int kBlocksPerCU = 1;
 
 __device__ __forceinline__ int clamped_len(const DecodeParams& p, int s) {
   return min(max(p.seq_lens[s], 0), p.len_cap);
@@ -287,11 +289,13 @@ __device__ __forceinline__ void compute_step(const StepRegs<D>& r, const uint4 (
 }
 
 // Steps j0 .. j0+take-1 of unit (s, h) by virtual worker w.  x is the global index of step j0.
-// Depth is the number of steps whose loads are in flight while one step is computed.
+// Depth is the number of steps whose loads are in flight while one step is computed.  With
+// `coop` set the wave's (m, l, acc) always goes to `coop` (its slot in LDS) and the workgroup
+// combines the slots; otherwise the piece is finished here.
 template <int D, int G, int Depth>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h, int j0, int take,
                                              int n_s, long long w, long long x, const Plan& plan,
-                                             uint16_t (*p_sh)[G][8]) {
+                                             uint16_t (*p_sh)[G][8], float* coop = nullptr) {
   constexpr int R = D / kSlice;
   constexpr int O = kOwn<G>;
   const int lane = threadIdx.x & 63;
@@ -299,8 +303,9 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   const int Hq = p.num_q_heads;
   const int L = uniform(clamped_len(p, s));
   const int u = s * p.num_kv_heads + h;
-  const bool whole = (j0 == 0) && (take == n_s);
-  if (j0 == 0 && lane == 0) p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1));
+  const bool whole = !coop && (j0 == 0) && (take == n_s);
+  if (!coop && j0 == 0 && lane == 0)
+    p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1));
 
   // This lane's head-dim slice of the G query rows sharing KV head h.
   uint4 q[G][D / 64];
@@ -398,7 +403,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
     y += __shfl_xor(y, 32, 64);
     lsum[j] = y;
   }
-  float* slot = p.partials + (size_t)(w + u) * (G * (2 + D));
+  float* slot = coop ? coop : p.partials + (size_t)(w + u) * (G * (2 + D));
   uint16_t* orow = p.out + ((size_t)s * Hq + (size_t)h * G) * D;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -421,11 +426,63 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   }
 }
 
-// Steps of virtual worker v, unit by unit.  (s, off) locate its first step: sequence s and offset
-// within that sequence's num_kv_heads * n_s steps.
+// A piece taken by the whole workgroup: wave r runs steps [j0 + take*r/kWaves,
+// j0 + take*(r+1)/kWaves) into its LDS slot, then the workgroup combines the slots in wave order
+// and writes the output (unit wholly inside the piece) or the piece's partial slot.  Contains
+// barriers: every wave of the block must call it with the same arguments.
 template <int D, int G, int Depth>
+__device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, int j0, int take,
+                                           int n_s, long long w, long long x, const Plan& plan,
+                                           uint16_t (*p_sh)[G][8], float (*st)[G * (2 + D)]) {
+  constexpr int PER = (G * D + kThreads - 1) / kThreads;
+  const int wave = threadIdx.x >> 6;
+  auto lo_of = [&](int r) { return j0 + (int)((long long)take * r / kWaves); };
+  const int a = lo_of(wave), b = lo_of(wave + 1);
+  if (b > a) decode_piece<D, G, Depth>(p, s, h, a, b - a, n_s, w, x + (a - j0), plan, p_sh, st[wave]);
+  __syncthreads();
+  const int u = s * p.num_kv_heads + h;
+  const bool whole = (j0 == 0) && (take == n_s);
+  if (j0 == 0 && threadIdx.x == 0)
+    p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1));
+  float* slot = p.partials + (size_t)(w + u) * (G * (2 + D));
+  uint16_t* orow = p.out + ((size_t)s * p.num_q_heads + (size_t)h * G) * D;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + kThreads * k;
+    if (i >= G * D) break;
+    const int g = i / D;
+    float M = kNegInf;
+#pragma unroll
+    for (int r = 0; r < kWaves; ++r)
+      if (lo_of(r + 1) > lo_of(r)) M = fmaxf(M, st[r][g]);
+    float lt = 0.f, acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < kWaves; ++r) {
+      if (lo_of(r + 1) > lo_of(r)) {
+        const float e = fast_exp2(st[r][g] - M);
+        lt += e * st[r][G + g];
+        acc += e * st[r][2 * G + i];
+      }
+    }
+    if (whole) {
+      orow[i] = to_bf16(acc / lt);
+    } else {
+      if (i % D == 0) {
+        slot[g] = M;
+        slot[G + g] = lt;
+      }
+      slot[2 * G + i] = acc;
+    }
+  }
+  __syncthreads();  // the slots are rewritten by the next piece
+}
+
+// Steps of virtual worker v, unit by unit.  (s, off) locate its first step: sequence s and offset
+// within that sequence's num_kv_heads * n_s steps.  Coop: each piece is shared by the workgroup.
+template <int D, int G, int Depth, bool Coop = false>
 __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& plan, long long v,
-                                           int s, long long off, uint16_t (*p_sh)[G][8]) {
+                                           int s, long long off, uint16_t (*p_sh)[G][8],
+                                           float (*st)[G * (2 + D)] = nullptr) {
   const int B = p.num_seqs, Hkv = p.num_kv_heads;
   long long x = plan.start(v);
   const long long x1 = plan.start(v + 1);
@@ -436,7 +493,8 @@ __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& pl
   int j = (int)(off % n_s);
   while (true) {
     const int take = (int)min((long long)(n_s - j), x1 - x);
-    decode_piece<D, G, Depth>(p, s, h, j, take, n_s, v, x, plan, p_sh);
+    if constexpr (Coop) coop_piece<D, G, Depth>(p, s, h, j, take, n_s, v, x, plan, p_sh, st);
+    else decode_piece<D, G, Depth>(p, s, h, j, take, n_s, v, x, plan, p_sh);
     x += take;
     if (x >= x1) break;
     j = 0;
@@ -463,6 +521,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ int sh_start_s[kWaves];
   __shared__ long long sh_start_off[kWaves];
   __shared__ __attribute__((aligned(16))) uint16_t p_lds[kWaves][2][G][8];
+  __shared__ unsigned sh_chunk;
+  __shared__ float coop_st[kWaves][G * (2 + D)];  // per-wave (m, l, acc) of a shared piece
   extern __shared__ int seq_prefix[];  // [B+1] steps per KV head before each sequence (dynamic mode)
 
   // Total steps of the batch.  The first kThreads sequences' step counts stay in a register for
@@ -530,14 +590,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __syncthreads();
 
   const long long w = wbase + wave;
-  if (w >= plan.ns) return;  // no barriers below
-  run_worker<D, G, Depth>(p, plan, w, sh_start_s[wave], sh_start_off[wave], p_lds[wave]);
-  if (!dynamic) return;
+  if (w < plan.ns)
+    run_worker<D, G, Depth>(p, plan, w, sh_start_s[wave], sh_start_off[wave], p_lds[wave]);
+  if (!dynamic) return;  // block-uniform
+
+  // Dynamic chunks, each shared by the whole workgroup (one counter increment per chunk; the
+  // next chunk is claimed while the current one runs).  In dynamic mode every wave has a static
+  // range (plan.ns == num_workers), so all waves reach these barriers.
+  if (threadIdx.x == 0) sh_chunk = atomicAdd(p.counter, 1u);
+  __syncthreads();
   while (true) {
-    unsigned d = 0;
-    if (lane == 0) d = atomicAdd(p.counter, 1u);
-    d = (unsigned)__shfl((int)d, 0, 64);
+    const unsigned d = sh_chunk;  // block-uniform
     if ((long long)d >= plan.nd) break;
+    unsigned nxt = 0;
+    if (threadIdx.x == 0) nxt = atomicAdd(p.counter, 1u);
     // Locate the chunk's first step: the last sequence whose prefix is <= x / Hkv.
     const long long x0 = plan.start(plan.ns + d);
     const long long xh = x0 / Hkv;
@@ -547,8 +613,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       if (seq_prefix[mid] <= xh) lo = mid;
       else hi = mid;
     }
-    run_worker<D, G, Depth>(p, plan, plan.ns + d, lo, x0 - (long long)seq_prefix[lo] * Hkv,
-                            p_lds[wave]);
+    run_worker<D, G, Depth, true>(p, plan, plan.ns + d, lo,
+                                  x0 - (long long)seq_prefix[lo] * Hkv, p_lds[wave], coop_st);
+    __syncthreads();  // every thread has read sh_chunk
+    if (threadIdx.x == 0) sh_chunk = nxt;
+    __syncthreads();
   }
 }
 
@@ -689,10 +758,11 @@ Ret dispatch(int D, int G, Ret fallback, F&& f) {
 
 int decode_workers(int head_dim, int group) {
   static std::mutex mu;
-  static std::map<std::pair<int, int>, int> cache;  // (device, variant) -> resident workgroups
+  // (device, variant) -> (default workgroups, resident workgroups)
+  static std::map<std::pair<int, int>, std::pair<int, int>> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  int blocks = 0;
+  std::pair<int, int> blocks{0, 0};
   {
     std::lock_guard<std::mutex> lk(mu);
     const auto key = std::make_pair(dev, (head_dim * 64 + group) * 4 + prefetch_depth());
@@ -708,16 +778,21 @@ int decode_workers(int head_dim, int group) {
       if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads,
                                                               kPrefixLdsBytes) != hipSuccess)
         return 0;
-      blocks = cus * std::max(per_cu, 1);
+      per_cu = std::max(per_cu, 1);
+      // One workgroup (one wave per SIMD) per CU by default: the kernel is bound by HBM
+      // bandwidth, and on the 70B-shaped batch a second resident wave per SIMD measured no
+      // more bytes moved, only more partial slots and merge work.
+      blocks = {cus * std::min(per_cu, kBlocksPerCU), cus * per_cu};
       cache[key] = blocks;
     }
   }
-  // Tuning and test override, read on every call: the total number of worker waves.
+  // Tuning and test override, read on every call: the total number of worker waves, at most
+  // what can be resident.
   if (const char* e = std::getenv("PA_DECODE_WORKERS"); e && *e) {
     const int v = std::atoi(e);
-    if (v >= kWaves) return std::min(v / kWaves, blocks) * kWaves;
+    if (v >= kWaves) return std::min(v / kWaves, blocks.second) * kWaves;
   }
-  return blocks * kWaves;
+  return blocks.first * kWaves;
 }
 
 DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group) {

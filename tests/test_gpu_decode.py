@@ -181,6 +181,25 @@ def test_decode_static_and_dynamic_splits(static_q10, chunk, monkeypatch):
     assert_close(upcast(outs[0])[seqs], ref[seqs], f"decode static {static_q10}/1024, chunk {chunk}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(16, 1, 64, 16), (8, 2, 128, 32), (8, 2, 256, 16),
+                                          (4, 4, 128, 16)])
+@pytest.mark.parametrize("chunk", [1, 3, 16])
+def test_decode_shared_chunks_shapes(Hq, Hkv, D, bs, chunk, monkeypatch):
+    """Dynamic chunks are shared by a workgroup's waves (some idle when a piece has fewer steps
+    than waves) and combined in LDS: every head shape must match the oracle, deterministically."""
+    case = build_case(Spec(name="shared", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           block_size=bs, seed=(26, Hq, D, bs),
+                           decode_lens=[1, 17, 300, 1000, 2049, 5, 640]))
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    monkeypatch.setenv("PA_DECODE_WORKERS", "8")
+    monkeypatch.setenv("PA_DECODE_STATIC_Q10", "600")
+    monkeypatch.setenv("PA_DECODE_CHUNK", str(chunk))
+    a = gpu_decode(case, kc, vc)
+    assert np.array_equal(a, gpu_decode(case, kc, vc))
+    assert_close(upcast(a), oracle_decode(case, case.key_cache, case.value_cache),
+                 f"shared chunks of {chunk} steps")
+
+
 def test_decode_workspace_sizes_on_device():
     n = pa.decode_workspace_bytes(128, 64, 8, 128, 8192)
     assert n >= 128 * 8 * 8 * (128 + 2) * 4  # at least one partial slot per unit

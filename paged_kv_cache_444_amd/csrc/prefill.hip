@@ -86,21 +86,45 @@ __device__ __forceinline__ void lds_dma_16(const uint16_t* src, lds_u16* dst) {
                : "memory", "m0");
 }
 
+// LDS layout of a stage (bank-conflict-free operand reads).  Each 1 KB piece keeps the pool's
+// content but permutes its 16-byte chunks:
+//   K piece (16 keys x 32 dims, 64 B per key): chunk c of key kk of sub-block sb sits in slot
+//       c ^ swz_k(sb, kk) of the key's row;
+//   V piece (32 dims x 16 keys, 32 B per dim): the 8-key half c of dim row r sits in slot
+//       c ^ swz_v(r).
+// The MFMA operand reads below (16 lanes: K rows of keys {0-3, 8-11} of both sub-blocks, or 16
+// consecutive V dims) then touch 16 distinct 16-byte bank groups, and any 8 consecutive lanes 8
+// distinct ones, so neither 32 nor 64 four-byte banks see a conflict.  The direct loads write a
+// piece linearly (lane l's 16 bytes at 16*l), so the permutation is applied to the source
+// address each lane fetches.
+__device__ __forceinline__ int swz_k(int sb, int kk) {
+  return (((kk >> 1) & 1) + 2 * (kk >> 3) + sb) & 3;
+}
+__device__ __forceinline__ int swz_v(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
 template <int D>
 __device__ __forceinline__ void issue_tile(const PrefillParams& p, const int* ids_lds, int blk0,
                                            int h, int tile, int L, lds_u16* stage) {
   constexpr int NP = D / 32;
   const int lane = threadIdx.x & 63;
-  const int r = threadIdx.x >> 6;  // region = wave
+  const int r = threadIdx.x >> 6;  // region = wave: K sub-block 0, K 1, V 0, V 1
   const int key0 = tile * kKeyTile + 16 * (r & 1);
   const int bs = p.block_size;
   // Keys at or past L fetch block 0 (always inside the pool): their V rows are zeroed before use
   // and their scores are masked.
   const int id = (key0 < L) ? ids_lds[min(max(key0 / bs - blk0, 0), kMaxTableLds - 1)] : 0;
   const size_t tile_elems = (size_t)bs * D;
+  int off;  // element offset inside a piece of the chunk this lane's slot holds
+  if (r < 2) {
+    const int kk = lane >> 2;
+    off = kk * 32 + 8 * ((lane & 3) ^ swz_k(r, kk));
+  } else {
+    const int row = lane >> 1;
+    off = row * 16 + 8 * ((lane & 1) ^ swz_v(row));
+  }
   const uint16_t* src = ((r < 2) ? p.kpool : p.vpool) +
                         ((size_t)id * p.num_kv_heads + h) * tile_elems +
-                        (size_t)(key0 % bs) * D + 8 * lane;
+                        (size_t)(key0 % bs) * D + off;
 #pragma unroll
   for (int pc = 0; pc < NP; ++pc)
     lds_dma_16(src + pc * 512, stage + r * 16 * D + pc * 512);
@@ -218,7 +242,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       if (t * kKeyTile + kKeyTile > L) {  // block-uniform: zero V rows of keys at or past L
         uint16_t* vz = &lds[cur][2 * 16 * D];
         for (int i = threadIdx.x; i < 2 * 16 * D; i += kPThreads) {
-          const int key = t * kKeyTile + 16 * (i / (16 * D)) + (i % 16);
+          const int e = i % (16 * D);  // dim row e / 16, slot (e / 8) % 2, element e % 8
+          const int kk = 8 * (((e >> 3) & 1) ^ swz_v((e >> 4) & 31)) + (e & 7);
+          const int key = t * kKeyTile + 16 * (i / (16 * D)) + kk;
           if (key >= L) vz[i] = 0;
         }
         __syncthreads();
@@ -226,16 +252,20 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       const uint16_t* kl = lds[cur];
       const uint16_t* vl = lds[cur] + 2 * 16 * D;
 
-      // Scores for keys 32t + 16kt + 4*(lane/16) + i.
+      // Scores.  Row m of product kt is key 8*(m/4) + m%4 + 4*kt of the tile, so lane l gets
+      // keys 8*(l/16) + 4*kt + i: eight consecutive keys of one sub-block, the B operand layout
+      // the second product needs.
       f32x4_t sc[2][RT];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        const int key = 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * kt;
+        const int sbk = key >> 4, kk = key & 15;
+        const uint16_t* krow = kl + sbk * 16 * D + kk * 32 + 8 * ((lane >> 4) ^ swz_k(sbk, kk));
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) sc[kt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint4 ka =
-              *(const uint4*)(kl + kt * 16 * D + ks * 512 + (lane & 15) * 32 + 8 * (lane >> 4));
+          const uint4 ka = *(const uint4*)(krow + ks * 512);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) sc[kt][rt] = mfma(ka, qb[rt][ks], sc[kt][rt]);
         }
@@ -251,7 +281,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
           for (int i = 0; i < 4; ++i) {
             float v = sc[kt][rt][i];
             if (masked) {
-              const int key = t * kKeyTile + 16 * kt + 4 * (lane >> 4) + i;
+              const int key = t * kKeyTile + 8 * (lane >> 4) + 4 * kt + i;
               v = (key <= row_lim[rt]) ? v : kNegInf;
             }
             x[4 * kt + i] = v;
@@ -285,17 +315,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
           ps += pr[i];
         }
         l[rt] += ps;
-        // B operand of the second product: item j < 4 is key 4*(lane/16)+j of sub-block 0,
-        // item j >= 4 the same key of sub-block 1 (the A operand below uses the same order).
+        // B operand of the second product: item j is key 8*(lane/16) + j of the tile (the A
+        // operand below uses the same order).
         pb[rt] = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                             pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
       }
+      // A operand: dim 16dt + lane%16, keys 8g .. 8g+7 (g = lane/16), i.e. half g%2 of the
+      // dim's row in V sub-block g/2.
+      const int g = lane >> 4;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 16 * dt + (lane & 15);
-        const uint2 v0 = *(const uint2*)(vl + d * 16 + 4 * (lane >> 4));
-        const uint2 v1 = *(const uint2*)(vl + 16 * D + d * 16 + 4 * (lane >> 4));
-        const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        const uint4 va =
+            *(const uint4*)(vl + (g >> 1) * 16 * D + d * 16 + 8 * ((g & 1) ^ swz_v(d & 31)));
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[dt][rt] = mfma(va, pb[rt], acc[dt][rt]);
       }

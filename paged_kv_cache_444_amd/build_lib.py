@@ -22,6 +22,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",
     # Packed fp32 VALU forms are kept out of the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core accumulators in ordinary VGPRs: the prefill walk rescales them with vector
+    # ops, which on accumulation registers costs a copy of every accumulator per key tile.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

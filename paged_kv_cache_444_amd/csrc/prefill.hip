@@ -33,6 +33,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 namespace pa {
 namespace {
@@ -75,11 +76,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at lds + 16*l (M0 holds
-// the wave-uniform LDS address).  Written as inline assembly so the compiler does not treat every
-// later LDS access as dependent on it; the walk below waits for these loads explicitly.
-__device__ __forceinline__ void lds_dma_16(const uint16_t* src, lds_u16* dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at LDS byte address
+// m0 + 16*l (m0 wave-uniform).  No immediate offset: on these loads it would move the LDS
+// destination as well as the source.  Written as inline assembly so the compiler does not treat
+// every later LDS access as dependent on it; the walk below waits for these loads explicitly.
+__device__ __forceinline__ void lds_dma_16(const uint16_t* src, unsigned m0) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "s"(m0)
@@ -102,32 +103,54 @@ __device__ __forceinline__ int swz_k(int sb, int kk) {
 }
 __device__ __forceinline__ int swz_v(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
+// Where this wave's tile loads come from and go to.  Wave r fetches region r of every tile
+// (K sub-block 0, K 1, V 0, V 1); everything but `base` is wave-uniform.
+struct TileSrc {
+  const uint16_t* base;  // pool + KV head h + this lane's chunk offset inside a piece
+  long long block_stride;  // elements per physical block (all KV heads)
+  unsigned lds;          // LDS byte address of region r in stage 0
+  int r, shift, bmask;   // region, log2(block_size), block_size - 1
+  int max_id;            // num_blocks - 1
+};
+
 template <int D>
-__device__ __forceinline__ void issue_tile(const PrefillParams& p, const int* ids_lds, int blk0,
-                                           int h, int tile, int L, lds_u16* stage) {
-  constexpr int NP = D / 32;
+__device__ __forceinline__ TileSrc tile_src(const PrefillParams& p, int h, const void* lds0) {
   const int lane = threadIdx.x & 63;
-  const int r = threadIdx.x >> 6;  // region = wave: K sub-block 0, K 1, V 0, V 1
-  const int key0 = tile * kKeyTile + 16 * (r & 1);
-  const int bs = p.block_size;
-  // Keys at or past L fetch block 0 (always inside the pool): their V rows are zeroed before use
-  // and their scores are masked.
-  const int id = (key0 < L) ? ids_lds[min(max(key0 / bs - blk0, 0), kMaxTableLds - 1)] : 0;
-  const size_t tile_elems = (size_t)bs * D;
+  TileSrc ts;
+  ts.r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  ts.shift = (p.block_size == 32) ? 5 : 4;
+  ts.bmask = p.block_size - 1;
+  ts.block_stride = (long long)p.num_kv_heads * p.block_size * D;
+  ts.max_id = (int)(p.num_blocks - 1);
   int off;  // element offset inside a piece of the chunk this lane's slot holds
-  if (r < 2) {
+  if (ts.r < 2) {
     const int kk = lane >> 2;
-    off = kk * 32 + 8 * ((lane & 3) ^ swz_k(r, kk));
+    off = kk * 32 + 8 * ((lane & 3) ^ swz_k(ts.r, kk));
   } else {
     const int row = lane >> 1;
     off = row * 16 + 8 * ((lane & 1) ^ swz_v(row));
   }
-  const uint16_t* src = ((r < 2) ? p.kpool : p.vpool) +
-                        ((size_t)id * p.num_kv_heads + h) * tile_elems +
-                        (size_t)(key0 % bs) * D + off;
+  ts.base = ((ts.r < 2) ? p.kpool : p.vpool) + (size_t)h * p.block_size * D + off;
+  const unsigned l0 = (unsigned)(uintptr_t)(const lds_u16*)lds0;
+  ts.lds = __builtin_amdgcn_readfirstlane(l0 + (unsigned)ts.r * 16 * D * 2);
+  return ts;
+}
+
+template <int D>
+__device__ __forceinline__ void issue_tile(const TileSrc& ts, const int* ids_lds, int blk0,
+                                           int tile, int L, int stage) {
+  constexpr int NP = D / 32;
+  const int key0 = tile * kKeyTile + 16 * (ts.r & 1);
+  // Keys at or past L fetch block 0 (always inside the pool): their V rows are zeroed before use
+  // and their scores are masked.
+  int id = 0;
+  if (key0 < L) id = ids_lds[min(max((key0 >> ts.shift) - blk0, 0), kMaxTableLds - 1)];
+  id = min(max(__builtin_amdgcn_readfirstlane(id), 0), ts.max_id);  // stays inside the pool
+  const uint16_t* src = ts.base + (long long)id * ts.block_stride + (key0 & ts.bmask) * D;
+  const unsigned m0 = ts.lds + (unsigned)stage * (4 * 16 * D * 2);
+  // Piece pc (1 KB) sits at byte offset 1024*pc of source and destination.
 #pragma unroll
-  for (int pc = 0; pc < NP; ++pc)
-    lds_dma_16(src + pc * 512, stage + r * 16 * D + pc * 512);
+  for (int pc = 0; pc < NP; ++pc) lds_dma_16(src + pc * 512, m0 + pc * 1024);
 }
 
 template <int D, int G>
@@ -230,15 +253,20 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   __syncthreads();
   if (t_first < t_end) {
     constexpr int NP = D / 32;
+    const TileSrc ts = tile_src<D>(p, h, &lds[0][0]);
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k)
-      issue_tile<D>(p, ids_lds, blk0, h, min(t_first + k, t_end - 1), L, (lds_u16*)&lds[k][0]);
-    for (int t = t_first; t < t_end; ++t) {
+      issue_tile<D>(ts, ids_lds, blk0, min(t_first + k, t_end - 1), L, k);
+    // One key tile.  kMasked: the tile reaches past the first row's diagonal and the causal mask
+    // is applied per score; those tiles are the last ones of the walk, so the two variants run
+    // as two loops and the other tiles carry no per-score selects.
+    auto walk_tile = [&](int t, auto masked_c) __attribute__((always_inline)) {
+      constexpr bool kMasked = decltype(masked_c)::value;
       const int cur = (t - t_first) % kStages;
       wait_vmcnt<NP * (kStages - 2)>();  // this wave's part of tile t has landed
       __syncthreads();                   // all parts landed; every wave is done with tile t-1
-      issue_tile<D>(p, ids_lds, blk0, h, min(t + kStages - 1, t_end - 1), L,
-                    (lds_u16*)&lds[(cur + kStages - 1) % kStages][0]);
+      issue_tile<D>(ts, ids_lds, blk0, min(t + kStages - 1, t_end - 1), L,
+                    (cur + kStages - 1) % kStages);
       if (t * kKeyTile + kKeyTile > L) {  // block-uniform: zero V rows of keys at or past L
         uint16_t* vz = &lds[cur][2 * 16 * D];
         for (int i = threadIdx.x; i < 2 * 16 * D; i += kPThreads) {
@@ -270,68 +298,74 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
           for (int rt = 0; rt < RT; ++rt) sc[kt][rt] = mfma(ka, qb[rt][ks], sc[kt][rt]);
         }
       }
-      const bool masked = t * kKeyTile + kKeyTile - 1 > diag;  // block-uniform
-      uint4 pb[RT];
+      {
+        uint4 pb[RT];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        float x[8];  // raw scores; -inf where masked
+        for (int rt = 0; rt < RT; ++rt) {
+          float x[8];  // raw scores; -inf where masked
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = sc[kt][rt][i];
-            if (masked) {
-              const int key = t * kKeyTile + 8 * (lane >> 4) + 4 * kt + i;
-              v = (key <= row_lim[rt]) ? v : kNegInf;
+            for (int i = 0; i < 4; ++i) {
+              float v = sc[kt][rt][i];
+              if constexpr (kMasked) {
+                const int key = t * kKeyTile + 8 * (lane >> 4) + 4 * kt + i;
+                v = (key <= row_lim[rt]) ? v : kNegInf;
+              }
+              x[4 * kt + i] = v;
             }
-            x[4 * kt + i] = v;
+          // The running max is raised (and acc rescaled) only when a score exceeds it by the
+          // slack, so probabilities stay below 2^slack and the accumulators are rarely touched.
+          bool raise = false;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) raise |= x[i] > thr[rt];
+          if (__ballot(raise)) {
+            float mx = x[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+            mx = fmaxf(mx, xor16_f32(mx));
+            mx = fmaxf(mx, xor32_f32(mx));
+            const float mn = fmaxf(m[rt], mx);  // raw units
+            if (mn != kNegInf && mn != m[rt]) {
+              const float alpha = fast_exp2((m[rt] - mn) * c);  // 0 when the old max is -inf
+              l[rt] *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) acc[dt][rt] *= alpha;
+              m[rt] = mn;
+              nmc[rt] = -mn * c;
+              thr[rt] = mn + slack_raw;
+            }
           }
-        // The running max is raised (and acc rescaled) only when a score exceeds it by the slack,
-        // so probabilities stay below 2^slack and the accumulators are rarely touched.
-        bool raise = false;
+          float pr[8], ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) raise |= x[i] > thr[rt];
-        if (__ballot(raise)) {
-          float mx = x[0];
-#pragma unroll
-          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-          mx = fmaxf(mx, xor16_f32(mx));
-          mx = fmaxf(mx, xor32_f32(mx));
-          const float mn = fmaxf(m[rt], mx);  // raw units
-          if (mn != kNegInf && mn != m[rt]) {
-            const float alpha = fast_exp2((m[rt] - mn) * c);  // 0 when the old max is -inf
-            l[rt] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt][rt] *= alpha;
-            m[rt] = mn;
-            nmc[rt] = -mn * c;
-            thr[rt] = mn + slack_raw;
+          for (int i = 0; i < 8; ++i) {
+            pr[i] = fast_exp2(__builtin_fmaf(x[i], c, nmc[rt]));
+            ps += pr[i];
           }
+          l[rt] += ps;
+          // B operand of the second product: item j is key 8*(lane/16) + j of the tile (the A
+          // operand below uses the same order).
+          pb[rt] = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                              pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
         }
-        float pr[8], ps = 0.f;
+        // A operand: dim 16dt + lane%16, keys 8g .. 8g+7 (g = lane/16), i.e. half g%2 of the
+        // dim's row in V sub-block g/2.
+        const int g = lane >> 4;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pr[i] = fast_exp2(__builtin_fmaf(x[i], c, nmc[rt]));
-          ps += pr[i];
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 16 * dt + (lane & 15);
+          const uint4 va =
+              *(const uint4*)(vl + (g >> 1) * 16 * D + d * 16 + 8 * ((g & 1) ^ swz_v(d & 31)));
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[dt][rt] = mfma(va, pb[rt], acc[dt][rt]);
         }
-        l[rt] += ps;
-        // B operand of the second product: item j is key 8*(lane/16) + j of the tile (the A
-        // operand below uses the same order).
-        pb[rt] = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                            pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
       }
-      // A operand: dim 16dt + lane%16, keys 8g .. 8g+7 (g = lane/16), i.e. half g%2 of the
-      // dim's row in V sub-block g/2.
-      const int g = lane >> 4;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 16 * dt + (lane & 15);
-        const uint4 va =
-            *(const uint4*)(vl + (g >> 1) * 16 * D + d * 16 + 8 * ((g & 1) ^ swz_v(d & 31)));
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[dt][rt] = mfma(va, pb[rt], acc[dt][rt]);
-      }
-    }
+    };
+    // Tile t needs the mask iff 32t + 31 > diag.
+    const int t_mask = min(max((diag + 1) / kKeyTile, t_first), t_end);
+    int t = t_first;
+    for (; t < t_mask; ++t) walk_tile(t, std::false_type{});
+    for (; t < t_end; ++t) walk_tile(t, std::true_type{});
     wait_vmcnt<0>();  // no tile load may still be writing LDS when the workgroup ends
   }
 

@@ -280,85 +280,101 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       const uint16_t* kl = lds[cur];
       const uint16_t* vl = lds[cur] + 2 * 16 * D;
 
-      // Scores.  Row m of product kt is key 8*(m/4) + m%4 + 4*kt of the tile, so lane l gets
-      // keys 8*(l/16) + 4*kt + i: eight consecutive keys of one sub-block, the B operand layout
-      // the second product needs.
-      f32x4_t sc[2][RT];
+      // K fragments, the A operands of the score product, shared by the row tiles.  Row m of
+      // product kt is key 8*(m/4) + m%4 + 4*kt of the tile, so lane l gets keys
+      // 8*(l/16) + 4*kt + i: eight consecutive keys of one sub-block, the B operand layout the
+      // second product needs.
+      uint4 kf[2][KS];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int key = 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * kt;
         const int sbk = key >> 4, kk = key & 15;
         const uint16_t* krow = kl + sbk * 16 * D + kk * 32 + 8 * ((lane >> 4) ^ swz_k(sbk, kk));
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) sc[kt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 ka = *(const uint4*)(krow + ks * 512);
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) sc[kt][rt] = mfma(ka, qb[rt][ks], sc[kt][rt]);
-        }
+        for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = *(const uint4*)(krow + ks * 512);
       }
-      {
-        uint4 pb[RT];
+      // V fragments, the A operands of the second product: dim 16dt + lane%16, keys 8g .. 8g+7
+      // (g = lane/16), i.e. half g%2 of the dim's row in V sub-block g/2.
+      const int g = lane >> 4;
+      auto v_frag = [&](int dt) __attribute__((always_inline)) {
+        const int d = 16 * dt + (lane & 15);
+        return *(const uint4*)(vl + (g >> 1) * 16 * D + d * 16 + 8 * ((g & 1) ^ swz_v(d & 31)));
+      };
+      auto scores = [&](int rt, f32x4_t (&sc)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          float x[8];  // raw scores; -inf where masked
+        for (int kt = 0; kt < 2; ++kt) {
+          sc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float v = sc[kt][rt][i];
-              if constexpr (kMasked) {
-                const int key = t * kKeyTile + 8 * (lane >> 4) + 4 * kt + i;
-                v = (key <= row_lim[rt]) ? v : kNegInf;
-              }
-              x[4 * kt + i] = v;
-            }
-          // The running max is raised (and acc rescaled) only when a score exceeds it by the
-          // slack, so probabilities stay below 2^slack and the accumulators are rarely touched.
-          bool raise = false;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) raise |= x[i] > thr[rt];
-          if (__ballot(raise)) {
-            float mx = x[0];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-            mx = fmaxf(mx, xor16_f32(mx));
-            mx = fmaxf(mx, xor32_f32(mx));
-            const float mn = fmaxf(m[rt], mx);  // raw units
-            if (mn != kNegInf && mn != m[rt]) {
-              const float alpha = fast_exp2((m[rt] - mn) * c);  // 0 when the old max is -inf
-              l[rt] *= alpha;
-#pragma unroll
-              for (int dt = 0; dt < DT; ++dt) acc[dt][rt] *= alpha;
-              m[rt] = mn;
-              nmc[rt] = -mn * c;
-              thr[rt] = mn + slack_raw;
-            }
-          }
-          float pr[8], ps = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            pr[i] = fast_exp2(__builtin_fmaf(x[i], c, nmc[rt]));
-            ps += pr[i];
-          }
-          l[rt] += ps;
-          // B operand of the second product: item j is key 8*(lane/16) + j of the tile (the A
-          // operand below uses the same order).
-          pb[rt] = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                              pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
+          for (int ks = 0; ks < KS; ++ks) sc[kt] = mfma(kf[kt][ks], qb[rt][ks], sc[kt]);
         }
-        // A operand: dim 16dt + lane%16, keys 8g .. 8g+7 (g = lane/16), i.e. half g%2 of the
-        // dim's row in V sub-block g/2.
-        const int g = lane >> 4;
+      };
+      // Online softmax of row tile rt, then its second product with the V fragments vf.
+      auto softmax_pv = [&](int rt, const f32x4_t (&sc)[2], auto&& vf)
+                            __attribute__((always_inline)) {
+        float x[8];  // raw scores; -inf where masked
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int d = 16 * dt + (lane & 15);
-          const uint4 va =
-              *(const uint4*)(vl + (g >> 1) * 16 * D + d * 16 + 8 * ((g & 1) ^ swz_v(d & 31)));
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc[dt][rt] = mfma(va, pb[rt], acc[dt][rt]);
+          for (int i = 0; i < 4; ++i) {
+            float v = sc[kt][i];
+            if constexpr (kMasked) {
+              const int key = t * kKeyTile + 8 * (lane >> 4) + 4 * kt + i;
+              v = (key <= row_lim[rt]) ? v : kNegInf;
+            }
+            x[4 * kt + i] = v;
+          }
+        // The running max is raised (and acc rescaled) only when a score exceeds it by the
+        // slack, so probabilities stay below 2^slack and the accumulators are rarely touched.
+        bool raise = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) raise |= x[i] > thr[rt];
+        if (__ballot(raise)) {
+          float mx = x[0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+          mx = fmaxf(mx, xor16_f32(mx));
+          mx = fmaxf(mx, xor32_f32(mx));
+          const float mn = fmaxf(m[rt], mx);  // raw units
+          if (mn != kNegInf && mn != m[rt]) {
+            const float alpha = fast_exp2((m[rt] - mn) * c);  // 0 when the old max is -inf
+            l[rt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt][rt] *= alpha;
+            m[rt] = mn;
+            nmc[rt] = -mn * c;
+            thr[rt] = mn + slack_raw;
+          }
         }
+        float pr[8], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pr[i] = fast_exp2(__builtin_fmaf(x[i], c, nmc[rt]));
+          ps += pr[i];
+        }
+        l[rt] += ps;
+        // B operand of the second product: item j is key 8*(lane/16) + j of the tile (the V
+        // fragments use the same order).
+        const uint4 pb = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                    pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = mfma(vf(dt), pb, acc[dt][rt]);
+      };
+      if constexpr (RT == 2) {
+        // Row tile 1's scores are issued before row tile 0's softmax and row tile 0's second
+        // product before row tile 1's softmax, so the matrix cores run while the vector ALUs do.
+        uint4 vf[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vf[dt] = v_frag(dt);
+        auto vreg = [&](int dt) __attribute__((always_inline)) { return vf[dt]; };
+        f32x4_t s0[2], s1[2];
+        scores(0, s0);
+        scores(1, s1);
+        softmax_pv(0, s0, vreg);
+        softmax_pv(1, s1, vreg);
+      } else {
+        f32x4_t s0[2];
+        scores(0, s0);
+        softmax_pv(0, s0, v_frag);
       }
     };
     // Tile t needs the mask iff 32t + 31 > diag.

@@ -58,13 +58,19 @@ __device__ __forceinline__ f32x4_t mfma(const uint4& a, const uint4& b, f32x4_t 
 
 __device__ __forceinline__ float xor32_f32(float x) { return __shfl_xor(x, 32, 64); }
 
-// K/V tile pipeline.  kStages LDS stages each hold one 32-key tile as [K sub-block 0][K sub-block 1]
-// [V sub-block 0][V sub-block 1] (16*D elements each, in pool layout).  Wave w fetches region w
-// with D/32 direct global->LDS loads of 1 KB (lane l's 16 bytes land at 16*l), so every wave
-// issues the same number of loads per tile and a vmcnt wait releases exactly one tile without
+// K/V tile pipeline.  kStages LDS stages each hold one 32-key tile in operand order: the K
+// pieces [kt][ks] of the score product, then the V pieces [dt] of the second product, each 1 KB
+// piece holding the 16-byte MFMA operand of lane l at 16*l, so every operand read is one linear
+// ds_read_b128.  Wave 0 fetches the K pieces of product kt = 0, wave 1 those of kt = 1, waves 2
+// and 3 half of the V pieces each, with D/32 direct global->LDS loads of 1 KB (lane l's 16 bytes
+// land at 16*l); each lane's source address picks its own key's physical block.  Every wave
+// issues the same number of loads per tile, so a vmcnt wait releases exactly one tile without
 // touching registers.  Physical block ids come from an LDS copy of the table slice, so no other
 // vector-memory load is in flight inside the walk.
-constexpr int kStages = 3;
+#ifndef PA_PREFILL_STAGES
+#define PA_PREFILL_STAGES 3
+#endif
+constexpr int kStages = PA_PREFILL_STAGES;
 constexpr int kMaxTableLds = 2048;  // block ids of one workgroup's key range
 
 // s_waitcnt with vmcnt(n) and no wait on the other counters (gfx9 encoding).
@@ -87,52 +93,46 @@ __device__ __forceinline__ void lds_dma_16(const uint16_t* src, unsigned m0) {
                : "memory", "m0");
 }
 
-// LDS layout of a stage (bank-conflict-free operand reads).  Each 1 KB piece keeps the pool's
-// content but permutes its 16-byte chunks:
-//   K piece (16 keys x 32 dims, 64 B per key): chunk c of key kk of sub-block sb sits in slot
-//       c ^ swz_k(sb, kk) of the key's row;
-//   V piece (32 dims x 16 keys, 32 B per dim): the 8-key half c of dim row r sits in slot
-//       c ^ swz_v(r).
-// The MFMA operand reads below (16 lanes: K rows of keys {0-3, 8-11} of both sub-blocks, or 16
-// consecutive V dims) then touch 16 distinct 16-byte bank groups, and any 8 consecutive lanes 8
-// distinct ones, so neither 32 nor 64 four-byte banks see a conflict.  The direct loads write a
-// piece linearly (lane l's 16 bytes at 16*l), so the permutation is applied to the source
-// address each lane fetches.
-__device__ __forceinline__ int swz_k(int sb, int kk) {
-  return (((kk >> 1) & 1) + 2 * (kk >> 3) + sb) & 3;
-}
-__device__ __forceinline__ int swz_v(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
-
-// Where this wave's tile loads come from and go to.  Wave r fetches region r of every tile
-// (K sub-block 0, K 1, V 0, V 1); everything but `base` is wave-uniform.
+// Where this wave's tile loads come from and go to; everything but `pool` and `sb` is
+// wave-uniform.
 struct TileSrc {
-  const uint16_t* base;  // pool + KV head h + this lane's chunk offset inside a piece
+  const uint16_t* pool;    // K or V pool + KV head h + this lane's offset inside a piece
   long long block_stride;  // elements per physical block (all KV heads)
-  unsigned lds;          // LDS byte address of region r in stage 0
-  int r, shift, bmask;   // region, log2(block_size), block_size - 1
-  int max_id;            // num_blocks - 1
+  unsigned lds;            // LDS byte address of this wave's first piece in stage 0
+  int sb;                  // sub-block (0: keys 0-15 of the tile, 1: keys 16-31) of this lane
+  int piece_step;          // source elements between this wave's consecutive pieces
+  int shift, bmask, max_id;  // log2(block_size), block_size - 1, num_blocks - 1
 };
 
+// Lane l of K piece (kt, ks): key kappa = 8*((l%16)/4) + l%4 + 4*kt of the tile, dims
+// 32*ks + 8*(l/16) .. +7.  Lane l of V piece dt: dim 16*dt + l%16, keys 8*(l/16) .. +7.
 template <int D>
 __device__ __forceinline__ TileSrc tile_src(const PrefillParams& p, int h, const void* lds0) {
+  constexpr int KS = D / 32, DT = D / 16;
   const int lane = threadIdx.x & 63;
+  const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   TileSrc ts;
-  ts.r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   ts.shift = (p.block_size == 32) ? 5 : 4;
   ts.bmask = p.block_size - 1;
-  ts.block_stride = (long long)p.num_kv_heads * p.block_size * D;
   ts.max_id = (int)(p.num_blocks - 1);
-  int off;  // element offset inside a piece of the chunk this lane's slot holds
-  if (ts.r < 2) {
-    const int kk = lane >> 2;
-    off = kk * 32 + 8 * ((lane & 3) ^ swz_k(ts.r, kk));
-  } else {
-    const int row = lane >> 1;
-    off = row * 16 + 8 * ((lane & 1) ^ swz_v(row));
+  ts.block_stride = (long long)p.num_kv_heads * p.block_size * D;
+  int off, first_piece;
+  if (r < 2) {  // K of product kt = r; the pool sub-block layout is [D/32][16 keys][32 dims]
+    const int key = 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * r;
+    ts.sb = key >> 4;
+    off = (key & 15) * 32 + 8 * (lane >> 4);
+    ts.piece_step = 512;
+    first_piece = r * KS;
+  } else {  // V pieces dt = (r-2)*DT/2 ..; the pool sub-block layout is [D dims][16 keys]
+    const int g = lane >> 4;
+    ts.sb = g >> 1;
+    off = ((r - 2) * (DT / 2) * 16 + (lane & 15)) * 16 + 8 * (g & 1);
+    ts.piece_step = 256;
+    first_piece = 2 * KS + (r - 2) * (DT / 2);
   }
-  ts.base = ((ts.r < 2) ? p.kpool : p.vpool) + (size_t)h * p.block_size * D + off;
+  ts.pool = ((r < 2) ? p.kpool : p.vpool) + (size_t)h * p.block_size * D + off;
   const unsigned l0 = (unsigned)(uintptr_t)(const lds_u16*)lds0;
-  ts.lds = __builtin_amdgcn_readfirstlane(l0 + (unsigned)ts.r * 16 * D * 2);
+  ts.lds = __builtin_amdgcn_readfirstlane(l0 + (unsigned)first_piece * 1024);
   return ts;
 }
 
@@ -140,17 +140,21 @@ template <int D>
 __device__ __forceinline__ void issue_tile(const TileSrc& ts, const int* ids_lds, int blk0,
                                            int tile, int L, int stage) {
   constexpr int NP = D / 32;
-  const int key0 = tile * kKeyTile + 16 * (ts.r & 1);
-  // Keys at or past L fetch block 0 (always inside the pool): their V rows are zeroed before use
-  // and their scores are masked.
-  int id = 0;
-  if (key0 < L) id = ids_lds[min(max((key0 >> ts.shift) - blk0, 0), kMaxTableLds - 1)];
-  id = min(max(__builtin_amdgcn_readfirstlane(id), 0), ts.max_id);  // stays inside the pool
-  const uint16_t* src = ts.base + (long long)id * ts.block_stride + (key0 & ts.bmask) * D;
-  const unsigned m0 = ts.lds + (unsigned)stage * (4 * 16 * D * 2);
-  // Piece pc (1 KB) sits at byte offset 1024*pc of source and destination.
+  // Physical blocks of the tile's two sub-blocks.  Keys at or past L fetch block 0 (always
+  // inside the pool): their V rows are zeroed before use and their scores are masked.
+  long long base[2];
 #pragma unroll
-  for (int pc = 0; pc < NP; ++pc) lds_dma_16(src + pc * 512, m0 + pc * 1024);
+  for (int sb = 0; sb < 2; ++sb) {
+    const int key0 = tile * kKeyTile + 16 * sb;
+    int id = 0;
+    if (key0 < L) id = ids_lds[min(max((key0 >> ts.shift) - blk0, 0), kMaxTableLds - 1)];
+    id = min(max(__builtin_amdgcn_readfirstlane(id), 0), ts.max_id);  // stays inside the pool
+    base[sb] = (long long)id * ts.block_stride + (long long)(key0 & ts.bmask) * D;
+  }
+  const uint16_t* src = ts.pool + (ts.sb ? base[1] : base[0]);
+  const unsigned m0 = ts.lds + (unsigned)stage * (4 * 16 * D * 2);
+#pragma unroll
+  for (int pc = 0; pc < NP; ++pc) lds_dma_16(src + pc * ts.piece_step, m0 + pc * 1024);
 }
 
 template <int D, int G>
@@ -211,15 +215,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
 
   // Online-softmax state per row (the same in the four lanes sharing a row): m is the running
   // maximum of raw scores, nmc = -m * scale * log2(e) (0 while m is -inf), thr = m + slack.
-  f32x4_t acc[DT][RT];
-  float m[RT], nmc[RT], thr[RT], l[RT];
+  // The running sum of the row's probabilities is accumulated on the matrix cores as one more
+  // product, an all-ones A operand times the bf16 probabilities, so every element of lsum[rt]
+  // holds the sum of the row the lane's column belongs to (the same rounded probabilities that
+  // weight V).
+  f32x4_t acc[DT][RT], lsum[RT];
+  float m[RT], nmc[RT], thr[RT];
   const float slack_raw = kRescaleSlack / c;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m[rt] = kNegInf;
     nmc[rt] = 0.f;
     thr[rt] = kNegInf;
-    l[rt] = 0.f;
+    lsum[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -260,19 +268,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     // One key tile.  kMasked: the tile reaches past the first row's diagonal and the causal mask
     // is applied per score; those tiles are the last ones of the walk, so the two variants run
     // as two loops and the other tiles carry no per-score selects.
+    // cur is tile t's stage, (t - t_first) % kStages, kept as a rotating counter.
+    int cur = 0;
     auto walk_tile = [&](int t, auto masked_c) __attribute__((always_inline)) {
       constexpr bool kMasked = decltype(masked_c)::value;
-      const int cur = (t - t_first) % kStages;
+      const int prev = (cur == 0) ? kStages - 1 : cur - 1;  // tile t-1's stage, free below
       wait_vmcnt<NP * (kStages - 2)>();  // this wave's part of tile t has landed
       __syncthreads();                   // all parts landed; every wave is done with tile t-1
-      issue_tile<D>(ts, ids_lds, blk0, min(t + kStages - 1, t_end - 1), L,
-                    (cur + kStages - 1) % kStages);
+      issue_tile<D>(ts, ids_lds, blk0, min(t + kStages - 1, t_end - 1), L, prev);
       if (t * kKeyTile + kKeyTile > L) {  // block-uniform: zero V rows of keys at or past L
         uint16_t* vz = &lds[cur][2 * 16 * D];
         for (int i = threadIdx.x; i < 2 * 16 * D; i += kPThreads) {
-          const int e = i % (16 * D);  // dim row e / 16, slot (e / 8) % 2, element e % 8
-          const int kk = 8 * (((e >> 3) & 1) ^ swz_v((e >> 4) & 31)) + (e & 7);
-          const int key = t * kKeyTile + 16 * (i / (16 * D)) + kk;
+          // piece i / 512, lane (i % 512) / 8 holding keys 8 * (lane / 16) .., element i % 8
+          const int key = t * kKeyTile + 8 * ((i >> 7) & 3) + (i & 7);
           if (key >= L) vz[i] = 0;
         }
         __syncthreads();
@@ -286,19 +294,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       // second product needs.
       uint4 kf[2][KS];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int key = 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * kt;
-        const int sbk = key >> 4, kk = key & 15;
-        const uint16_t* krow = kl + sbk * 16 * D + kk * 32 + 8 * ((lane >> 4) ^ swz_k(sbk, kk));
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = *(const uint4*)(krow + ks * 512);
-      }
+        for (int ks = 0; ks < KS; ++ks)
+          kf[kt][ks] = *(const uint4*)(kl + ((kt * KS + ks) * 64 + lane) * 8);
       // V fragments, the A operands of the second product: dim 16dt + lane%16, keys 8g .. 8g+7
-      // (g = lane/16), i.e. half g%2 of the dim's row in V sub-block g/2.
-      const int g = lane >> 4;
+      // (g = lane/16).
       auto v_frag = [&](int dt) __attribute__((always_inline)) {
-        const int d = 16 * dt + (lane & 15);
-        return *(const uint4*)(vl + (g >> 1) * 16 * D + d * 16 + 8 * ((g & 1) ^ swz_v(d & 31)));
+        return *(const uint4*)(vl + (dt * 64 + lane) * 8);
       };
       auto scores = [&](int rt, f32x4_t (&sc)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
           const float mn = fmaxf(m[rt], mx);  // raw units
           if (mn != kNegInf && mn != m[rt]) {
             const float alpha = fast_exp2((m[rt] - mn) * c);  // 0 when the old max is -inf
-            l[rt] *= alpha;
+            lsum[rt] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[dt][rt] *= alpha;
             m[rt] = mn;
@@ -345,17 +348,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
             thr[rt] = mn + slack_raw;
           }
         }
-        float pr[8], ps = 0.f;
+        float pr[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pr[i] = fast_exp2(__builtin_fmaf(x[i], c, nmc[rt]));
-          ps += pr[i];
-        }
-        l[rt] += ps;
+        for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, nmc[rt]));
         // B operand of the second product: item j is key 8*(lane/16) + j of the tile (the V
         // fragments use the same order).
         const uint4 pb = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                                     pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
+        constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+        lsum[rt] = mfma(make_uint4(kOnes, kOnes, kOnes, kOnes), pb, lsum[rt]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = mfma(vf(dt), pb, acc[dt][rt]);
       };
@@ -376,6 +377,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
         scores(0, s0);
         softmax_pv(0, s0, v_frag);
       }
+      cur = (cur == kStages - 1) ? 0 : cur + 1;
     };
     // Tile t needs the mask iff 32t + 31 > diag.
     const int t_mask = min(max((diag + 1) / kKeyTile, t_first), t_end);
@@ -385,12 +387,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     wait_vmcnt<0>();  // no tile load may still be writing LDS when the workgroup ends
   }
 
-  // Finish: row sums over the four lane groups, then normalise or hand the split's state over.
+  // Finish: normalise or hand the split's state over.
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    float lt = l[rt];
-    lt += xor16_f32(lt);
-    lt += xor32_f32(lt);
+    const float lt = lsum[rt][0];
     if (!row_ok[rt]) continue;
     const int r = wave * 16 * RT + 16 * rt + (lane & 15);
     const size_t orow = (size_t)(qs + row_tok[rt]) * Hq + (size_t)h * G + r % G;

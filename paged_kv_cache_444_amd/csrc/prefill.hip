@@ -13,17 +13,19 @@
 // (query token, head-in-group) pair: the G query heads that share a KV head share every K/V tile,
 // so they are packed into the rows of one tile (row r = token r / G, head r % G).  Each wave owns
 // RT tiles of 16 rows.  The keys are walked in tiles of 32 (two 16-token sub-blocks); each tile's
-// K and V are copied from the pool into LDS in the pool's own layout (double buffered) and every
-// wave computes
+// K and V are copied into LDS in MFMA operand order (see the tile pipeline below) and every wave
+// computes
 //   Sᵀ[key][row] = K·Qᵀ      A = K from LDS (16 keys x 32 dims per instruction), B = Q rows kept
 //                            in registers for the whole walk;
-//   Oᵀ[dim][row] += Vᵀ·Pᵀ    A = V from LDS, B = the bf16 probabilities.
+//   Oᵀ[dim][row] += Vᵀ·Pᵀ    A = V from LDS, B = the bf16 probabilities;
+//   lsum[row]    += 1·Pᵀ     the running row sum, on the matrix cores as well.
 // With the transposed product the score tile comes out of the matrix core exactly in the lane
-// layout the second product needs as its B operand (lane l holds keys 4*(l/16)+i of row l%16), so
-// probabilities never leave registers.  The softmax is online per row in the log2 domain; masking
-// is applied only on tiles that reach past the first token's diagonal, by selection (NaN-safe),
-// and V rows of keys at or past L are zeroed in LDS so that 0 * NaN cannot enter the accumulator.
-//
+// layout the second product needs as its B operand (lane l holds keys 8*(l/16) .. +7 of row l%16),
+// so probabilities never leave registers.  The softmax is online per row in the log2 domain;
+// masking is applied only on tiles that reach past the first token's diagonal, by selection
+// (NaN-safe), and V rows of keys at or past L are zeroed in LDS so that 0 * NaN cannot enter the
+// accumulator.
+
 // Context split.  Long contexts are cut into `splits` key ranges (multiples of 32 keys) so the
 // launch has enough workgroups; each range's (m, l, acc) per row goes to the workspace and
 // prefill_merge combines them in split order.  With one split the output is written directly.

@@ -35,6 +35,8 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 namespace pa {
@@ -486,6 +488,40 @@ int cu_count() {
   return cus > 0 ? cus : 256;
 }
 
+template <int D>
+const void* kernel_of(int G) {
+  switch (G) {
+    case 1: return reinterpret_cast<const void*>(&prefill_kernel<D, 1>);
+    case 2: return reinterpret_cast<const void*>(&prefill_kernel<D, 2>);
+    case 4: return reinterpret_cast<const void*>(&prefill_kernel<D, 4>);
+    case 8: if constexpr (D <= 128) return reinterpret_cast<const void*>(&prefill_kernel<D, 8>); break;
+    case 16: if constexpr (D <= 64) return reinterpret_cast<const void*>(&prefill_kernel<D, 16>); break;
+    default: break;
+  }
+  return nullptr;
+}
+
+// Workgroups of the (head_dim, group) variant resident on one CU at once (at least 1).
+int resident_per_cu(int head_dim, int group) {
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_pair(dev, head_dim * 64 + group);
+  if (auto it = cache.find(key); it != cache.end()) return it->second;
+  const void* fn = head_dim == 64    ? kernel_of<64>(group)
+                   : head_dim == 128 ? kernel_of<128>(group)
+                   : head_dim == 256 ? kernel_of<256>(group)
+                                     : nullptr;
+  int n = 0;
+  if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kPThreads, 0) != hipSuccess)
+    n = 1;
+  n = std::max(n, 1);
+  cache[key] = n;
+  return n;
+}
+
 }  // namespace
 
 PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int group, int head_dim,
@@ -498,8 +534,10 @@ PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int gr
   const int rows = kPWaves * 16 * (head_dim == 256 ? 1 : 2);
   const int tq = rows / group;
   const long long base = (long long)((max_q_len + tq - 1) / tq) * num_kv_heads * num_seqs;
-  // Enough workgroups for four per CU, each range at least 256 keys, at most 16 ranges.
-  long long want = (4LL * cu_count() + base - 1) / base;
+  // Enough workgroups for one round of every CU's resident slots (more rounds only add merge
+  // work), each range at least 256 keys, at most 16 ranges.
+  const long long slots = (long long)resident_per_cu(head_dim, group) * cu_count();
+  long long want = (slots + base - 1) / base;
   if (const char* e = std::getenv("PA_PREFILL_SPLITS"); e && *e) want = std::atoi(e);
   want = std::min<long long>(std::max<long long>(want, 1), 16);
   want = std::min<long long>(want, std::max(1, max_seq_len / 256));

@@ -122,6 +122,13 @@ __device__ __forceinline__ float uniform_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
+// Partial slot of the piece of unit u (s * num_kv_heads + h) held by worker w.  Later workers
+// hold later units, so w + u is unique among pieces; with head quads the worker is a workgroup
+// and the order is over quad units u / kWaves, so the slot is (w + u / kWaves) * kWaves + u % kWaves.
+__device__ __forceinline__ size_t slot_of(const DecodeParams& p, long long w, int u) {
+  return p.quad ? (size_t)(w + u / kWaves) * kWaves + u % kWaves : (size_t)(w + u);
+}
+
 // Head owned by this lane in slot j, or -1.
 template <int G>
 __device__ __forceinline__ int own_head(int c, int j) {
@@ -403,7 +410,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
     y += __shfl_xor(y, 32, 64);
     lsum[j] = y;
   }
-  float* slot = coop ? coop : p.partials + (size_t)(w + u) * (G * (2 + D));
+  float* slot = coop ? coop : p.partials + slot_of(p, w, u) * (G * (2 + D));
   uint16_t* orow = p.out + ((size_t)s * Hq + (size_t)h * G) * D;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -444,7 +451,7 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
   const bool whole = (j0 == 0) && (take == n_s);
   if (j0 == 0 && threadIdx.x == 0)
     p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1));
-  float* slot = p.partials + (size_t)(w + u) * (G * (2 + D));
+  float* slot = p.partials + slot_of(p, w, u) * (G * (2 + D));
   uint16_t* orow = p.out + ((size_t)s * p.num_q_heads + (size_t)h * G) * D;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
@@ -478,12 +485,15 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
 }
 
 // Steps of virtual worker v, unit by unit.  (s, off) locate its first step: sequence s and offset
-// within that sequence's num_kv_heads * n_s steps.  Coop: each piece is shared by the workgroup.
+// within that sequence's U * n_s steps, U = num_kv_heads units per sequence, or with `quad`
+// num_kv_heads / kWaves units of kWaves consecutive KV heads, wave r taking head kWaves*unit + r
+// (the workgroup is the worker).  Coop: each piece is shared by the workgroup.
 template <int D, int G, int Depth, bool Coop = false>
 __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& plan, long long v,
                                            int s, long long off, uint16_t (*p_sh)[G][8],
-                                           float (*st)[G * (2 + D)] = nullptr) {
-  const int B = p.num_seqs, Hkv = p.num_kv_heads;
+                                           float (*st)[G * (2 + D)] = nullptr, bool quad = false) {
+  const int B = p.num_seqs;
+  const int Hkv = quad ? p.num_kv_heads / kWaves : p.num_kv_heads;
   long long x = plan.start(v);
   const long long x1 = plan.start(v + 1);
   if (x >= x1 || s < 0 || s >= B) return;
@@ -494,7 +504,8 @@ __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& pl
   while (true) {
     const int take = (int)min((long long)(n_s - j), x1 - x);
     if constexpr (Coop) coop_piece<D, G, Depth>(p, s, h, j, take, n_s, v, x, plan, p_sh, st);
-    else decode_piece<D, G, Depth>(p, s, h, j, take, n_s, v, x, plan, p_sh);
+    else decode_piece<D, G, Depth>(p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h, j, take,
+                                   n_s, v, x, plan, p_sh);
     x += take;
     if (x >= x1) break;
     j = 0;
@@ -538,11 +549,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   long long per_head = 0;
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) per_head += sh_sum[k];
+  // quad: the workgroup is one worker over units of kWaves consecutive KV heads.
+  const bool quad = p.quad != 0;
+  const int U = quad ? Hkv / kWaves : Hkv;  // units per sequence
   Plan plan;
-  plan.T = per_head * Hkv;
+  plan.T = per_head * U;
   if (plan.T == 0) return;  // block-uniform
-  plan.ns = min((long long)p.num_workers, (plan.T + kMinStepsPerWave - 1) / kMinStepsPerWave);
-  const bool dynamic = p.dyn_cap > 0 && plan.ns == p.num_workers;
+  const long long workers = quad ? (long long)gridDim.x : (long long)p.num_workers;
+  plan.ns = min(workers, (plan.T + kMinStepsPerWave - 1) / kMinStepsPerWave);
+  const bool dynamic = !quad && p.dyn_cap > 0 && plan.ns == p.num_workers;
   if (dynamic) {
     plan.S = max(plan.ns, plan.T * p.static_frac_q10 / 1024);
     const long long rest = plan.T - plan.S;
@@ -572,11 +587,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     const long long excl = base + before + incl - n;
     if (dynamic && s < B) seq_prefix[s] = (int)excl;
-    const long long lo = excl * Hkv;
-    const long long hi = (excl + n) * Hkv;
+    const long long lo = excl * U;
+    const long long hi = (excl + n) * U;
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) {
-      const long long wk = wbase + k;
+      const long long wk = quad ? (long long)blockIdx.x : wbase + k;
       const long long x0 = plan.start(wk);
       if (wk < plan.ns && x0 >= lo && x0 < hi) {
         sh_start_s[k] = s;
@@ -589,9 +604,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   if (dynamic && threadIdx.x == 0) seq_prefix[B] = (int)base;
   __syncthreads();
 
-  const long long w = wbase + wave;
+  const long long w = quad ? (long long)blockIdx.x : wbase + wave;
   if (w < plan.ns)
-    run_worker<D, G, Depth>(p, plan, w, sh_start_s[wave], sh_start_off[wave], p_lds[wave]);
+    run_worker<D, G, Depth>(p, plan, w, sh_start_s[wave], sh_start_off[wave], p_lds[wave],
+                            nullptr, quad);
   if (!dynamic) return;  // block-uniform
 
   // Dynamic chunks, each shared by the whole workgroup (one counter increment per chunk; the
@@ -654,7 +670,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
     for (int r = 0; r < kRound; ++r) {
       const int w = min(w0 + r, info.y);
-      const float* slot = p.partials + (size_t)(w + u) * (G * (2 + D));
+      const float* slot = p.partials + slot_of(p, w, u) * (G * (2 + D));
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         const int i = min(threadIdx.x + 256 * k, G * D - 1);

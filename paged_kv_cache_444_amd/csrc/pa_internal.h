@@ -28,6 +28,10 @@ struct DecodeParams {
   int dyn_cap;         // most dynamic chunks the workspace holds (0: static split only)
   int chunk_steps;     // smallest dynamic chunk, in steps
   int static_frac_q10; // share of the steps split statically, in 1/1024
+  // Nonzero: workgroup-level workers over units of four consecutive KV heads (wave r takes head
+  // 4*unit + r), so the four waves of a CU read neighbouring 4 KB tiles of the same block
+  // together.  Static split only; num_kv_heads a multiple of four.
+  int quad;
   // Lengths are clamped to this (min of max_seq_len and the table width) so a length beyond the
   // caller's bound cannot take a kernel outside the table.
   int len_cap;

@@ -200,6 +200,38 @@ def test_decode_shared_chunks_shapes(Hq, Hkv, D, bs, chunk, monkeypatch):
                  f"shared chunks of {chunk} steps")
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,bs,workers", [(32, 8, 128, 16, None), (16, 4, 256, 32, "8"),
+                                                 (32, 8, 64, 16, "12"), (8, 2, 128, 16, None),
+                                                 (16, 4, 128, 32, "4")])
+def test_decode_head_quads(Hq, Hkv, D, bs, workers, monkeypatch):
+    """Workgroup workers over units of four KV heads (a wave per head, the four reading the same
+    block together) change only how steps are handed out: every shape must match the oracle,
+    deterministically, with the merge kernel combining units split between workgroups."""
+    case = build_case(Spec(name="quads", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           block_size=bs, seed=(28, Hq, D, bs),
+                           decode_lens=[1, 17, 300, 1000, 2049, 5, 640, 0, 3000]))
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    monkeypatch.setenv("PA_DECODE_QUAD", "1")
+    if workers:
+        monkeypatch.setenv("PA_DECODE_WORKERS", workers)
+    a = gpu_decode(case, kc, vc)
+    assert np.array_equal(a, gpu_decode(case, kc, vc))
+    assert_close(upcast(a), oracle_decode(case, case.key_cache, case.value_cache),
+                 "decode over head quads")
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_decode_head_quads_named(cfg, monkeypatch):
+    case = cached_named_case(cfg)
+    d = case.decode
+    monkeypatch.setenv("PA_DECODE_QUAD", "1")
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    got = upcast(gpu_decode(case, kc, vc))
+    seqs = list(range(0, d.num_seqs, 11))
+    ref = oracle_decode(case, case.key_cache, case.value_cache, seqs=seqs)
+    assert_close(got[seqs], ref[seqs], f"decode over head quads, workload {cfg}")
+
+
 def test_decode_workspace_sizes_on_device():
     n = pa.decode_workspace_bytes(128, 64, 8, 128, 8192)
     assert n >= 128 * 8 * 8 * (128 + 2) * 4  # at least one partial slot per unit

@@ -7,9 +7,12 @@ through `--layers` distinct copies of the KV pools, as consecutive decode calls 
 different layers' caches, so a step cannot be served from the 256 MB last-level cache that the
 previous step filled.  Prints one JSON line.
 
-  value        algorithmic bytes of one call / wall time per step (GB/s)
+  value        algorithmic bytes of one call / wall time per step (GB/s), K steps with nothing
+               but the calls on the stream
   roofline     the dominant kernel (decode_kernel): algorithmic bytes per launch / its mean
-               event-timed duration over the timed steps, against the 8 TB/s HBM peak
+               duration over the same K steps run again with HIP events recorded around every
+               kernel launch (the events' marker packets add a few us per step, so this second
+               pass is not the one `value` is taken from), against the 8 TB/s HBM peak
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same batch (a correctness tool,
                not an optimised CPU kernel)
 
@@ -90,7 +93,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--layers", type=int, default=4,
                     help="distinct KV pool copies cycled through by consecutive steps")
     ap.add_argument("--warm-steps", type=int, default=50,
@@ -100,6 +103,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["decode", "copy", "mixed"], default="decode")
     ap.add_argument("--mixed-steps", type=int, default=30)
+    ap.add_argument("--mixed-warmup", type=int, default=60)
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-step measurement")
     ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
@@ -178,18 +182,26 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    pa.trace_enable(True)
-    for name in ("decode_partition", "decode_merge"):
-        pa.trace_read(name)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    log(f"timed {args.steps} steps")
+
+    pa.trace_enable(True)
+    for name in ("decode_partition", "decode_merge"):
+        pa.trace_read(name)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
     n_main, ms_main = pa.trace_read("decode_partition")
     n_merge, ms_merge = pa.trace_read("decode_merge")
-    log(f"timed {args.steps} steps")
+    pa.trace_enable(False)
+    log(f"timed {args.steps} steps with per-launch events")
 
     warm_us = None
     if args.warm_steps > 0:
@@ -201,9 +213,6 @@ def main():
             step(0)
         torch.cuda.synchronize()
         warm_us = (time.perf_counter() - w0) * 1e6 / args.warm_steps
-        pa.trace_read("decode_partition")
-        pa.trace_read("decode_merge")
-    pa.trace_enable(False)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     nbytes = decode_bytes(d.seq_lens, Hq, Hkv, D, bs)
@@ -253,6 +262,7 @@ def main():
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(main_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("decode_kernel"), "launch_us": round(main_ms * 1e3, 2),
             "merge_launch_us": round(ms_merge / max(n_merge, 1) * 1e3, 2),
+            "ms_per_step_with_events": round((t3 - t2) * 1e3 / args.steps, 5),
         },
         "warm_single_pool_us_per_step": None if warm_us is None else round(warm_us, 2),
         "mixed_step": mixed,
@@ -298,17 +308,22 @@ def run_mixed(args):
                   max_seq_len=dc.max_seq_len, out=dout, workspace=dws)
 
     names = ("reshape_and_cache", "prefill_chunk", "prefill_merge", "decode_partition", "decode_merge")
-    for _ in range(5):
+    # The matrix cores' clock ramps up over the first few tens of milliseconds of this load.
+    for _ in range(args.mixed_warmup):
         step()
     torch.cuda.synchronize()
-    pa.trace_enable(True)
-    for n in names:
-        pa.trace_read(n)
     t0 = time.perf_counter()
     for _ in range(args.mixed_steps):
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.mixed_steps
+    # Per-kernel durations from a second pass with events around every launch.
+    pa.trace_enable(True)
+    for n in names:
+        pa.trace_read(n)
+    for _ in range(args.mixed_steps):
+        step()
+    torch.cuda.synchronize()
     per = {}
     for n in names:
         k, ms = pa.trace_read(n)
@@ -322,6 +337,7 @@ def run_mixed(args):
     log(f"mixed step {ms_step * 1e3:.1f} us")
     return {
         "workload": case.name, "us_per_step": round(ms_step * 1e3, 2), "steps": args.mixed_steps,
+        "warmup": args.mixed_warmup,
         "kernel_us": per,
         "prefill_roofline": {"bound": "mfma", "kernel": "prefill_chunk",
                              "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -95,8 +95,10 @@ hipEvent_t take_event() {
     g_event_pool.pop_back();
     return e;
   }
+  // Trace events only time kernels, so they skip the system-scope release (an L2 write-back)
+  // that a default event performs when it is recorded between two launches.
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

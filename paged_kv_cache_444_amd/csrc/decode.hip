@@ -23,9 +23,11 @@
 //
 // Lane roles within a step (one 16-token sub-block of one physical block, one KV head; the pool
 // layout puts K as [D/32][16][32] and V as [D][16] inside the sub-block):
-//   K side: lane l holds tokens l/8 and 8 + l/8 and the head-dim slice [c*D/8, (c+1)*D/8),
-//           c = l % 8; the same slice of the G query rows stays in registers for the whole piece
-//           (G*D/16 registers, at most 64), and three DPP adds finish each score.
+//   K side: lane l holds tokens l/8 and 8 + l/8 and the head-dim values 8c + 64x + [0, 8),
+//           c = l % 8, x < D/64, so that each load instruction of the wave reads whole 64-byte
+//           token rows of two 32-wide slices; the same values of the G query rows stay in
+//           registers for the whole piece (G*D/16 registers, at most 64), and three DPP adds
+//           finish each score.
 //   softmax: online in the log2 domain with one running max per head for the whole wave; lane
 //           l computes the probabilities of its own head(s) c + 8j.  The max is only raised (and
 //           acc rescaled) when a score exceeds it by more than kRescaleSlack, which after the
@@ -39,6 +41,7 @@
 #include "pa_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <cstdlib>
 #include <map>
 #include <mutex>
@@ -94,8 +97,10 @@ struct Plan {
 };
 
 // K-side lane roles: lane l holds token 8p + l/8 of the step's two octets (p = 0, 1) and the
-// D/8 head-dim values [c*D/8, (c+1)*D/8) with c = l % 8; the 8 lanes of a token finish its scores
-// with three DPP adds.  V-side: lane l holds head-dim rows l%32 + 32x of octet l/32.
+// D/8 head-dim values 8c + 64x + [0, 8) with c = l % 8; the 8 lanes of a token finish its scores
+// with three DPP adds.  Load (p, x) of the wave covers rows 8p .. 8p+7 of slices 2x and 2x+1:
+// two 512-byte runs of whole cache lines.  V-side: lane l holds head-dim rows l%32 + 32x of
+// octet l/32, so load x is 1 KB contiguous.
 template <int D>
 struct StepRegs {
   uint4 k[2][D / 64];
@@ -138,12 +143,24 @@ __device__ __forceinline__ int own_head(int c, int j) {
 
 // Issue the loads of step i of the current unit.  `win`/`ids` hold up to 64 physical block ids
 // of the unit, one per lane, starting at logical block `win`.
-template <int D>
+// 16-byte global load.  Stream = read-once data: the non-temporal hint keeps it from displacing
+// lines in L2 and the last-level cache, which the 70B-shaped batch measured 9 % faster.
+template <bool Stream>
+__device__ __forceinline__ uint4 load16(const uint16_t* ptr) {
+  if constexpr (Stream) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)ptr);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *(const uint4*)ptr;
+  }
+}
+
+template <int D, bool Stream>
 __device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodeParams& p,
                                           const int* bt, int& win, int& ids,
                                           size_t head_off, size_t block_elems) {
   constexpr int R = D / kSlice;
-  constexpr int DL = D / 8;  // head-dim values per K-side lane
   const int lane = threadIdx.x & 63;
   const int bs = p.block_size;
   const int t0 = i * kSub;
@@ -162,13 +179,13 @@ __device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodePar
   for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
     for (int x = 0; x < D / 64; ++x) {
-      const int d = c * DL + 8 * x;
-      r.k[pp][x] = *(const uint4*)(kp + (d >> 5) * (kSub * kSlice) + (8 * pp + tt) * kSlice +
-                                   (d & 31));
+      const int d = 8 * c + 64 * x;
+      r.k[pp][x] = load16<Stream>(kp + (d >> 5) * (kSub * kSlice) + (8 * pp + tt) * kSlice +
+                                  (d & 31));
     }
   const int vd = lane & 31, vo = lane >> 5;
 #pragma unroll
-  for (int x = 0; x < R; ++x) r.v[x] = *(const uint4*)(vp + (vd + 32 * x) * kSub + 8 * vo);
+  for (int x = 0; x < R; ++x) r.v[x] = load16<Stream>(vp + (vd + 32 * x) * kSub + 8 * vo);
 }
 
 // One 16-token step: scores, online softmax, P·V.  nvalid = tokens of the step inside the piece
@@ -299,7 +316,7 @@ __device__ __forceinline__ void compute_step(const StepRegs<D>& r, const uint4 (
 // Depth is the number of steps whose loads are in flight while one step is computed.  With
 // `coop` set the wave's (m, l, acc) always goes to `coop` (its slot in LDS) and the workgroup
 // combines the slots; otherwise the piece is finished here.
-template <int D, int G, int Depth>
+template <int D, int G, int Depth, bool Stream>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h, int j0, int take,
                                              int n_s, long long w, long long x, const Plan& plan,
                                              uint16_t (*p_sh)[G][8], float* coop = nullptr) {
@@ -317,11 +334,11 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   // This lane's head-dim slice of the G query rows sharing KV head h.
   uint4 q[G][D / 64];
   {
-    const uint16_t* qg = p.query + ((size_t)s * Hq + (size_t)h * G) * D + lc * (D / 8);
+    const uint16_t* qg = p.query + ((size_t)s * Hq + (size_t)h * G) * D + 8 * lc;
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int y = 0; y < D / 64; ++y) q[g][y] = *(const uint4*)(qg + g * D + 8 * y);
+      for (int y = 0; y < D / 64; ++y) q[g][y] = *(const uint4*)(qg + g * D + 64 * y);
   }
 
   const int bs = p.block_size;
@@ -358,41 +375,41 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   }
 
   // Prefetch loads are issued unconditionally (past the last step they repeat the last step's
-  // addresses, which hit in cache): a load issued on only some paths would make the compiler wait
-  // for every outstanding load before each step.
+  // addresses, which hit in cache): a load issued on only some paths would make the compiler
+  // wait for every outstanding load before each step.
   const int iend = j0 + take;
   const int ilast = iend - 1;
   int i = j0;
   if constexpr (Depth == 0) {  // no prefetch: fewer registers, more resident waves
     while (true) {
       StepRegs<D> ra;
-      load_step<D>(ra, i, p, bt, win, ids, head_off, block_elems);
+      load_step<D, Stream>(ra, i, p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else if constexpr (Depth == 1) {
     StepRegs<D> ra, rb;
-    load_step<D>(ra, i, p, bt, win, ids, head_off, block_elems);
+    load_step<D, Stream>(ra, i, p, bt, win, ids, head_off, block_elems);
     while (true) {
-      load_step<D>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      load_step<D, Stream>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      load_step<D, Stream>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(rb, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else {  // two steps in flight while one is computed
     StepRegs<D> r0, r1, r2;
-    load_step<D>(r0, i, p, bt, win, ids, head_off, block_elems);
-    load_step<D>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+    load_step<D, Stream>(r0, i, p, bt, win, ids, head_off, block_elems);
+    load_step<D, Stream>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
     while (true) {
-      load_step<D>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      load_step<D, Stream>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(r0, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      load_step<D, Stream>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(r1, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      load_step<D, Stream>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
       compute_step<D, G>(r2, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
@@ -437,7 +454,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
 // j0 + take*(r+1)/kWaves) into its LDS slot, then the workgroup combines the slots in wave order
 // and writes the output (unit wholly inside the piece) or the piece's partial slot.  Contains
 // barriers: every wave of the block must call it with the same arguments.
-template <int D, int G, int Depth>
+template <int D, int G, int Depth, bool Stream>
 __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, int j0, int take,
                                            int n_s, long long w, long long x, const Plan& plan,
                                            uint16_t (*p_sh)[G][8], float (*st)[G * (2 + D)]) {
@@ -445,7 +462,8 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
   const int wave = threadIdx.x >> 6;
   auto lo_of = [&](int r) { return j0 + (int)((long long)take * r / kWaves); };
   const int a = lo_of(wave), b = lo_of(wave + 1);
-  if (b > a) decode_piece<D, G, Depth>(p, s, h, a, b - a, n_s, w, x + (a - j0), plan, p_sh, st[wave]);
+  if (b > a)
+    decode_piece<D, G, Depth, Stream>(p, s, h, a, b - a, n_s, w, x + (a - j0), plan, p_sh, st[wave]);
   __syncthreads();
   const int u = s * p.num_kv_heads + h;
   const bool whole = (j0 == 0) && (take == n_s);
@@ -488,7 +506,7 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
 // within that sequence's U * n_s steps, U = num_kv_heads units per sequence, or with `quad`
 // num_kv_heads / kWaves units of kWaves consecutive KV heads, wave r taking head kWaves*unit + r
 // (the workgroup is the worker).  Coop: each piece is shared by the workgroup.
-template <int D, int G, int Depth, bool Coop = false>
+template <int D, int G, int Depth, bool Stream, bool Coop = false>
 __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& plan, long long v,
                                            int s, long long off, uint16_t (*p_sh)[G][8],
                                            float (*st)[G * (2 + D)] = nullptr, bool quad = false) {
@@ -503,9 +521,9 @@ __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& pl
   int j = (int)(off % n_s);
   while (true) {
     const int take = (int)min((long long)(n_s - j), x1 - x);
-    if constexpr (Coop) coop_piece<D, G, Depth>(p, s, h, j, take, n_s, v, x, plan, p_sh, st);
-    else decode_piece<D, G, Depth>(p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h, j, take,
-                                   n_s, v, x, plan, p_sh);
+    if constexpr (Coop) coop_piece<D, G, Depth, Stream>(p, s, h, j, take, n_s, v, x, plan, p_sh, st);
+    else decode_piece<D, G, Depth, Stream>(p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h, j,
+                                           take, n_s, v, x, plan, p_sh);
     x += take;
     if (x >= x1) break;
     j = 0;
@@ -528,6 +546,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int Hkv = p.num_kv_heads;
 
   __shared__ long long sh_sum[kWaves];
+  __shared__ int sh_shares[kWaves];
   __shared__ int sh_scan[kWaves];
   __shared__ int sh_start_s[kWaves];
   __shared__ long long sh_start_off[kWaves];
@@ -541,14 +560,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int n_first = (int)threadIdx.x < B ? steps_of(p, threadIdx.x) : 0;
   long long mine = n_first;
   for (int s = threadIdx.x + kThreads; s < B; s += kThreads) mine += steps_of(p, s);
+  // Prefix sharing (several sequences reading the same physical blocks, as when many samples
+  // continue one prompt) shows as a sequence starting at the same block as the next one.  Such a
+  // batch re-reads blocks, so its K/V loads stay ordinary; any other batch streams them.
+  int shares = 0;
+  const size_t row = (size_t)p.max_blocks_per_seq;
+  for (int s = threadIdx.x; s + 1 < B; s += kThreads)
+    shares |= p.block_tables[(size_t)s * row] == p.block_tables[(size_t)(s + 1) * row];
+  shares = __any(shares);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
-  if (lane == 0) sh_sum[wave] = mine;
+  if (lane == 0) {
+    sh_sum[wave] = mine;
+    sh_shares[wave] = shares;
+  }
   if (threadIdx.x < kWaves) sh_start_s[threadIdx.x] = -1;
   __syncthreads();
   long long per_head = 0;
+  bool shared = false;
 #pragma unroll
-  for (int k = 0; k < kWaves; ++k) per_head += sh_sum[k];
+  for (int k = 0; k < kWaves; ++k) {
+    per_head += sh_sum[k];
+    shared |= sh_shares[k] != 0;
+  }
   // quad: the workgroup is one worker over units of kWaves consecutive KV heads.
   const bool quad = p.quad != 0;
   const int U = quad ? Hkv / kWaves : Hkv;  // units per sequence
@@ -605,36 +639,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __syncthreads();
 
   const long long w = quad ? (long long)blockIdx.x : wbase + wave;
-  if (w < plan.ns)
-    run_worker<D, G, Depth>(p, plan, w, sh_start_s[wave], sh_start_off[wave], p_lds[wave],
-                            nullptr, quad);
-  if (!dynamic) return;  // block-uniform
+  // One instantiation of the worker per load kind (the choice is uniform over the grid).
+  auto body = [&](auto stream) {
+    constexpr bool S = decltype(stream)::value;
+    if (w < plan.ns)
+      run_worker<D, G, Depth, S>(p, plan, w, sh_start_s[wave], sh_start_off[wave], p_lds[wave],
+                                 nullptr, quad);
+    if (!dynamic) return;  // block-uniform
 
-  // Dynamic chunks, each shared by the whole workgroup (one counter increment per chunk; the
-  // next chunk is claimed while the current one runs).  In dynamic mode every wave has a static
-  // range (plan.ns == num_workers), so all waves reach these barriers.
-  if (threadIdx.x == 0) sh_chunk = atomicAdd(p.counter, 1u);
-  __syncthreads();
-  while (true) {
-    const unsigned d = sh_chunk;  // block-uniform
-    if ((long long)d >= plan.nd) break;
-    unsigned nxt = 0;
-    if (threadIdx.x == 0) nxt = atomicAdd(p.counter, 1u);
-    // Locate the chunk's first step: the last sequence whose prefix is <= x / Hkv.
-    const long long x0 = plan.start(plan.ns + d);
-    const long long xh = x0 / Hkv;
-    int lo = 0, hi = B;  // invariant: seq_prefix[lo] <= xh < seq_prefix[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (seq_prefix[mid] <= xh) lo = mid;
-      else hi = mid;
-    }
-    run_worker<D, G, Depth, true>(p, plan, plan.ns + d, lo,
-                                  x0 - (long long)seq_prefix[lo] * Hkv, p_lds[wave], coop_st);
-    __syncthreads();  // every thread has read sh_chunk
-    if (threadIdx.x == 0) sh_chunk = nxt;
+    // Dynamic chunks, each shared by the whole workgroup (one counter increment per chunk; the
+    // next chunk is claimed while the current one runs).  In dynamic mode every wave has a static
+    // range (plan.ns == num_workers), so all waves reach these barriers.
+    if (threadIdx.x == 0) sh_chunk = atomicAdd(p.counter, 1u);
     __syncthreads();
-  }
+    while (true) {
+      const unsigned d = sh_chunk;  // block-uniform
+      if ((long long)d >= plan.nd) break;
+      unsigned nxt = 0;
+      if (threadIdx.x == 0) nxt = atomicAdd(p.counter, 1u);
+      // Locate the chunk's first step: the last sequence whose prefix is <= x / Hkv.
+      const long long x0 = plan.start(plan.ns + d);
+      const long long xh = x0 / Hkv;
+      int lo = 0, hi = B;  // invariant: seq_prefix[lo] <= xh < seq_prefix[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (seq_prefix[mid] <= xh) lo = mid;
+        else hi = mid;
+      }
+      run_worker<D, G, Depth, S, true>(p, plan, plan.ns + d, lo,
+                                       x0 - (long long)seq_prefix[lo] * Hkv, p_lds[wave], coop_st);
+      __syncthreads();  // every thread has read sh_chunk
+      if (threadIdx.x == 0) sh_chunk = nxt;
+      __syncthreads();
+    }
+  };
+  if (shared) body(std::false_type{});
+  else body(std::true_type{});
 }
 
 // Combine the pieces of every unit that spans several waves; write zeros for empty sequences.

@@ -261,6 +261,8 @@ def test_decode_block_permutation_bitwise():
 
 
 def test_decode_prefix_sharing_bitwise():
+    # The shared tables make the kernel use ordinary loads and the private copies streaming
+    # (non-temporal) loads, so this also checks that the load kind never changes the result.
     groups = [([0, 1, 2], 512), ([3, 4], 256)]
     case = _small(31, decode_lens=[600, 513, 1100, 300, 257], share_groups=groups)
     kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)

@@ -86,13 +86,21 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 // of C steps covering [S, T), taken by whichever wave is free (an atomic counter hands them out).
 // Which wave runs a worker never changes what the worker computes, and every piece of work has a
 // fixed partial slot (worker + unit), so results do not depend on the dynamic order.
+//
+// The static split balances cost, not steps: every piece a worker starts costs A steps' worth of
+// time (the block-id window and the first K/V tile are dependent loads that nothing overlaps), so
+// step x of the batch's j-th non-empty unit costs position x + A*(j+1) on a line of length
+// CT = S + A * (non-empty units).  Worker v starts at the first step whose cost position reaches
+// v*CT/ns; A = 0 gives the even split of steps.  Dynamic chunks keep A = 0.
 struct Plan {
-  long long T, S, ns, C, nd;
-  __device__ long long start(long long v) const {
+  long long T, S, ns, C, nd, A, CT;
+  __device__ long long start(long long v) const {  // A = 0 only
     return v <= ns ? v * S / ns : min(T, S + (v - ns) * C);
   }
-  __device__ long long owner(long long x) const {
-    return x < S ? ((x + 1) * ns - 1) / S : ns + (x - S) / C;
+  __device__ long long target(long long v) const { return v * CT / ns; }
+  // Worker holding step x, which lies in non-empty unit j.
+  __device__ long long owner(long long x, long long j) const {
+    return x < S ? ((x + A * (j + 1) + 1) * ns - 1) / CT : ns + (x - S) / C;
   }
 };
 
@@ -318,8 +326,9 @@ __device__ __forceinline__ void compute_step(const StepRegs<D>& r, const uint4 (
 // combines the slots; otherwise the piece is finished here.
 template <int D, int G, int Depth, bool Stream>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h, int j0, int take,
-                                             int n_s, long long w, long long x, const Plan& plan,
-                                             uint16_t (*p_sh)[G][8], float* coop = nullptr) {
+                                             int n_s, long long w, long long x, long long jn,
+                                             const Plan& plan, uint16_t (*p_sh)[G][8],
+                                             float* coop = nullptr) {
   constexpr int R = D / kSlice;
   constexpr int O = kOwn<G>;
   const int lane = threadIdx.x & 63;
@@ -329,7 +338,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   const int u = s * p.num_kv_heads + h;
   const bool whole = !coop && (j0 == 0) && (take == n_s);
   if (!coop && j0 == 0 && lane == 0)
-    p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1));
+    p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1, jn));
 
   // This lane's head-dim slice of the G query rows sharing KV head h.
   uint4 q[G][D / 64];
@@ -456,19 +465,21 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
 // barriers: every wave of the block must call it with the same arguments.
 template <int D, int G, int Depth, bool Stream>
 __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, int j0, int take,
-                                           int n_s, long long w, long long x, const Plan& plan,
-                                           uint16_t (*p_sh)[G][8], float (*st)[G * (2 + D)]) {
+                                           int n_s, long long w, long long x, long long jn,
+                                           const Plan& plan, uint16_t (*p_sh)[G][8],
+                                           float (*st)[G * (2 + D)]) {
   constexpr int PER = (G * D + kThreads - 1) / kThreads;
   const int wave = threadIdx.x >> 6;
   auto lo_of = [&](int r) { return j0 + (int)((long long)take * r / kWaves); };
   const int a = lo_of(wave), b = lo_of(wave + 1);
   if (b > a)
-    decode_piece<D, G, Depth, Stream>(p, s, h, a, b - a, n_s, w, x + (a - j0), plan, p_sh, st[wave]);
+    decode_piece<D, G, Depth, Stream>(p, s, h, a, b - a, n_s, w, x + (a - j0), jn, plan, p_sh,
+                                      st[wave]);
   __syncthreads();
   const int u = s * p.num_kv_heads + h;
   const bool whole = (j0 == 0) && (take == n_s);
   if (j0 == 0 && threadIdx.x == 0)
-    p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1));
+    p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1, jn));
   float* slot = p.partials + slot_of(p, w, u) * (G * (2 + D));
   uint16_t* orow = p.out + ((size_t)s * p.num_q_heads + (size_t)h * G) * D;
 #pragma unroll
@@ -502,18 +513,18 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
   __syncthreads();  // the slots are rewritten by the next piece
 }
 
-// Steps of virtual worker v, unit by unit.  (s, off) locate its first step: sequence s and offset
-// within that sequence's U * n_s steps, U = num_kv_heads units per sequence, or with `quad`
-// num_kv_heads / kWaves units of kWaves consecutive KV heads, wave r taking head kWaves*unit + r
-// (the workgroup is the worker).  Coop: each piece is shared by the workgroup.
+// Steps [x, x1) of virtual worker v, unit by unit.  (s, off) locate its first step: sequence s
+// and offset within that sequence's U * n_s steps, U = num_kv_heads units per sequence, or with
+// `quad` num_kv_heads / kWaves units of kWaves consecutive KV heads, wave r taking head
+// kWaves*unit + r (the workgroup is the worker); jn is that unit's index among the non-empty
+// units.  Coop: each piece is shared by the workgroup.
 template <int D, int G, int Depth, bool Stream, bool Coop = false>
 __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& plan, long long v,
-                                           int s, long long off, uint16_t (*p_sh)[G][8],
+                                           int s, long long off, long long jn, long long x,
+                                           long long x1, uint16_t (*p_sh)[G][8],
                                            float (*st)[G * (2 + D)] = nullptr, bool quad = false) {
   const int B = p.num_seqs;
   const int Hkv = quad ? p.num_kv_heads / kWaves : p.num_kv_heads;
-  long long x = plan.start(v);
-  const long long x1 = plan.start(v + 1);
   if (x >= x1 || s < 0 || s >= B) return;
   int n_s = steps_of(p, s);
   if (n_s == 0) return;  // unreachable: every step lies in a sequence with steps
@@ -521,12 +532,15 @@ __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& pl
   int j = (int)(off % n_s);
   while (true) {
     const int take = (int)min((long long)(n_s - j), x1 - x);
-    if constexpr (Coop) coop_piece<D, G, Depth, Stream>(p, s, h, j, take, n_s, v, x, plan, p_sh, st);
-    else decode_piece<D, G, Depth, Stream>(p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h, j,
-                                           take, n_s, v, x, plan, p_sh);
+    if constexpr (Coop)
+      coop_piece<D, G, Depth, Stream>(p, s, h, j, take, n_s, v, x, jn, plan, p_sh, st);
+    else
+      decode_piece<D, G, Depth, Stream>(p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h, j,
+                                        take, n_s, v, x, jn, plan, p_sh);
     x += take;
     if (x >= x1) break;
     j = 0;
+    ++jn;
     if (++h == Hkv) {
       h = 0;
       do {
@@ -546,10 +560,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int Hkv = p.num_kv_heads;
 
   __shared__ long long sh_sum[kWaves];
+  __shared__ int sh_nonempty[kWaves];
   __shared__ int sh_shares[kWaves];
   __shared__ int sh_scan[kWaves];
-  __shared__ int sh_start_s[kWaves];
-  __shared__ long long sh_start_off[kWaves];
+  __shared__ int sh_scan_ne[kWaves];
+  // Start of each of this block's workers and of the next block's first one: sequence, offset
+  // within the sequence's steps, non-empty unit index, global step.
+  __shared__ int sh_start_s[kWaves + 1];
+  __shared__ long long sh_start_off[kWaves + 1];
+  __shared__ long long sh_start_j[kWaves + 1];
+  __shared__ long long sh_start_x[kWaves + 1];
   __shared__ __attribute__((aligned(16))) uint16_t p_lds[kWaves][2][G][8];
   __shared__ unsigned sh_chunk;
   __shared__ float coop_st[kWaves][G * (2 + D)];  // per-wave (m, l, acc) of a shared piece
@@ -559,7 +579,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // the prefix sums below, so small batches read their lengths once.
   const int n_first = (int)threadIdx.x < B ? steps_of(p, threadIdx.x) : 0;
   long long mine = n_first;
-  for (int s = threadIdx.x + kThreads; s < B; s += kThreads) mine += steps_of(p, s);
+  int nonempty = n_first > 0;
+  for (int s = threadIdx.x + kThreads; s < B; s += kThreads) {
+    const int n = steps_of(p, s);
+    mine += n;
+    nonempty += n > 0;
+  }
   // Prefix sharing (several sequences reading the same physical blocks, as when many samples
   // continue one prompt) shows as a sequence starting at the same block as the next one.  Such a
   // batch re-reads blocks, so its K/V loads stay ordinary; any other batch streams them.
@@ -569,18 +594,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     shares |= p.block_tables[(size_t)s * row] == p.block_tables[(size_t)(s + 1) * row];
   shares = __any(shares);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  for (int o = 32; o >= 1; o >>= 1) {
+    mine += __shfl_xor(mine, o, 64);
+    nonempty += __shfl_xor(nonempty, o, 64);
+  }
   if (lane == 0) {
     sh_sum[wave] = mine;
+    sh_nonempty[wave] = nonempty;
     sh_shares[wave] = shares;
   }
-  if (threadIdx.x < kWaves) sh_start_s[threadIdx.x] = -1;
   __syncthreads();
   long long per_head = 0;
+  long long seqs_nonempty = 0;
   bool shared = false;
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) {
     per_head += sh_sum[k];
+    seqs_nonempty += sh_nonempty[k];
     shared |= sh_shares[k] != 0;
   }
   // quad: the workgroup is one worker over units of kWaves consecutive KV heads.
@@ -602,37 +632,68 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     plan.C = 1;
     plan.nd = 0;
   }
+  // Piece cost, kept below half a worker's share of steps so that no static worker's cost range
+  // falls inside one piece's overhead (every static worker gets at least one step).
+  plan.A = dynamic ? 0 : min((long long)p.piece_cost, plan.T / plan.ns / 2);
+  plan.CT = plan.S + plan.A * seqs_nonempty * U;
   const long long wbase = (long long)blockIdx.x * kWaves;
+  // Workers whose starts this block needs: its own (1 with quads, else kWaves) and the next one.
+  const int n_own = quad ? 1 : kWaves;
+  const long long wfirst = quad ? (long long)blockIdx.x : wbase;
+  if (threadIdx.x <= n_own) {
+    sh_start_s[threadIdx.x] = -1;
+    sh_start_off[threadIdx.x] = 0;
+    sh_start_j[threadIdx.x] = 0;
+    sh_start_x[threadIdx.x] = plan.S;  // workers at or past ns start (and end) at S
+  }
+  __syncthreads();
 
   // Prefix sums over sequences: locate where each static worker of this block starts, and keep
   // the prefix in LDS for the dynamic chunks.
-  long long base = 0;
+  long long base = 0, ne_base = 0;
   for (int c = 0; c < B; c += kThreads) {
     const int s = c + threadIdx.x;
     const int n = (c == 0) ? n_first : (s < B ? steps_of(p, s) : 0);
+    const int ne = n > 0;
     const int incl = wave_inclusive_scan(n);
-    if (lane == 63) sh_scan[wave] = incl;
+    const int ne_incl = wave_inclusive_scan(ne);
+    if (lane == 63) {
+      sh_scan[wave] = incl;
+      sh_scan_ne[wave] = ne_incl;
+    }
     __syncthreads();
-    int before = 0, chunk = 0;
+    int before = 0, chunk = 0, ne_before = 0, ne_chunk = 0;
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) {
       before += (k < wave) ? sh_scan[k] : 0;
       chunk += sh_scan[k];
+      ne_before += (k < wave) ? sh_scan_ne[k] : 0;
+      ne_chunk += sh_scan_ne[k];
     }
     const long long excl = base + before + incl - n;
     if (dynamic && s < B) seq_prefix[s] = (int)excl;
-    const long long lo = excl * U;
-    const long long hi = (excl + n) * U;
-#pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
-      const long long wk = quad ? (long long)blockIdx.x : wbase + k;
-      const long long x0 = plan.start(wk);
-      if (wk < plan.ns && x0 >= lo && x0 < hi) {
-        sh_start_s[k] = s;
-        sh_start_off[k] = x0 - lo;
+    if (n > 0) {
+      // The sequence's U units cover cost positions [c_lo, c_lo + U*(n + A)).
+      const long long lo = excl * U;
+      const long long j0 = (ne_base + ne_before + ne_incl - ne) * U;
+      const long long c_lo = lo + plan.A * j0;
+      const long long per_unit = n + plan.A;
+      for (int k = 0; k <= n_own; ++k) {
+        const long long wk = wfirst + k;
+        if (wk >= plan.ns) break;
+        const long long t = plan.target(wk);
+        if (t >= c_lo && t < c_lo + U * per_unit) {
+          const long long kk = (t - c_lo) / per_unit;
+          const long long o = max(0LL, t - c_lo - kk * per_unit - plan.A);
+          sh_start_s[k] = s;
+          sh_start_off[k] = kk * n + o;
+          sh_start_j[k] = j0 + kk;
+          sh_start_x[k] = lo + kk * n + o;
+        }
       }
     }
     base += chunk;
+    ne_base += ne_chunk;
     __syncthreads();
   }
   if (dynamic && threadIdx.x == 0) seq_prefix[B] = (int)base;
@@ -642,9 +703,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // One instantiation of the worker per load kind (the choice is uniform over the grid).
   auto body = [&](auto stream) {
     constexpr bool S = decltype(stream)::value;
+    const int k = quad ? 0 : wave;
     if (w < plan.ns)
-      run_worker<D, G, Depth, S>(p, plan, w, sh_start_s[wave], sh_start_off[wave], p_lds[wave],
-                                 nullptr, quad);
+      run_worker<D, G, Depth, S>(p, plan, w, sh_start_s[k], sh_start_off[k], sh_start_j[k],
+                                 sh_start_x[k], sh_start_x[k + 1], p_lds[wave], nullptr, quad);
     if (!dynamic) return;  // block-uniform
 
     // Dynamic chunks, each shared by the whole workgroup (one counter increment per chunk; the
@@ -667,7 +729,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         else hi = mid;
       }
       run_worker<D, G, Depth, S, true>(p, plan, plan.ns + d, lo,
-                                       x0 - (long long)seq_prefix[lo] * Hkv, p_lds[wave], coop_st);
+                                       x0 - (long long)seq_prefix[lo] * Hkv, 0, x0,
+                                       plan.start(plan.ns + d + 1), p_lds[wave], coop_st);
       __syncthreads();  // every thread has read sh_chunk
       if (threadIdx.x == 0) sh_chunk = nxt;
       __syncthreads();

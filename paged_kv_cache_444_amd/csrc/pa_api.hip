@@ -266,6 +266,7 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
   // Head quads (four KV heads per workgroup worker) need a multiple of four KV heads.
   p.quad = p.static_frac_q10 == 1024 && num_kv_heads % 4 == 0 &&
            env_int("PA_DECODE_QUAD", 1, 0, 1);
+  p.piece_cost = env_int("PA_DECODE_PIECE_COST", 6, 0, 64);
   p.len_cap = max_seq_len;
   p.scale_log2 = scale * 1.4426950408889634f;
   char* base = static_cast<char*>(workspace);

@@ -32,6 +32,9 @@ struct DecodeParams {
   // 4*unit + r), so the four waves of a CU read neighbouring 4 KB tiles of the same block
   // together.  Static split only; num_kv_heads a multiple of four.
   int quad;
+  // Cost of starting a piece, in steps: the static split balances steps plus this much per unit
+  // a worker starts, since each piece begins with dependent loads that nothing overlaps.
+  int piece_cost;
   // Lengths are clamped to this (min of max_seq_len and the table width) so a length beyond the
   // caller's bound cannot take a kernel outside the table.
   int len_cap;

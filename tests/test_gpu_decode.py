@@ -232,6 +232,29 @@ def test_decode_head_quads_named(cfg, monkeypatch):
     assert_close(got[seqs], ref[seqs], f"decode over head quads, workload {cfg}")
 
 
+@pytest.mark.parametrize("quad", ["0", "1"])
+@pytest.mark.parametrize("piece_cost,workers", [("0", None), ("1", "8"), ("6", None), ("64", "12"),
+                                                ("64", None)])
+def test_decode_piece_cost_split(quad, piece_cost, workers, monkeypatch):
+    """The static split weighs every unit a worker starts as extra steps.  Any weight (clamped to
+    half a worker's share of steps) must still give each worker a non-empty range, owners that the
+    merge agrees with, and the oracle's result, with many short and empty sequences between long
+    ones."""
+    case = build_case(Spec(name="piece_cost", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=16, seed=(29, int(piece_cost)),
+                           decode_lens=[1, 0, 17, 2000, 3, 16, 0, 33, 700, 1, 1, 4100, 250, 0, 9]))
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    monkeypatch.setenv("PA_DECODE_QUAD", quad)
+    monkeypatch.setenv("PA_DECODE_PIECE_COST", piece_cost)
+    if workers:
+        monkeypatch.setenv("PA_DECODE_WORKERS", workers)
+    say(f"decode piece cost {piece_cost}, quad {quad}, workers {workers}")
+    a = gpu_decode(case, kc, vc)
+    assert np.array_equal(a, gpu_decode(case, kc, vc))
+    assert_close(upcast(a), oracle_decode(case, case.key_cache, case.value_cache),
+                 f"decode with piece cost {piece_cost}")
+
+
 def test_decode_workspace_sizes_on_device():
     n = pa.decode_workspace_bytes(128, 64, 8, 128, 8192)
     assert n >= 128 * 8 * 8 * (128 + 2) * 4  # at least one partial slot per unit

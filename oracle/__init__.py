@@ -6,14 +6,15 @@ the benchmark's CPU-baseline leg may import it; the library and its Python
 binding never do, and this package imports nothing from them.
 
 Contents
-  paged_attention  scatter of new K/V rows into pool slots, block-table gather,
-                   decode attention and causal prefill-chunk attention (fp64)
+  paged_attention  scatter of new K/V rows into pool slots, whole-block copies
+                   for copy-on-write, block-table gather, decode attention and
+                   causal prefill-chunk attention (fp64)
   kv_memory        the KV-cache size formula and reservation-waste arithmetic
 
 Every function is pinned by a test in tests/ against something other than
 itself: closed forms, invariants stated by the pages (block placement does not
 change the result, paged equals contiguous, shared prompt blocks equal private
-copies), a library attention routine on special cases, or values the pages
+copies, a copy-on-write step equals private sequences), a library attention routine on special cases, or values the pages
 print.  Parity of the attention values is pinned only through those checks: the
 pages print no attention outputs.
 """

@@ -100,6 +100,40 @@ def reshape_and_cache(key_cache: np.ndarray, value_cache: np.ndarray, key: np.nd
     return kc, vc
 
 
+def copy_blocks(key_cache: np.ndarray, value_cache: np.ndarray,
+                block_mapping: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Copy whole physical blocks, K and V, every KV head; return the new pool images (copies).
+
+    Copy-on-write: sequences that share a prompt reference the same physical
+    blocks, and a sequence receives its own block only where it diverges from
+    the others ("Inference optimization" lesson, Paged attention section;
+    vLLM-on-H100 article, PagedAttention section, on rollouts that share a
+    prompt's pages until their completions diverge).  A sequence about to write
+    into a block that others still reference first gets a fresh block holding a
+    copy of the shared one; this is that copy.
+
+    `block_mapping` is int64 [n][2] of (source, destination) block ids.  Each
+    destination takes the source's contents as they were before the call.
+    Destinations must be distinct and none may also be a source; otherwise the
+    result would depend on the order of the copies, so the oracle refuses it.
+    """
+    m = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    n = key_cache.shape[0]
+    src, dst = m[:, 0], m[:, 1]
+    if m.size and (min(src.min(), dst.min()) < 0 or max(src.max(), dst.max()) >= n):
+        raise ValueError("block id outside the pool")
+    if np.unique(dst).size != dst.size:
+        raise ValueError("duplicate destination blocks")
+    if np.intersect1d(src, dst).size:
+        raise ValueError("a destination block is also a source")
+    kc = key_cache.copy()
+    vc = value_cache.copy()
+    for s, d in zip(src.tolist(), dst.tolist()):
+        kc[d] = key_cache[s]
+        vc[d] = value_cache[s]
+    return kc, vc
+
+
 def gather_kv(key_cache: np.ndarray, value_cache: np.ndarray, block_table_row: Sequence[int],
               seq_len: int, num_kv_heads: int, head_dim: int,
               block_size: int) -> Tuple[np.ndarray, np.ndarray]:

@@ -18,7 +18,7 @@ import torch
 
 from oracle import kv_memory
 from oracle import paged_attention as pa
-from workloads import BlockAllocator, Spec, bf16_bits, build_case, lognormal_lengths
+from workloads import BlockAllocator, Spec, bf16_bits, build_case, build_cow_case, lognormal_lengths
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -405,6 +405,111 @@ def test_zero_length_sequence_gives_zeros():
     case = small_case(13, lens=(0, 5))
     out = oracle_decode(case)
     assert np.array_equal(out[0], np.zeros_like(out[0]))
+
+
+# ---------------------------------------------------------------- copy-on-write
+
+def test_copy_blocks_closed_form_and_rejections():
+    rng = np.random.default_rng(21)
+    kc = rng.integers(0, 1 << 16, size=(12, 2 * 16 * 64), dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, size=(12, 2 * 16 * 64), dtype=np.uint16)
+    m = np.array([[3, 7], [3, 9], [0, 11]])
+    k2, v2 = pa.copy_blocks(kc, vc, m)
+    for b in range(12):
+        src = {7: 3, 9: 3, 11: 0}.get(b, b)
+        assert np.array_equal(k2[b], kc[src]) and np.array_equal(v2[b], vc[src])
+    # inputs are not modified; an empty mapping is the identity
+    assert not np.array_equal(kc[7], kc[3])
+    k3, v3 = pa.copy_blocks(kc, vc, np.zeros((0, 2), dtype=np.int64))
+    assert np.array_equal(k3, kc) and np.array_equal(v3, vc)
+    for bad in ([[1, 2], [3, 2]], [[1, 2], [2, 4]], [[1, 12]], [[-1, 2]]):
+        with pytest.raises(ValueError):
+            pa.copy_blocks(kc, vc, np.array(bad))
+
+
+def test_cow_rule_keeps_refcounts():
+    alloc = BlockAllocator(8)
+    a = alloc.allocate(2)
+    alloc.share(a)
+    alloc.share(a)  # three holders
+    t1, t2, t3 = list(a), list(a), list(a)
+    p1 = alloc.prepare_write(t1, 20, 16)
+    assert p1 == (a[1], t1[1]) and t1[0] == a[0] and alloc.refcount(a[1]) == 2
+    assert alloc.refcount(t1[1]) == 1
+    p2 = alloc.prepare_write(t2, 17, 16)
+    assert p2 is not None and alloc.refcount(a[1]) == 1
+    assert alloc.prepare_write(t3, 31, 16) is None and t3 == a  # last holder writes in place
+    assert alloc.prepare_write(t1, 21, 16) is None  # already private
+    assert alloc.num_free == 8 - 4
+
+
+def _cow_expected(case):
+    """Each candidate's decode output computed without any block copy: its K/V gathered from the
+    pool as it was before the step through its table before the step, the new token appended."""
+    d, r = case.decode, case.reshape
+    Hkv, D, bs = case.num_kv_heads, case.head_dim, case.block_size
+    out = np.zeros(d.query.shape)
+    for b, table in enumerate(case.info["tables_before"]):
+        L = int(d.seq_lens[b])
+        k, v = pa.gather_kv(case.key_cache, case.value_cache, table, L - 1, Hkv, D, bs)
+        k = np.concatenate([k, pa.bf16_to_f64(r.key[b])[None]])
+        v = np.concatenate([v, pa.bf16_to_f64(r.value[b])[None]])
+        out[b] = pa.attention(pa.bf16_to_f64(d.query[b])[None], k, v, case.scale)[0]
+    return out
+
+
+def _cow_step(case, copies):
+    kc, vc = pa.copy_blocks(case.key_cache, case.value_cache, copies)
+    r = case.reshape
+    kc, vc = pa.reshape_and_cache(kc, vc, r.key, r.value, r.slot_mapping, case.num_kv_heads,
+                                  case.head_dim, case.block_size)
+    d = case.decode
+    return pa.decode(d.query, kc, vc, d.block_tables, d.seq_lens, case.num_kv_heads,
+                     case.head_dim, case.block_size, case.scale)
+
+
+def test_cow_step_equals_private_sequences():
+    # Two prompts of 37 tokens (the third 16-token block is partial) with four candidates each;
+    # some candidates already diverged.  Copy-on-write must give every candidate exactly the
+    # attention it would get with its own private cache.
+    case, copies = build_cow_case("cow", 2, 4, 37, 8, 2, 64, 16, (444, 7),
+                                  tails=[0, 0, 3, 11, 0, 5, 0, 20])
+    assert len(copies) == 2
+    assert np.array_equal(_cow_step(case, copies), _cow_expected(case))
+    # Without the copies the candidates of a group would write the same slot.
+    with pytest.raises(ValueError):
+        _cow_step_without_copies(case)
+
+
+def _cow_step_without_copies(case):
+    d, r = case.decode, case.reshape
+    bs = case.block_size
+    slots = []
+    for b, t in enumerate(case.info["tables_before"]):
+        pos = int(d.seq_lens[b]) - 1
+        blk = t[pos // bs] if pos // bs < len(t) else int(d.block_tables[b, pos // bs])
+        slots.append(blk * bs + pos % bs)
+    pa.reshape_and_cache(case.key_cache, case.value_cache, r.key, r.value, np.array(slots),
+                         case.num_kv_heads, case.head_dim, case.block_size)
+
+
+def test_cow_pin_catches_planted_copy_mistakes(monkeypatch):
+    case, copies = build_cow_case("cow", 2, 4, 37, 8, 2, 64, 16, (444, 7),
+                                  tails=[0, 0, 3, 11, 0, 5, 0, 20])
+    want = _cow_expected(case)
+    real = pa.copy_blocks
+
+    def k_only(kc, vc, m):
+        k2, _ = real(kc, vc, m)
+        return k2, vc.copy()
+
+    def reversed_pairs(kc, vc, m):
+        return real(kc, vc, np.asarray(m)[:, ::-1])
+
+    for fake in (k_only, reversed_pairs):
+        with monkeypatch.context() as mp:
+            mp.setattr(pa, "copy_blocks", fake)
+            assert not np.array_equal(_cow_step(case, copies), want), fake.__name__
 
 
 # ---------------------------------------------------------------- planted mistakes

@@ -16,6 +16,7 @@ from .inputs import (  # noqa: F401
     Spec,
     bf16_bits,
     build_case,
+    build_cow_case,
     lognormal_lengths,
     named_case,
     NAMED_CASES,

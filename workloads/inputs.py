@@ -141,6 +141,25 @@ class BlockAllocator:
     def refcount(self, b: int) -> int:
         return int(self._ref[b])
 
+    def prepare_write(self, table: List[int], pos: int, block_size: int) -> Optional[Tuple[int, int]]:
+        """Copy-on-write before a sequence writes logical position `pos`.
+
+        If the block holding `pos` is still referenced by other sequences, the
+        writer takes a fresh block, drops its reference to the shared one and
+        points its table entry at the fresh block; the returned (source,
+        destination) pair is the copy that must run before the write.  A block
+        with a single holder is written in place (returns None), so the last
+        sequence still holding a shared block keeps it.
+        """
+        j = pos // block_size
+        b = int(table[j])
+        if self._ref[b] <= 1:
+            return None
+        fresh = self.allocate(1)[0]
+        self.release([b])
+        table[j] = fresh
+        return b, fresh
+
 
 @dataclasses.dataclass
 class DecodeBatch:
@@ -333,6 +352,92 @@ def build_case(spec: Spec) -> Case:
                 num_blocks=num_blocks, poison_block=poison,
                 scale=np.float32(1.0 / math.sqrt(D)), key_cache=kc, value_cache=vc,
                 reshape=reshape, decode=decode, prefill=prefill, info=info)
+
+
+def build_cow_case(name: str, num_prompts: int, candidates: int, prompt_len: int,
+                   num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                   seed: Tuple[int, ...], tails: Optional[Sequence[int]] = None,
+                   pool_slack: float = 1.1) -> Tuple[Case, np.ndarray]:
+    """Rollouts that share a prompt whose last block is only partly filled, at the step where
+    each candidate writes its next token.
+
+    Every candidate of a group references the prompt's blocks, the last one partial (prompt_len
+    need not be a multiple of block_size).  Candidate c already holds `tails[c]` generated tokens
+    (default 0); the first tokens of a tail that fall into the shared partial block were written
+    into a private copy of it when that candidate diverged.  The step appends one token per
+    candidate at position prompt_len + tail; a candidate whose token lands in a block still
+    shared gets a copy first (BlockAllocator.prepare_write).  Returns the case, whose reshape
+    batch holds the new tokens and whose decode batch attends prompt_len + tail + 1 keys, and the
+    int64 [n][2] (source, destination) copies to run before the reshape.  The pool holds the
+    state before the step: drawn contents everywhere, the private copies already made.
+    """
+    rng = np.random.default_rng(list(seed))
+    Hq, Hkv, D, bs = num_q_heads, num_kv_heads, head_dim, block_size
+    B = num_prompts * candidates
+    tails = [0] * B if tails is None else [int(t) for t in tails]
+    shared_blocks = _blocks_for(prompt_len, bs)
+    lens = [prompt_len + t + 1 for t in tails]
+    # Upper bound of the blocks the step can need: the shared prompt blocks once per group, each
+    # candidate's private blocks, and one copy per candidate.
+    needed = num_prompts * shared_blocks + sum(_blocks_for(L, bs) for L in lens) + B
+    usable = math.ceil(pool_slack * needed)
+    num_blocks = usable + 1
+    poison = usable
+    alloc = BlockAllocator(usable, rng)
+
+    elems = Hkv * bs * D
+    kc = normal_bf16(seed, 3, num_blocks * elems).reshape(num_blocks, elems)
+    vc = normal_bf16(seed, 4, num_blocks * elems).reshape(num_blocks, elems)
+    kc[poison] = BF16_NAN
+    vc[poison] = BF16_NAN
+
+    tables: List[List[int]] = []
+    for g in range(num_prompts):
+        prompt = alloc.allocate(shared_blocks)
+        alloc.share(prompt * (candidates - 1))
+        for c in range(candidates):
+            t = list(prompt)
+            tail = tails[g * candidates + c]
+            # Earlier divergence: a tail that reached into the partial block made a private copy.
+            if tail > 0 and prompt_len % bs:
+                pair = alloc.prepare_write(t, prompt_len, bs)
+                if pair is not None:
+                    kc[pair[1]] = kc[pair[0]]
+                    vc[pair[1]] = vc[pair[0]]
+            extra = _blocks_for(prompt_len + tail, bs) - shared_blocks
+            if extra > 0:
+                t += alloc.allocate(extra)
+            tables.append(t)
+
+    tables_before = [list(t) for t in tables]
+    # The step: one new token per candidate at position prompt_len + tail.
+    copies: List[Tuple[int, int]] = []
+    slots: List[int] = []
+    for b, t in enumerate(tables):
+        pos = prompt_len + tails[b]
+        if pos // bs >= len(t):
+            t += alloc.allocate(1)
+        pair = alloc.prepare_write(t, pos, bs)
+        if pair is not None:
+            copies.append(pair)
+        slots.append(t[pos // bs] * bs + pos % bs)
+
+    width = max(len(t) for t in tables)
+    bt = np.full((B, width), poison, dtype=np.int32)
+    for r, t in enumerate(tables):
+        bt[r, :len(t)] = t
+    reshape = ReshapeBatch(key=normal_bf16(seed, 5, B * Hkv * D).reshape(B, Hkv, D),
+                           value=normal_bf16(seed, 6, B * Hkv * D).reshape(B, Hkv, D),
+                           slot_mapping=np.asarray(slots, dtype=np.int64))
+    decode = DecodeBatch(block_tables=bt, seq_lens=np.asarray(lens, dtype=np.int32),
+                         query=normal_bf16(seed, 1, B * Hq * D).reshape(B, Hq, D))
+    info = {"pool_blocks_usable": usable, "prompt_len": prompt_len, "tails": tails,
+            "copies": len(copies), "free_blocks_after": alloc.num_free,
+            "tables_before": tables_before}
+    case = Case(name=name, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                num_blocks=num_blocks, poison_block=poison, scale=np.float32(1.0 / math.sqrt(D)),
+                key_cache=kc, value_cache=vc, reshape=reshape, decode=decode, info=info)
+    return case, np.asarray(copies, dtype=np.int64).reshape(-1, 2)
 
 
 # ----------------------------------------------------------------------------------------

@@ -21,8 +21,11 @@ previous step filled.  Prints one JSON line.
                prefill kernel's MFMA roofline (causal FLOPs / its event-timed duration against the
                2.5 PFLOP/s dense bf16 peak)
 
+  cow_step     a copy-on-write step of rollouts sharing a 4,100-token prompt (8 prompts x 16
+               candidates): block copies, the new tokens' reshape and the decode, per kernel
+
 `--mode copy` instead times a plain device-to-device copy of a known size: the calibration run for
-the FETCH_SIZE / WRITE_SIZE hardware counters.  `--mode mixed` runs only the mixed step.
+the FETCH_SIZE / WRITE_SIZE hardware counters.  `--mode mixed` / `--mode cow` run only that step.
 """
 
 from __future__ import annotations
@@ -101,10 +104,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over the whole batch until this much CPU time is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["decode", "copy", "mixed"], default="decode")
+    ap.add_argument("--mode", choices=["decode", "copy", "mixed", "cow"], default="decode")
     ap.add_argument("--mixed-steps", type=int, default=30)
     ap.add_argument("--mixed-warmup", type=int, default=60)
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-step measurement")
+    ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write step measurement")
+    ap.add_argument("--cow-steps", type=int, default=50)
     ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
 
@@ -147,6 +152,9 @@ def main():
         return
     if args.mode == "mixed":
         print(json.dumps(run_mixed(args)), flush=True)
+        return
+    if args.mode == "cow":
+        print(json.dumps(run_cow(args)), flush=True)
         return
 
     import paged_kv_cache_444_amd as pa
@@ -226,6 +234,9 @@ def main():
         del pools, kc0, vc0
         torch.cuda.empty_cache()
         mixed = run_mixed(args)
+    cow = None
+    if not args.no_cow:
+        cow = run_cow(args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -266,6 +277,7 @@ def main():
         },
         "warm_single_pool_us_per_step": None if warm_us is None else round(warm_us, 2),
         "mixed_step": mixed,
+        "cow_step": cow,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -346,6 +358,74 @@ def run_mixed(args):
         "decode_gbs": round(dbytes / (per["decode_partition"] * 1e-6) / 1e9, 1),
         "reshape_gbs": round(rbytes / (per["reshape_and_cache"] * 1e-6) / 1e9, 1),
         "reshape_bytes": rbytes, "decode_bytes": dbytes,
+    }
+
+
+def run_cow(args):
+    """Copy-on-write step of rollouts at the 70B shape: 8 prompts x 16 candidates share a
+    4,100-token prompt whose last block holds 4 tokens.  Every candidate writes its first token at
+    position 4,100; all but the last holder of each group first copy that block (120 copies), then
+    the 128 tokens are written and the 128 sequences decoded.  Repeating the step rewrites the same
+    bytes, so every repetition does the same work."""
+    import torch
+
+    import paged_kv_cache_444_amd as pa
+    from workloads import build_cow_case
+
+    log("generating the copy-on-write rollout step")
+    case, copies = build_cow_case("cow_rollouts_8x16_prompt4100", 8, 16, 4100, 64, 8, 128, 16,
+                                  (444, 64))
+    Hq, Hkv, D, bs = case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+    d, r = case.decode, case.reshape
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    kc, vc = dev(case.key_cache), dev(case.value_cache)
+    cm = torch.from_numpy(copies).cuda()
+    rk, rv, slots = dev(r.key), dev(r.value), torch.from_numpy(r.slot_mapping).cuda()
+    q, bt, sl = dev(d.query), torch.from_numpy(d.block_tables).cuda(), torch.from_numpy(d.seq_lens).cuda()
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(pa.decode_workspace_bytes(d.num_seqs, Hq, Hkv, D, d.max_seq_len), 1),
+                     dtype=torch.uint8, device="cuda")
+    kw = dict(num_kv_heads=Hkv, head_dim=D, block_size=bs)
+
+    def step():
+        pa.copy_blocks(kc, vc, cm, **kw)
+        pa.reshape_and_cache(rk, rv, kc, vc, slots, **kw)
+        pa.decode(q, kc, vc, bt, sl, num_kv_heads=Hkv, block_size=bs, scale=float(case.scale),
+                  max_seq_len=d.max_seq_len, out=out, workspace=ws)
+
+    for _ in range(20):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.cow_steps):
+        step()
+    torch.cuda.synchronize()
+    us_step = (time.perf_counter() - t0) * 1e6 / args.cow_steps
+    names = ("copy_blocks", "reshape_and_cache", "decode_partition", "decode_merge")
+    pa.trace_enable(True)
+    for n in names:
+        pa.trace_read(n)
+    for _ in range(args.cow_steps):
+        step()
+    torch.cuda.synchronize()
+    per = {}
+    for n in names:
+        k, ms = pa.trace_read(n)
+        per[n] = round(ms / k * 1e3, 2) if k else None
+    pa.trace_enable(False)
+    block_bytes = Hkv * bs * D * 2
+    cbytes = 4 * len(copies) * block_bytes  # K and V blocks, each read once and written once
+    log(f"copy-on-write step {us_step:.1f} us")
+    return {
+        "workload": case.name, "us_per_step": round(us_step, 2), "steps": args.cow_steps,
+        "copies": len(copies), "new_tokens": len(r.slot_mapping), "kernel_us": per,
+        "copy_blocks_bytes": cbytes,
+        "copy_blocks_gbs": round(cbytes / (per["copy_blocks"] * 1e-6) / 1e9, 1),
+        "decode_logical_gbs": round(decode_bytes(d.seq_lens, Hq, Hkv, D, bs)
+                                    / (per["decode_partition"] * 1e-6) / 1e9, 1),
     }
 
 

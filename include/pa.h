@@ -79,6 +79,30 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_
                                  int32_t block_size, int64_t num_blocks, void* stream);
 
 /*
+ * pa_copy_blocks — copy whole physical blocks (K and V, every KV head) for copy-on-write.
+ *
+ * Source: sequences that share a prompt reference the prompt's physical blocks, and a sequence
+ * receives a block of its own only where it diverges ("Inference optimization" lesson, section
+ * "Paged attention"; vLLM-on-H100 article, PagedAttention section: rollouts of one prompt share
+ * its pages and copy only where their completions diverge).  Before a sequence writes into a
+ * block that others still reference, the caller allocates a fresh block, points that sequence's
+ * table entry at it and copies the shared block there with this call; pa_reshape_and_cache then
+ * writes the new token into the copy.
+ *
+ *   key_cache, value_cache  pools of num_blocks blocks (layout above), modified in place
+ *   block_mapping  int64 [num_pairs][2]: (source, destination) block ids; a pair with an id
+ *                  outside [0, num_blocks) is skipped
+ *   num_kv_heads, head_dim, block_size  the pools' shape (a block is
+ *                  num_kv_heads*block_size*head_dim bf16 values in each pool)
+ * Destinations must be pairwise distinct and no destination may also be a source within one call
+ * (otherwise the result is unspecified); each destination then holds the bytes its source held
+ * before the call.  The copy is bit-exact.  num_pairs == 0 is a no-op.
+ */
+pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, int64_t num_blocks,
+                           const int64_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, void* stream);
+
+/*
  * Bytes of workspace pa_decode needs for this batch shape on the current device (0 if the shape is
  * unsupported or num_seqs <= 0).  The workspace holds partial softmax states of sequences whose
  * context is split over several waves and a counter that hands out work; it must be filled with
@@ -175,8 +199,9 @@ pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache
  * Kernel timing (tracing).  While enabled, every kernel the library launches is bracketed by a
  * pair of HIP events recorded on its stream.  pa_trace_read synchronises on the recorded events,
  * returns the number of launches and their summed duration (milliseconds) for one kernel name, and
- * forgets those records.  Kernel names: "reshape_and_cache", "decode_partition", "decode_merge",
- * "prefill_chunk", "prefill_merge".  Events are host-side driver objects; no device memory is used.
+ * forgets those records.  Kernel names: "reshape_and_cache", "copy_blocks", "decode_partition",
+ * "decode_merge", "prefill_chunk", "prefill_merge".  Events are host-side driver objects; no
+ * device memory is used.
  */
 pa_status_t pa_trace_enable(int32_t enable);
 pa_status_t pa_trace_read(const char* kernel_name, int32_t* launches, double* total_ms);

@@ -16,8 +16,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "load_library", "reshape_and_cache", "decode", "prefill_chunk", "decode_workspace_bytes",
-    "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
+    "load_library", "reshape_and_cache", "copy_blocks", "decode", "prefill_chunk",
+    "decode_workspace_bytes", "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
     "LIB_PATH",
 ]
 
@@ -44,6 +44,7 @@ _SIGNATURES = {
     "pa_version": (_I32, []),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_reshape_and_cache": (_I32, [_P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _P]),
+    "pa_copy_blocks": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _P]),
     "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pa_decode": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                          ctypes.c_float, _P, _SZ, _P]),
@@ -120,6 +121,18 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
                                     _bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache"),
                                     _ints(slot_mapping, torch.int64, "slot_mapping"), T, num_kv_heads,
                                     head_dim, block_size, n, _stream()))
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_mapping: torch.Tensor, *,
+                num_kv_heads: int, head_dim: int, block_size: int) -> None:
+    """Copy whole blocks of both pools: block_mapping int64 [n][2] of (source, destination) ids."""
+    lib = load_library()
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [n][2]")
+    n = _num_blocks(key_cache, num_kv_heads, block_size, head_dim)
+    _check(lib.pa_copy_blocks(_bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache"), n,
+                              _ints(block_mapping, torch.int64, "block_mapping"),
+                              block_mapping.shape[0], num_kv_heads, head_dim, block_size, _stream()))
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

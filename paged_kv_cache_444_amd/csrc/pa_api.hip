@@ -2,6 +2,7 @@
 // Every check that host scalars allow happens here, before any launch.
 
 #include "../../include/pa.h"
+#include "copy_blocks.h"
 #include "pa_internal.h"
 
 #include <algorithm>
@@ -194,6 +195,31 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_
   p.block_size = block_size;
   p.num_blocks = num_blocks;
   return hip_status(pa::launch_reshape(p, static_cast<hipStream_t>(stream)), "reshape_and_cache");
+}
+
+pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, int64_t num_blocks,
+                           const int64_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, void* stream) {
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs %d < 0", num_pairs);
+  if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d <= 0", num_kv_heads);
+  if (!supported_head_dim(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", head_dim);
+  if (!supported_block(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not in {16,32}", block_size);
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks %lld <= 0", (long long)num_blocks);
+  if (num_pairs == 0) return ok();
+  if (!key_cache || !value_cache || !block_mapping)
+    return fail(PA_ERR_NULL_POINTER, "null pointer argument");
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(block_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for the pools)");
+  pa::CopyBlocksParams p{};
+  p.kpool = static_cast<uint16_t*>(key_cache);
+  p.vpool = static_cast<uint16_t*>(value_cache);
+  p.mapping = block_mapping;
+  p.num_blocks = num_blocks;
+  p.block_vec16 = (int64_t)num_kv_heads * block_size * head_dim / 8;
+  p.num_pairs = num_pairs;
+  return hip_status(pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)), "copy_blocks");
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -64,4 +64,9 @@ def test_host_side_validation(lib):
     assert lib.pa_reshape_and_cache(z, z, 100, z, z, z, 1, 2, 128, 16, 10, z) == 2     # stride
     assert lib.pa_reshape_and_cache(z, z, 256, z, z, z, 0, 2, 128, 16, 10, z) == 0     # no tokens
     assert lib.pa_reshape_and_cache(z, z, 256, z, z, z, 1, 2, 128, 16, 0, z) == 2      # no blocks
+    assert lib.pa_copy_blocks(z, z, 10, z, 1, 2, 128, 16, z) == 1                  # nulls
+    assert lib.pa_copy_blocks(z, z, 10, z, -1, 2, 128, 16, z) == 2                 # pairs
+    assert lib.pa_copy_blocks(z, z, 10, z, 1, 2, 96, 16, z) == 3                   # head_dim
+    assert lib.pa_copy_blocks(z, z, 0, z, 1, 2, 128, 16, z) == 2                   # no blocks
+    assert lib.pa_copy_blocks(z, z, 10, z, 0, 2, 128, 16, z) == 0                  # no pairs
     assert lib.pa_trace_read(b"decode_partition", None, None) == 1

@@ -107,6 +107,8 @@ def parse():
     ap.add_argument("--mode", choices=["decode", "copy", "mixed", "cow"], default="decode")
     ap.add_argument("--mixed-steps", type=int, default=30)
     ap.add_argument("--mixed-warmup", type=int, default=60)
+    ap.add_argument("--mixed-order", choices=["decode-first", "prefill-first"], default="decode-first",
+                    help="which half of the overlapped mixed step is launched first")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-step measurement")
     ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write step measurement")
     ap.add_argument("--cow-steps", type=int, default=50)
@@ -311,30 +313,65 @@ def run_mixed(args):
                       dtype=torch.uint8, device="cuda")
     scale = float(case.scale)
 
-    def step():
-        pa.reshape_and_cache(rk, rv, kc, vc, slots, num_kv_heads=Hkv, head_dim=D, block_size=bs)
+    side = torch.cuda.Stream()
+    main_stream = torch.cuda.current_stream()
+
+    def do_prefill():
         pa.prefill_chunk(pq, kc, vc, pbt, pqsl, psl, num_kv_heads=Hkv, block_size=bs,
                          max_q_len=pf.max_q_len, max_seq_len=pf.max_seq_len, scale=scale, out=pout,
                          workspace=pws)
+
+    def do_decode():
         pa.decode(dq, kc, vc, dbt, dsl, num_kv_heads=Hkv, block_size=bs, scale=scale,
                   max_seq_len=dc.max_seq_len, out=dout, workspace=dws)
 
+    def serial_step():
+        pa.reshape_and_cache(rk, rv, kc, vc, slots, num_kv_heads=Hkv, head_dim=D, block_size=bs)
+        do_prefill()
+        do_decode()
+
+    pre_args = dict(query=pq, key_cache=kc, value_cache=vc, block_tables=pbt, query_start_loc=pqsl,
+                    seq_lens=psl, num_kv_heads=Hkv, block_size=bs, max_q_len=pf.max_q_len,
+                    max_seq_len=pf.max_seq_len, scale=scale, out=pout, workspace=pws)
+    dec_args = dict(query=dq, key_cache=kc, value_cache=vc, block_tables=dbt, seq_lens=dsl,
+                    num_kv_heads=Hkv, block_size=bs, scale=scale, max_seq_len=dc.max_seq_len,
+                    out=dout, workspace=dws)
+
+    def overlapped_step():
+        # The new tokens are written first; then decode runs on a second stream beside the
+        # prefill chunk, and the step ends when both have finished.
+        pa.reshape_and_cache(rk, rv, kc, vc, slots, num_kv_heads=Hkv, head_dim=D, block_size=bs)
+        if args.mixed_order == "decode-first":
+            pa.mixed_step(pre_args, dec_args, side_stream=side)
+            return
+        side.wait_stream(main_stream)
+        with torch.cuda.stream(side):
+            do_prefill()
+        do_decode()
+        main_stream.wait_stream(side)
+
     names = ("reshape_and_cache", "prefill_chunk", "prefill_merge", "decode_partition", "decode_merge")
-    # The matrix cores' clock ramps up over the first few tens of milliseconds of this load.
-    for _ in range(args.mixed_warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.mixed_steps):
-        step()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.mixed_steps
+
+    def timed(step):
+        # The matrix cores' clock ramps up over the first few tens of milliseconds of this load.
+        for _ in range(args.mixed_warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.mixed_steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.mixed_steps
+
+    ms_step = timed(serial_step)
+    ms_overlap = timed(overlapped_step)
+    ms_step2 = timed(serial_step)
     # Per-kernel durations from a second pass with events around every launch.
     pa.trace_enable(True)
     for n in names:
         pa.trace_read(n)
     for _ in range(args.mixed_steps):
-        step()
+        serial_step()
     torch.cuda.synchronize()
     per = {}
     for n in names:
@@ -346,10 +383,13 @@ def run_mixed(args):
     tflops = flops / (pre_us * 1e-6) / 1e12
     dbytes = decode_bytes(dc.seq_lens, Hq, Hkv, D, bs)
     rbytes = reshape_bytes(len(rs.slot_mapping), Hkv, D)
-    log(f"mixed step {ms_step * 1e3:.1f} us")
+    log(f"mixed step {ms_step * 1e3:.1f} us serial ({ms_step2 * 1e3:.1f} us again), "
+        f"{ms_overlap * 1e3:.1f} us with decode beside the prefill chunk")
     return {
         "workload": case.name, "us_per_step": round(ms_step * 1e3, 2), "steps": args.mixed_steps,
         "warmup": args.mixed_warmup,
+        "us_per_step_serial_again": round(ms_step2 * 1e3, 2),
+        "us_per_step_overlapped": round(ms_overlap * 1e3, 2), "overlap_order": args.mixed_order,
         "kernel_us": per,
         "prefill_roofline": {"bound": "mfma", "kernel": "prefill_chunk",
                              "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -419,11 +459,33 @@ def run_cow(args):
     block_bytes = Hkv * bs * D * 2
     cbytes = 4 * len(copies) * block_bytes  # K and V blocks, each read once and written once
     log(f"copy-on-write step {us_step:.1f} us")
+    # Larger copies on the same pools: a copy-on-write step moves too few blocks to reach the HBM
+    # rate, so the rate at 1,200 and 6,000 random pairs is reported beside it.
+    sweep = {}
+    rng = np.random.default_rng(7)
+    n_pool = case.num_blocks - 1  # the last block is the poison block
+    for pairs in (1200, 6000):
+        if 2 * pairs > n_pool:
+            continue
+        ids = rng.permutation(n_pool)
+        m = torch.from_numpy(np.stack([ids[:pairs], ids[pairs:2 * pairs]], 1).astype(np.int64)).cuda()
+        for _ in range(5):
+            pa.copy_blocks(kc, vc, m, **kw)
+        pa.trace_enable(True)
+        pa.trace_read("copy_blocks")
+        for _ in range(20):
+            pa.copy_blocks(kc, vc, m, **kw)
+        torch.cuda.synchronize()
+        k, ms = pa.trace_read("copy_blocks")
+        pa.trace_enable(False)
+        us = ms / k * 1e3
+        sweep[str(pairs)] = {"us": round(us, 2), "gbs": round(4 * pairs * block_bytes / us / 1e3, 1)}
     return {
         "workload": case.name, "us_per_step": round(us_step, 2), "steps": args.cow_steps,
         "copies": len(copies), "new_tokens": len(r.slot_mapping), "kernel_us": per,
         "copy_blocks_bytes": cbytes,
         "copy_blocks_gbs": round(cbytes / (per["copy_blocks"] * 1e-6) / 1e9, 1),
+        "copy_blocks_random_pairs": sweep,
         "decode_logical_gbs": round(decode_bytes(d.seq_lens, Hq, Hkv, D, bs)
                                     / (per["decode_partition"] * 1e-6) / 1e9, 1),
     }

@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "load_library", "reshape_and_cache", "copy_blocks", "decode", "prefill_chunk",
-    "decode_workspace_bytes", "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
+    "mixed_step", "decode_workspace_bytes", "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
     "LIB_PATH",
 ]
 
@@ -211,6 +211,37 @@ def prefill_chunk(query: torch.Tensor, key_cache: torch.Tensor, value_cache: tor
                                 num_kv_heads, D, block_size, block_tables.shape[1], max_seq_len,
                                 float(scale), ws, ws_bytes, _stream()))
     return out
+
+
+_side_streams = {}
+
+
+def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None):
+    """One chunked-prefill batch step: the prefill chunk and the decode of the other sequences run
+    side by side on two streams, so decode's HBM-bound work overlaps the matrix-core-bound chunk.
+
+    `prefill` and `decode_call` hold the keyword arguments of `prefill_chunk` and `decode`.  Both
+    halves start after the work already queued on the current stream (write every new token's
+    K/V with reshape_and_cache first), and the current stream waits for both before later work.
+    Decode is launched first, on `side_stream` (default: one stream per device, kept for reuse),
+    so its workgroups are resident before the prefill chunk's fill the remaining room.  Returns
+    (prefill output, decode output); the results are those of the two calls made one after the
+    other.
+    """
+    main = torch.cuda.current_stream()
+    if side_stream is None:
+        dev = main.device
+        side_stream = _side_streams.get(dev)
+        if side_stream is None:
+            side_stream = _side_streams[dev] = torch.cuda.Stream(device=dev)
+    side_stream.wait_stream(main)
+    with torch.cuda.stream(side_stream):
+        dout = decode(**decode_call)
+    pout = prefill_chunk(**prefill)
+    main.wait_stream(side_stream)
+    # The decode output (and a caller's tensors) are used on the current stream from here on.
+    dout.record_stream(main)
+    return pout, dout
 
 
 def trace_enable(on: bool = True) -> None:

@@ -26,6 +26,8 @@ from typing import Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
+from . import fp8
+
 SUB = 16    # tokens per sub-block
 SLICE = 32  # head-dimension slice of the K layout
 
@@ -247,3 +249,52 @@ def contiguous_attention(q: np.ndarray, k_contig: np.ndarray, v_contig: np.ndarr
     """Attention over an unpaged cache, as the Step 1 KVCache of the "Inference
     optimization" lesson keeps it: one array per sequence with positions in order."""
     return attention(q, k_contig, v_contig, scale)
+
+
+# ------------------------------------------------------------------------------------------
+# FP8 (E4M3) KV cache: the same block layout with one-byte codes, one scale per pool.
+# ------------------------------------------------------------------------------------------
+
+def reshape_and_cache_fp8(key_cache: np.ndarray, value_cache: np.ndarray, key: np.ndarray,
+                          value: np.ndarray, slot_mapping: np.ndarray, num_kv_heads: int,
+                          head_dim: int, block_size: int, k_scale: float,
+                          v_scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantise each new token's bf16 K/V rows to E4M3 codes (code = encode(x / scale), see
+    oracle.fp8) and write them into their slots of uint8 pools laid out like the bf16 pools,
+    one byte per element.  Returns the new pool images (copies)."""
+    return reshape_and_cache(key_cache, value_cache, fp8.quantize(key, k_scale),
+                             fp8.quantize(value, v_scale), slot_mapping, num_kv_heads, head_dim,
+                             block_size)
+
+
+def gather_kv_fp8(key_cache: np.ndarray, value_cache: np.ndarray, block_table_row: Sequence[int],
+                  seq_len: int, num_kv_heads: int, head_dim: int, block_size: int, k_scale: float,
+                  v_scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One sequence's dequantised K and V in logical order, [seq_len][Hkv][D] float64:
+    scale * value of the code, through the block table exactly as gather_kv."""
+    Hkv, D, bs = num_kv_heads, head_dim, block_size
+    _check_shape(Hkv, D, bs)
+    nb = -(-int(seq_len) // bs)
+    if nb == 0:
+        z = np.zeros((0, Hkv, D))
+        return z, z.copy()
+    ids = [int(b) for b in block_table_row[:nb]]
+    k = logical_blocks_k(key_cache, ids, Hkv, D, bs)
+    v = logical_blocks_v(value_cache, ids, Hkv, D, bs)
+    k = k.transpose(0, 2, 1, 3).reshape(nb * bs, Hkv, D)[:seq_len]
+    v = v.transpose(0, 2, 1, 3).reshape(nb * bs, Hkv, D)[:seq_len]
+    return float(k_scale) * fp8.decode(k), float(v_scale) * fp8.decode(v)
+
+
+def decode_fp8(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+               block_tables: np.ndarray, seq_lens: np.ndarray, num_kv_heads: int, head_dim: int,
+               block_size: int, scale: float, k_scale: float, v_scale: float,
+               seqs: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Decode over an FP8 cache: the attention of `decode` on the dequantised keys and values."""
+    B, Hq, D = query.shape
+    out = np.zeros((B, Hq, D))
+    for s in (range(B) if seqs is None else seqs):
+        k, v = gather_kv_fp8(key_cache, value_cache, block_tables[s], int(seq_lens[s]),
+                             num_kv_heads, head_dim, block_size, k_scale, v_scale)
+        out[s] = attention(bf16_to_f64(query[s])[None], k, v, scale)[0]
+    return out

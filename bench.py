@@ -111,6 +111,7 @@ def parse():
                     help="which half of the overlapped mixed step is launched first")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-step measurement")
     ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write step measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache decode measurement")
     ap.add_argument("--cow-steps", type=int, default=50)
     ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
@@ -230,6 +231,9 @@ def main():
     main_ms = ms_main / max(n_main, 1)
     main_gbs = nbytes / (main_ms * 1e-3) / 1e9
 
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = run_fp8_decode(args, case, pools, q, bt, sl, out, ws, ms_per_step, main_ms)
     n_pools = len(pools)
     mixed = None
     if not args.no_mixed:
@@ -269,6 +273,7 @@ def main():
             "decode_prefetch": int(os.environ.get("PA_DECODE_PREFETCH", "1")),
             "decode_static_q10": int(os.environ.get("PA_DECODE_STATIC_Q10", "1024")),
             "decode_chunk_steps": int(os.environ.get("PA_DECODE_CHUNK", "4")),
+            "decode_step": "matrix cores" if os.environ.get("PA_DECODE_MFMA") == "1" else "vector",
         },
         "roofline": {
             "bound": "hbm", "kernel": "decode_kernel", "achieved": round(main_gbs, 1),
@@ -278,11 +283,82 @@ def main():
             "ms_per_step_with_events": round((t3 - t2) * 1e3 / args.steps, 5),
         },
         "warm_single_pool_us_per_step": None if warm_us is None else round(warm_us, 2),
+        "fp8_decode": fp8,
         "mixed_step": mixed,
         "cow_step": cow,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def fp8_decode_bytes(seq_lens, Hq, Hkv, D, bs):
+    """Algorithmic bytes of one decode call over an FP8 cache: K and V one byte per element, the
+    bf16 query and output, the used table entries and the lengths."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    return int((L * Hkv * D * 2).sum()) + len(L) * 2 * Hq * D * 2 + \
+        int(((L + bs - 1) // bs).sum()) * 4 + len(L) * 4
+
+
+def run_fp8_decode(args, case, pools, q, bt, sl, out, ws, bf16_ms, bf16_kernel_ms):
+    """The same batch over an FP8 E4M3 cache (per-tensor scales 6/448 for K, 5.5/448 for V): the
+    bf16 pools are quantised on the device once (torch's float8_e4m3fn conversion after a clamp to
+    +-448; a synthetic-input step, outside the timed region), then timed like the bf16 decode."""
+    import torch
+
+    import paged_kv_cache_444_amd as pa
+
+    d = case.decode
+    Hq, Hkv, D, bs = case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+    ks, vs = 6.0 / 448.0, 5.5 / 448.0
+
+    def q8(t, s):
+        return (t.float() / s).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    pools8 = [(q8(kc, ks), q8(vc, vs)) for kc, vc in pools]
+    torch.cuda.synchronize()
+
+    def step(i):
+        kc8, vc8 = pools8[i % len(pools8)]
+        pa.decode_fp8(q, kc8, vc8, bt, sl, num_kv_heads=Hkv, block_size=bs, k_scale=ks, v_scale=vs,
+                      scale=float(case.scale), max_seq_len=d.max_seq_len, out=out, workspace=ws)
+
+    log("FP8 cache: warmup")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    pa.trace_enable(True)
+    pa.trace_read("decode_partition")
+    pa.trace_read("decode_merge")
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    n_main, ms_main = pa.trace_read("decode_partition")
+    n_merge, ms_merge = pa.trace_read("decode_merge")
+    pa.trace_enable(False)
+    kms = ms_main / max(n_main, 1)
+    nbytes = fp8_decode_bytes(d.seq_lens, Hq, Hkv, D, bs)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    kgbs = nbytes / (kms * 1e-3) / 1e9
+    log(f"FP8 cache: {ms * 1e3:.1f} us per call, kernel {kms * 1e3:.1f} us")
+    del pools8
+    return {
+        "kv_dtype": "fp8_e4m3", "k_scale": ks, "v_scale": vs, "algorithmic_bytes": nbytes,
+        "ms_per_step": round(ms, 5), "gbs": round(gbs, 1),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(d.num_seqs / (ms * 1e-3), 1),
+        "speedup_vs_bf16_call": round(bf16_ms / ms, 3),
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel (fp8)", "achieved": round(kgbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                     "launch_us": round(kms * 1e3, 2),
+                     "merge_launch_us": round(ms_merge / max(n_merge, 1) * 1e3, 2),
+                     "speedup_vs_bf16_kernel": round(bf16_kernel_ms / kms, 3)},
+        "prefetch_depth": int(os.environ.get("PA_DECODE_PREFETCH_FP8", "1")),
+    }
 
 
 def run_mixed(args):

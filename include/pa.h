@@ -79,6 +79,31 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_
                                  int32_t block_size, int64_t num_blocks, void* stream);
 
 /*
+ * FP8 KV cache.  The pages name FP8 as a serving precision (the "Serving engine internals" lesson
+ * quotes Llama 3.3 70B in FP8; the "Inference optimization" lesson lists FP8 quantization among
+ * kernel optimizations; the vLLM-on-H100 article names FP8 precision as a further lever) without
+ * fixing a format.  Here it is the OCP 8-bit E4M3 format (sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, largest finite 448, no infinities) with one scale per pool: a cached value is
+ * k_scale * (value of its code) for K and v_scale * (value of its code) for V.  FP8 pools have the
+ * layout above with one byte per element, so a block is num_kv_heads*block_size*head_dim bytes.
+ */
+
+/*
+ * pa_reshape_and_cache_fp8 — pa_reshape_and_cache into FP8 pools.  Each bf16 value x of a new
+ * token is stored as the E4M3 code of fp32(x) / scale (the correctly rounded fp32 quotient,
+ * rounded to the nearest E4M3 value with ties to even, magnitudes above 448 saturating to 448,
+ * NaN stored as 0x7F with x's sign).  key_cache / value_cache are byte pools; k_scale and v_scale
+ * must be finite and positive (PA_ERR_INVALID_ARG otherwise).  Other arguments, preconditions and
+ * errors as pa_reshape_and_cache.
+ */
+pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t kv_token_stride,
+                                     void* key_cache, void* value_cache,
+                                     const int64_t* slot_mapping, int32_t num_tokens,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int64_t num_blocks, float k_scale, float v_scale,
+                                     void* stream);
+
+/*
  * pa_copy_blocks — copy whole physical blocks (K and V, every KV head) for copy-on-write.
  *
  * Source: sequences that share a prompt reference the prompt's physical blocks, and a sequence
@@ -149,6 +174,21 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_fp8 — pa_decode over FP8 pools written by pa_reshape_and_cache_fp8, with the same
+ * k_scale and v_scale.  The attention is that of pa_decode on the dequantised cache: scores are
+ * scale * k_scale * (q · codes' values), outputs v_scale * (softmax-weighted codes' values); each
+ * code is widened to bf16 exactly and accumulated in fp32.  scale * k_scale must stay finite.
+ * Workspace, preconditions, limits and errors as pa_decode (same workspace size query).
+ */
+pa_status_t pa_decode_fp8(void* out, const void* query, const void* key_cache,
+                          const void* value_cache, int64_t num_blocks,
+                          const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                          float scale, float k_scale, float v_scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of workspace pa_prefill_chunk needs for this batch shape on the current device; 0 means

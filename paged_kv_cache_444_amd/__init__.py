@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "load_library", "reshape_and_cache", "copy_blocks", "decode", "prefill_chunk",
+    "load_library", "reshape_and_cache", "reshape_and_cache_fp8", "copy_blocks", "decode",
+    "decode_fp8", "prefill_chunk",
     "mixed_step", "decode_workspace_bytes", "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
     "LIB_PATH",
 ]
@@ -44,6 +45,10 @@ _SIGNATURES = {
     "pa_version": (_I32, []),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_reshape_and_cache": (_I32, [_P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _P]),
+    "pa_reshape_and_cache_fp8": (_I32, [_P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I64,
+                                        ctypes.c_float, ctypes.c_float, _P]),
+    "pa_decode_fp8": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                             ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _SZ, _P]),
     "pa_copy_blocks": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _P]),
     "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pa_decode": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -123,6 +128,34 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
                                     head_dim, block_size, n, _stream()))
 
 
+def _fp8_pool(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU uint8 tensor of E4M3 codes")
+    return t.data_ptr()
+
+
+def _num_blocks_fp8(pool: torch.Tensor, num_kv_heads: int, block_size: int, head_dim: int) -> int:
+    per = max(num_kv_heads * block_size * head_dim, 1)
+    return max(pool.numel() // per, 1)
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                          value_cache: torch.Tensor, slot_mapping: torch.Tensor, *, num_kv_heads: int,
+                          head_dim: int, block_size: int, k_scale: float, v_scale: float) -> None:
+    """reshape_and_cache into uint8 pools of E4M3 codes: code = E4M3(x / scale)."""
+    lib = load_library()
+    T = slot_mapping.numel()
+    if key.shape != value.shape or key.numel() != T * num_kv_heads * head_dim:
+        raise ValueError("key/value must be [T][num_kv_heads][head_dim]")
+    n = _num_blocks_fp8(key_cache, num_kv_heads, block_size, head_dim)
+    _check(lib.pa_reshape_and_cache_fp8(_bf16(key, "key"), _bf16(value, "value"),
+                                        num_kv_heads * head_dim, _fp8_pool(key_cache, "key_cache"),
+                                        _fp8_pool(value_cache, "value_cache"),
+                                        _ints(slot_mapping, torch.int64, "slot_mapping"), T,
+                                        num_kv_heads, head_dim, block_size, n, float(k_scale),
+                                        float(v_scale), _stream()))
+
+
 def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_mapping: torch.Tensor, *,
                 num_kv_heads: int, head_dim: int, block_size: int) -> None:
     """Copy whole blocks of both pools: block_mapping int64 [n][2] of (source, destination) ids."""
@@ -184,6 +217,32 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
                          _ints(block_tables, torch.int32, "block_tables"),
                          _ints(seq_lens, torch.int32, "seq_lens"), B, Hq, num_kv_heads, D, block_size,
                          block_tables.shape[1], max_seq_len, float(scale), ws, ws_bytes, _stream()))
+    return out
+
+
+def decode_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+               block_tables: torch.Tensor, seq_lens: torch.Tensor, *, num_kv_heads: int,
+               block_size: int, k_scale: float, v_scale: float, scale: Optional[float] = None,
+               max_seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged decode over uint8 pools of E4M3 codes (written by reshape_and_cache_fp8)."""
+    lib = load_library()
+    B, Hq, D = query.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(query)
+    ws, ws_bytes = _workspace(decode_workspace_bytes(B, Hq, num_kv_heads, D, max_seq_len), workspace,
+                              query.device)
+    n = _num_blocks_fp8(key_cache, num_kv_heads, block_size, D)
+    _check(lib.pa_decode_fp8(_bf16(out, "out"), _bf16(query, "query"),
+                             _fp8_pool(key_cache, "key_cache"), _fp8_pool(value_cache, "value_cache"),
+                             n, _ints(block_tables, torch.int32, "block_tables"),
+                             _ints(seq_lens, torch.int32, "seq_lens"), B, Hq, num_kv_heads, D,
+                             block_size, block_tables.shape[1], max_seq_len, float(scale),
+                             float(k_scale), float(v_scale), ws, ws_bytes, _stream()))
     return out
 
 

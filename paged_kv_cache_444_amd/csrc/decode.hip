@@ -36,6 +36,12 @@
 //           pairs with the probabilities read back from LDS as bf16 pairs.
 // The next step's K and V are loaded into a second register set while the current step is
 // computed.
+//
+// FP8 cache.  Pools of E4M3 codes keep the bf16 element order with one byte per element, so every
+// lane loads the same elements as above with 8-byte instead of 16-byte loads, and widens them to
+// bf16 pairs (v_cvt_scalef32_pk_bf16_fp8 with scale 1, exact: every E4M3 value is a bf16 value)
+// before the same step arithmetic.  The K scale is folded into the softmax scale and the V scale
+// multiplies each output row, so the codes are never rescaled one by one.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -109,11 +115,37 @@ struct Plan {
 // with three DPP adds.  Load (p, x) of the wave covers rows 8p .. 8p+7 of slices 2x and 2x+1:
 // two 512-byte runs of whole cache lines.  V-side: lane l holds head-dim rows l%32 + 32x of
 // octet l/32, so load x is 1 KB contiguous.
-template <int D>
+template <int D, bool Fp8 = false>
 struct StepRegs {
-  uint4 k[2][D / 64];
-  uint4 v[D / kSlice];
+  using T = std::conditional_t<Fp8, uint2, uint4>;  // 8 elements: bf16 or E4M3 codes
+  T k[2][D / 64];
+  T v[D / kSlice];
 };
+
+// Eight E4M3 codes -> eight bf16 values, same order (two per conversion).
+template <bool Hi>
+__device__ __forceinline__ uint32_t fp8_pair_to_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, Hi));
+}
+__device__ __forceinline__ uint4 widen8(const uint2& w) {
+  return make_uint4(fp8_pair_to_bf16<false>(w.x), fp8_pair_to_bf16<true>(w.x),
+                    fp8_pair_to_bf16<false>(w.y), fp8_pair_to_bf16<true>(w.y));
+}
+template <int D>
+__device__ __forceinline__ const StepRegs<D>& as_bf16(const StepRegs<D>& r) {
+  return r;
+}
+template <int D>
+__device__ __forceinline__ StepRegs<D> as_bf16(const StepRegs<D, true>& r) {
+  StepRegs<D> o;
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+    for (int x = 0; x < D / 64; ++x) o.k[pp][x] = widen8(r.k[pp][x]);
+#pragma unroll
+  for (int x = 0; x < D / kSlice; ++x) o.v[x] = widen8(r.v[x]);
+  return o;
+}
 
 // Query heads a lane computes probabilities for: heads c + 8j (j < kOwn) of the G sharing the
 // KV head, where c = lane % 8; for G < 8 only lanes with c < G own a head.
@@ -163,9 +195,27 @@ __device__ __forceinline__ uint4 load16(const uint16_t* ptr) {
     return *(const uint4*)ptr;
   }
 }
+// 8-byte load of eight E4M3 codes (FP8 pools).
+template <bool Stream>
+__device__ __forceinline__ uint2 load8(const uint8_t* ptr) {
+  if constexpr (Stream) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)ptr);
+    return make_uint2(v.x, v.y);
+  } else {
+    return *(const uint2*)ptr;
+  }
+}
+// Eight elements at element offset `off` of a pool: 16 bytes of bf16 or 8 bytes of codes.
+template <bool Stream, bool Fp8>
+__device__ __forceinline__ typename StepRegs<64, Fp8>::T load_elems(const uint16_t* pool,
+                                                                    size_t off) {
+  if constexpr (Fp8) return load8<Stream>(reinterpret_cast<const uint8_t*>(pool) + off);
+  else return load16<Stream>(pool + off);
+}
 
-template <int D, bool Stream>
-__device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodeParams& p,
+template <int D, bool Stream, bool Fp8>
+__device__ __forceinline__ void load_step(StepRegs<D, Fp8>& r, int i, const DecodeParams& p,
                                           const int* bt, int& win, int& ids,
                                           size_t head_off, size_t block_elems) {
   constexpr int R = D / kSlice;
@@ -180,20 +230,19 @@ __device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodePar
   }
   const int id = __builtin_amdgcn_readlane(ids, b - win);
   const size_t off = (size_t)id * block_elems + head_off + (size_t)(t0 & (bs - 1)) * D;
-  const uint16_t* kp = p.kpool + off;
-  const uint16_t* vp = p.vpool + off;
   const int c = lane & 7, tt = lane >> 3;
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
     for (int x = 0; x < D / 64; ++x) {
       const int d = 8 * c + 64 * x;
-      r.k[pp][x] = load16<Stream>(kp + (d >> 5) * (kSub * kSlice) + (8 * pp + tt) * kSlice +
-                                  (d & 31));
+      r.k[pp][x] = load_elems<Stream, Fp8>(
+          p.kpool, off + (d >> 5) * (kSub * kSlice) + (8 * pp + tt) * kSlice + (d & 31));
     }
   const int vd = lane & 31, vo = lane >> 5;
 #pragma unroll
-  for (int x = 0; x < R; ++x) r.v[x] = load16<Stream>(vp + (vd + 32 * x) * kSub + 8 * vo);
+  for (int x = 0; x < R; ++x)
+    r.v[x] = load_elems<Stream, Fp8>(p.vpool, off + (vd + 32 * x) * kSub + 8 * vo);
 }
 
 // One 16-token step: scores, online softmax, P·V.  nvalid = tokens of the step inside the piece
@@ -324,7 +373,7 @@ __device__ __forceinline__ void compute_step(const StepRegs<D>& r, const uint4 (
 // Depth is the number of steps whose loads are in flight while one step is computed.  With
 // `coop` set the wave's (m, l, acc) always goes to `coop` (its slot in LDS) and the workgroup
 // combines the slots; otherwise the piece is finished here.
-template <int D, int G, int Depth, bool Stream>
+template <int D, int G, int Depth, bool Stream, bool Fp8>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h, int j0, int take,
                                              int n_s, long long w, long long x, long long jn,
                                              const Plan& plan, uint16_t (*p_sh)[G][8],
@@ -391,35 +440,35 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   int i = j0;
   if constexpr (Depth == 0) {  // no prefetch: fewer registers, more resident waves
     while (true) {
-      StepRegs<D> ra;
-      load_step<D, Stream>(ra, i, p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      StepRegs<D, Fp8> ra;
+      load_step<D, Stream, Fp8>(ra, i, p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(as_bf16<D>(ra), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else if constexpr (Depth == 1) {
-    StepRegs<D> ra, rb;
-    load_step<D, Stream>(ra, i, p, bt, win, ids, head_off, block_elems);
+    StepRegs<D, Fp8> ra, rb;
+    load_step<D, Stream, Fp8>(ra, i, p, bt, win, ids, head_off, block_elems);
     while (true) {
-      load_step<D, Stream>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream, Fp8>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(as_bf16<D>(ra), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D, Stream>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(rb, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream, Fp8>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(as_bf16<D>(rb), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else {  // two steps in flight while one is computed
-    StepRegs<D> r0, r1, r2;
-    load_step<D, Stream>(r0, i, p, bt, win, ids, head_off, block_elems);
-    load_step<D, Stream>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+    StepRegs<D, Fp8> r0, r1, r2;
+    load_step<D, Stream, Fp8>(r0, i, p, bt, win, ids, head_off, block_elems);
+    load_step<D, Stream, Fp8>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
     while (true) {
-      load_step<D, Stream>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(r0, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream, Fp8>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(as_bf16<D>(r0), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D, Stream>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(r1, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream, Fp8>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(as_bf16<D>(r1), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D, Stream>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(r2, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream, Fp8>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(as_bf16<D>(r2), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   }
@@ -453,17 +502,254 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
       const float send = vo ? st.acc[g][k] : st.acc[g][k + R / 2];
       const float a = mine + __shfl_xor(send, 32, 64);
       const int d = vd + 32 * (k + (vo ? R / 2 : 0));
-      if (whole) orow[g * D + d] = to_bf16(a / lt);
+      if (whole) orow[g * D + d] = to_bf16(a * p.v_scale / lt);
       else slot[2 * G + g * D + d] = a;
     }
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Matrix-core step (FP8 pools).  With an FP8 cache a step carries half the bytes, and the vector
+// step above (about 430 instructions per 16-token step of one KV head with the conversions)
+// becomes the limit, not HBM.  The G query heads sharing a KV head make the step a small dense
+// contraction, so it runs on the matrix cores instead:
+//   S[token][head] = K·Qᵀ    v_mfma_f32_16x16x32_bf16 per 32-dim slice: A = K (row = token
+//                          lane%16, dims 8*(lane/16) .. +7 of the slice: 8 contiguous elements of
+//                          the K sub-block layout), B = Q (column = head lane%16, zero past G);
+//                          lane l ends up with tokens 4*(l/16) + i of head l%16.
+//   Oᵀ[dim][head] += Vᵀ·P   v_mfma_f32_16x16x16_bf16 per 16-dim tile: A = V (row = dim
+//                          16m + lane%16, tokens 4*(lane/16) .. +3: 4 contiguous elements of the
+//                          V sub-block layout), B = P, which the score product left in exactly
+//                          this operand layout, so probabilities never leave registers.
+// Each lane owns one head (column lane%16); its online-softmax state is a scalar, the same in
+// the four lanes of a column, and its accumulators hold dims 16m + 4*(lane/16) + i of that head.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D, bool Fp8>
+struct MStepRegs {
+  std::conditional_t<Fp8, uint2, uint4> k[D / kSlice];     // 8 elements per 32-dim slice
+  std::conditional_t<Fp8, uint32_t, uint2> v[D / kSub];    // 4 elements per 16-dim tile
+};
+
+template <int D>
+struct MState {
+  float m, nmc, thr, l;
+  f32x4_t acc[D / kSub];
+};
+
+template <bool Stream>
+__device__ __forceinline__ uint32_t load4(const uint8_t* ptr) {
+  if constexpr (Stream) return __builtin_nontemporal_load((const uint32_t*)ptr);
+  else return *(const uint32_t*)ptr;
+}
+template <bool Stream>
+__device__ __forceinline__ uint2 load8_u16(const uint16_t* ptr) {
+  return load8<Stream>(reinterpret_cast<const uint8_t*>(ptr));
+}
+
+template <int D, bool Stream, bool Fp8>
+__device__ __forceinline__ void load_mstep(MStepRegs<D, Fp8>& r, int i, const DecodeParams& p,
+                                           const int* bt, int& win, int& ids, size_t head_off,
+                                           size_t block_elems) {
+  const int lane = threadIdx.x & 63;
+  const int bs = p.block_size;
+  const int t0 = i * kSub;
+  const int b = t0 >> (bs == 32 ? 5 : 4);
+  if (b - win >= 64) {  // rare: refill the block-id window
+    win = b;
+    const int id = (win + lane < p.max_blocks_per_seq) ? bt[win + lane] : 0;
+    ids = min(max(id, 0), (int)(p.num_blocks - 1));
+  }
+  const int id = __builtin_amdgcn_readlane(ids, b - win);
+  const size_t off = (size_t)id * block_elems + head_off + (size_t)(t0 & (bs - 1)) * D;
+  const int r16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+  for (int sl = 0; sl < D / kSlice; ++sl)
+    r.k[sl] = load_elems<Stream, Fp8>(p.kpool, off + sl * (kSub * kSlice) + r16 * kSlice + 8 * q4);
+#pragma unroll
+  for (int m = 0; m < D / kSub; ++m) {
+    const size_t e = off + (size_t)(kSub * m + r16) * kSub + 4 * q4;
+    if constexpr (Fp8) r.v[m] = load4<Stream>(reinterpret_cast<const uint8_t*>(p.vpool) + e);
+    else r.v[m] = load8_u16<Stream>(p.vpool + e);
+  }
+}
+
+__device__ __forceinline__ uint4 k_operand(const uint4& k) { return k; }
+__device__ __forceinline__ uint4 k_operand(const uint2& k) { return widen8(k); }
+// V operand (4 elements) with tokens at or past nvalid zeroed, so 0 * NaN cannot reach acc.
+__device__ __forceinline__ uint2 v_operand(const uint2& v, int t, int nvalid, bool tail) {
+  if (!tail) return v;
+  const uint32_t k0 = (t + 1 < nvalid) ? 0xFFFFFFFFu : ((t < nvalid) ? 0xFFFFu : 0u);
+  const uint32_t k1 = (t + 3 < nvalid) ? 0xFFFFFFFFu : ((t + 2 < nvalid) ? 0xFFFFu : 0u);
+  return make_uint2(v.x & k0, v.y & k1);
+}
+__device__ __forceinline__ uint2 v_operand(uint32_t v, int t, int nvalid, bool tail) {
+  if (tail) {  // one code per token; code 0 is +0
+    const int n = min(max(nvalid - t, 0), 4);
+    v &= (n >= 4) ? 0xFFFFFFFFu : ((1u << (8 * n)) - 1u);
+  }
+  return make_uint2(fp8_pair_to_bf16<false>(v), fp8_pair_to_bf16<true>(v));
+}
+
+template <int D, bool Fp8>
+__device__ __forceinline__ void compute_mstep(const MStepRegs<D, Fp8>& r,
+                                              const uint4 (&qb)[D / kSlice], int nvalid, float c,
+                                              float slack_raw, MState<D>& st) {
+  const int lane = threadIdx.x & 63;
+  const int q4 = lane >> 4;
+  const bool tail = nvalid < kSub;  // wave-uniform
+  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sl = 0; sl < D / kSlice; ++sl)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k_operand(r.k[sl])),
+                                                 __builtin_bit_cast(bf16x8_t, qb[sl]), sc, 0, 0, 0);
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (!tail || 4 * q4 + i < nvalid) ? sc[i] : kNegInf;
+  const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (__ballot(mx > st.thr)) {
+    float cm = fmaxf(mx, xor16_f32(mx));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));  // the column's max over its 16 tokens
+    const float mn = fmaxf(st.m, cm);
+    if (mn != kNegInf && mn != st.m) {
+      const float alpha = fast_exp2((st.m - mn) * c);  // 0 when the old max is -inf
+      st.l *= alpha;
+#pragma unroll
+      for (int m = 0; m < D / kSub; ++m) st.acc[m] *= alpha;
+      st.m = mn;
+      st.nmc = -mn * c;
+      st.thr = mn + slack_raw;
+    }
+  }
+  float pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, st.nmc));
+  st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  const uint2 pb = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
+#pragma unroll
+  for (int m = 0; m < D / kSub; ++m)
+    st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        __builtin_bit_cast(s16x4_t, v_operand(r.v[m], 4 * q4, nvalid, tail)),
+        __builtin_bit_cast(s16x4_t, pb), st.acc[m], 0, 0, 0);
+}
+
+// decode_piece on the matrix cores (same contract and partial-slot format).
+template <int D, int G, int Depth, bool Stream, bool Fp8>
+__device__ __forceinline__ void decode_piece_mfma(const DecodeParams& p, int s, int h, int j0,
+                                                  int take, int n_s, long long w, long long x,
+                                                  long long jn, const Plan& plan,
+                                                  float* coop = nullptr) {
+  static_assert(G <= 16, "one matrix-core column per query head");
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int Hq = p.num_q_heads;
+  const int L = uniform(clamped_len(p, s));
+  const int u = s * p.num_kv_heads + h;
+  const bool whole = !coop && (j0 == 0) && (take == n_s);
+  if (!coop && j0 == 0 && lane == 0)
+    p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1, jn));
+
+  // B operand of the score product: head r16 (zero past G), dims 8*q4 .. +7 of each slice.
+  uint4 qb[D / kSlice];
+  {
+    const uint16_t* qg = p.query + ((size_t)s * Hq + (size_t)h * G + min(r16, G - 1)) * D + 8 * q4;
+#pragma unroll
+    for (int sl = 0; sl < D / kSlice; ++sl) {
+      const uint4 v = *(const uint4*)(qg + kSlice * sl);
+      qb[sl] = r16 < G ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  const int bs = p.block_size;
+  const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int tok_end = min(L, (j0 + take) * kSub);
+  int win = (j0 * kSub) / bs;
+  int ids;
+  {
+    const int id = (win + lane < p.max_blocks_per_seq) ? bt[win + lane] : 0;
+    ids = min(max(id, 0), (int)(p.num_blocks - 1));
+  }
+  const size_t tile = (size_t)bs * D;
+  const size_t block_elems = (size_t)p.num_kv_heads * tile;
+  const size_t head_off = (size_t)h * tile;
+
+  MState<D> st;
+  const float c = p.scale_log2;
+  const float slack_raw = kRescaleSlack / c;
+  st.m = kNegInf;
+  st.nmc = 0.f;
+  st.thr = kNegInf;
+  st.l = 0.f;
+#pragma unroll
+  for (int m = 0; m < D / kSub; ++m) st.acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Prefetch loads are issued unconditionally (past the last step they repeat its addresses).
+  const int iend = j0 + take;
+  const int ilast = iend - 1;
+  int i = j0;
+  if constexpr (Depth <= 1) {
+    MStepRegs<D, Fp8> ra, rb;
+    load_mstep<D, Stream, Fp8>(ra, i, p, bt, win, ids, head_off, block_elems);
+    while (true) {
+      load_mstep<D, Stream, Fp8>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_mstep<D, Fp8>(ra, qb, tok_end - i * kSub, c, slack_raw, st);
+      if (++i >= iend) break;
+      load_mstep<D, Stream, Fp8>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_mstep<D, Fp8>(rb, qb, tok_end - i * kSub, c, slack_raw, st);
+      if (++i >= iend) break;
+    }
+  } else {
+    MStepRegs<D, Fp8> r0, r1, r2;
+    load_mstep<D, Stream, Fp8>(r0, i, p, bt, win, ids, head_off, block_elems);
+    load_mstep<D, Stream, Fp8>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+    while (true) {
+      load_mstep<D, Stream, Fp8>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_mstep<D, Fp8>(r0, qb, tok_end - i * kSub, c, slack_raw, st);
+      if (++i >= iend) break;
+      load_mstep<D, Stream, Fp8>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_mstep<D, Fp8>(r1, qb, tok_end - i * kSub, c, slack_raw, st);
+      if (++i >= iend) break;
+      load_mstep<D, Stream, Fp8>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_mstep<D, Fp8>(r2, qb, tok_end - i * kSub, c, slack_raw, st);
+      if (++i >= iend) break;
+    }
+  }
+
+  // Finish: the column's sum over its four lanes; lane (r16, q4) holds dims 16m + 4*q4 + i.
+  float lt = st.l + xor16_f32(st.l);
+  lt += __shfl_xor(lt, 32, 64);
+  if (r16 >= G) return;
+  const int g = r16;
+  float* slot = coop ? coop : p.partials + slot_of(p, w, u) * (G * (2 + D));
+  uint16_t* orow = p.out + ((size_t)s * Hq + (size_t)h * G + g) * D;
+  if (whole) {
+#pragma unroll
+    for (int m = 0; m < D / kSub; ++m) {
+      const f32x4_t a = st.acc[m];
+      *(uint2*)(orow + kSub * m + 4 * q4) =
+          make_uint2(pack_bf16x2(a[0] * p.v_scale / lt, a[1] * p.v_scale / lt),
+                     pack_bf16x2(a[2] * p.v_scale / lt, a[3] * p.v_scale / lt));
+    }
+    return;
+  }
+  if (q4 == 0) {
+    slot[g] = st.m * c;  // the merge works in the log2 domain
+    slot[G + g] = lt;
+  }
+  // Scalar stores: a slot holds G*(2+D) floats, so it is only 4-byte aligned when G is odd.
+#pragma unroll
+  for (int m = 0; m < D / kSub; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) slot[2 * G + g * D + kSub * m + 4 * q4 + e] = st.acc[m][e];
 }
 
 // A piece taken by the whole workgroup: wave r runs steps [j0 + take*r/kWaves,
 // j0 + take*(r+1)/kWaves) into its LDS slot, then the workgroup combines the slots in wave order
 // and writes the output (unit wholly inside the piece) or the piece's partial slot.  Contains
 // barriers: every wave of the block must call it with the same arguments.
-template <int D, int G, int Depth, bool Stream>
+template <int D, int G, int Depth, bool Stream, bool Fp8, bool Mfma>
 __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, int j0, int take,
                                            int n_s, long long w, long long x, long long jn,
                                            const Plan& plan, uint16_t (*p_sh)[G][8],
@@ -472,9 +758,14 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
   const int wave = threadIdx.x >> 6;
   auto lo_of = [&](int r) { return j0 + (int)((long long)take * r / kWaves); };
   const int a = lo_of(wave), b = lo_of(wave + 1);
-  if (b > a)
-    decode_piece<D, G, Depth, Stream>(p, s, h, a, b - a, n_s, w, x + (a - j0), jn, plan, p_sh,
-                                      st[wave]);
+  if (b > a) {
+    if constexpr (Mfma)
+      decode_piece_mfma<D, G, Depth, Stream, Fp8>(p, s, h, a, b - a, n_s, w, x + (a - j0), jn,
+                                                  plan, st[wave]);
+    else
+      decode_piece<D, G, Depth, Stream, Fp8>(p, s, h, a, b - a, n_s, w, x + (a - j0), jn, plan,
+                                             p_sh, st[wave]);
+  }
   __syncthreads();
   const int u = s * p.num_kv_heads + h;
   const bool whole = (j0 == 0) && (take == n_s);
@@ -501,7 +792,7 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
       }
     }
     if (whole) {
-      orow[i] = to_bf16(acc / lt);
+      orow[i] = to_bf16(acc * p.v_scale / lt);
     } else {
       if (i % D == 0) {
         slot[g] = M;
@@ -518,7 +809,7 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
 // `quad` num_kv_heads / kWaves units of kWaves consecutive KV heads, wave r taking head
 // kWaves*unit + r (the workgroup is the worker); jn is that unit's index among the non-empty
 // units.  Coop: each piece is shared by the workgroup.
-template <int D, int G, int Depth, bool Stream, bool Coop = false>
+template <int D, int G, int Depth, bool Stream, bool Fp8, bool Mfma, bool Coop = false>
 __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& plan, long long v,
                                            int s, long long off, long long jn, long long x,
                                            long long x1, uint16_t (*p_sh)[G][8],
@@ -533,10 +824,13 @@ __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& pl
   while (true) {
     const int take = (int)min((long long)(n_s - j), x1 - x);
     if constexpr (Coop)
-      coop_piece<D, G, Depth, Stream>(p, s, h, j, take, n_s, v, x, jn, plan, p_sh, st);
+      coop_piece<D, G, Depth, Stream, Fp8, Mfma>(p, s, h, j, take, n_s, v, x, jn, plan, p_sh, st);
+    else if constexpr (Mfma)
+      decode_piece_mfma<D, G, Depth, Stream, Fp8>(
+          p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h, j, take, n_s, v, x, jn, plan);
     else
-      decode_piece<D, G, Depth, Stream>(p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h, j,
-                                        take, n_s, v, x, jn, plan, p_sh);
+      decode_piece<D, G, Depth, Stream, Fp8>(p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h,
+                                             j, take, n_s, v, x, jn, plan, p_sh);
     x += take;
     if (x >= x1) break;
     j = 0;
@@ -552,7 +846,8 @@ __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& pl
   }
 }
 
-template <int D, int G, int Depth>
+// Fp8: the pools hold E4M3 codes (always on the matrix cores).  Mfma: matrix-core steps.
+template <int D, int G, int Depth, bool Fp8, bool Mfma = Fp8>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -705,8 +1000,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     constexpr bool S = decltype(stream)::value;
     const int k = quad ? 0 : wave;
     if (w < plan.ns)
-      run_worker<D, G, Depth, S>(p, plan, w, sh_start_s[k], sh_start_off[k], sh_start_j[k],
-                                 sh_start_x[k], sh_start_x[k + 1], p_lds[wave], nullptr, quad);
+      run_worker<D, G, Depth, S, Fp8, Mfma>(p, plan, w, sh_start_s[k], sh_start_off[k], sh_start_j[k],
+                                      sh_start_x[k], sh_start_x[k + 1], p_lds[wave], nullptr,
+                                      quad);
     if (!dynamic) return;  // block-uniform
 
     // Dynamic chunks, each shared by the whole workgroup (one counter increment per chunk; the
@@ -728,7 +1024,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         if (seq_prefix[mid] <= xh) lo = mid;
         else hi = mid;
       }
-      run_worker<D, G, Depth, S, true>(p, plan, plan.ns + d, lo,
+      run_worker<D, G, Depth, S, Fp8, Mfma, true>(p, plan, plan.ns + d, lo,
                                        x0 - (long long)seq_prefix[lo] * Hkv, 0, x0,
                                        plan.start(plan.ns + d + 1), p_lds[wave], coop_st);
       __syncthreads();  // every thread has read sh_chunk
@@ -799,7 +1095,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int i = threadIdx.x + 256 * k;
-    if (i < G * D) orow[i] = to_bf16(a[k] / lt[k]);
+    if (i < G * D) orow[i] = to_bf16(a[k] * p.v_scale / lt[k]);
   }
 }
 
@@ -810,12 +1106,25 @@ int prefetch_depth() {
   return (v == 0 || v == 2) ? v : 1;
 }
 
+// Prefetch depth of the FP8 decode kernel: PA_DECODE_PREFETCH_FP8=1 or 2 (default 1).
+int prefetch_depth_fp8() {
+  const char* e = std::getenv("PA_DECODE_PREFETCH_FP8");
+  const int v = e ? std::atoi(e) : 1;
+  return v == 2 ? 2 : 1;
+}
+
+// bf16 pools on the matrix-core step: PA_DECODE_MFMA=1 (default 0, the vector step).
+bool bf16_on_matrix_cores() {
+  const char* e = std::getenv("PA_DECODE_MFMA");
+  return e && std::atoi(e) == 1;
+}
+
 template <int D, int G>
 const void* kernel_ptr() {
   switch (prefetch_depth()) {
-    case 0: return reinterpret_cast<const void*>(&decode_kernel<D, G, 0>);
-    case 1: return reinterpret_cast<const void*>(&decode_kernel<D, G, 1>);
-    default: return reinterpret_cast<const void*>(&decode_kernel<D, G, 2>);
+    case 0: return reinterpret_cast<const void*>(&decode_kernel<D, G, 0, false>);
+    case 1: return reinterpret_cast<const void*>(&decode_kernel<D, G, 1, false>);
+    default: return reinterpret_cast<const void*>(&decode_kernel<D, G, 2, false>);
   }
 }
 
@@ -825,10 +1134,26 @@ hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
     TraceScope t("decode_partition", stream);
     const dim3 grid(p.num_workers / kWaves), block(kThreads);
     const size_t lds = p.dyn_cap > 0 ? (size_t)(p.num_seqs + 1) * 4 : 0;
-    switch (prefetch_depth()) {
-      case 0: hipLaunchKernelGGL((decode_kernel<D, G, 0>), grid, block, lds, stream, p); break;
-      case 1: hipLaunchKernelGGL((decode_kernel<D, G, 1>), grid, block, lds, stream, p); break;
-      default: hipLaunchKernelGGL((decode_kernel<D, G, 2>), grid, block, lds, stream, p); break;
+    if (p.kv_fp8) {
+      // FP8 steps carry half the bytes: prefetch depth 1 or 2.
+      if (prefetch_depth_fp8() == 2)
+        hipLaunchKernelGGL((decode_kernel<D, G, 2, true>), grid, block, lds, stream, p);
+      else
+        hipLaunchKernelGGL((decode_kernel<D, G, 1, true>), grid, block, lds, stream, p);
+    } else if (bf16_on_matrix_cores()) {
+      hipLaunchKernelGGL((decode_kernel<D, G, 1, false, true>), grid, block, lds, stream, p);
+    } else {
+      switch (prefetch_depth()) {
+        case 0:
+          hipLaunchKernelGGL((decode_kernel<D, G, 0, false>), grid, block, lds, stream, p);
+          break;
+        case 1:
+          hipLaunchKernelGGL((decode_kernel<D, G, 1, false>), grid, block, lds, stream, p);
+          break;
+        default:
+          hipLaunchKernelGGL((decode_kernel<D, G, 2, false>), grid, block, lds, stream, p);
+          break;
+      }
     }
   }
   hipError_t e = hipGetLastError();

@@ -162,10 +162,19 @@ pa_status_t pa_trace_read(const char* kernel_name, int32_t* launches, double* to
   return ok();
 }
 
-pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_token_stride,
-                                 void* key_cache, void* value_cache, const int64_t* slot_mapping,
-                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t block_size, int64_t num_blocks, void* stream) {
+}  // extern "C"
+
+namespace {
+
+bool valid_kv_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+pa_status_t reshape_impl(const void* key, const void* value, int64_t kv_token_stride,
+                         void* key_cache, void* value_cache, const int64_t* slot_mapping,
+                         int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, bool fp8, float k_scale,
+                         float v_scale, void* stream) {
+  if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
+    return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
   if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d <= 0", num_kv_heads);
   if (!supported_head_dim(head_dim))
@@ -183,6 +192,9 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_
       !aligned(value_cache, 16) || !aligned(slot_mapping, 8))
     return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for bf16 arrays)");
   pa::ReshapeParams p{};
+  p.kv_fp8 = fp8;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   p.key = static_cast<const uint16_t*>(key);
   p.value = static_cast<const uint16_t*>(value);
   p.token_stride = kv_token_stride;
@@ -195,6 +207,30 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_
   p.block_size = block_size;
   p.num_blocks = num_blocks;
   return hip_status(pa::launch_reshape(p, static_cast<hipStream_t>(stream)), "reshape_and_cache");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, int64_t kv_token_stride,
+                                 void* key_cache, void* value_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, void* stream) {
+  return reshape_impl(key, value, kv_token_stride, key_cache, value_cache, slot_mapping,
+                      num_tokens, num_kv_heads, head_dim, block_size, num_blocks, false, 1.f, 1.f,
+                      stream);
+}
+
+pa_status_t pa_reshape_and_cache_fp8(const void* key, const void* value, int64_t kv_token_stride,
+                                     void* key_cache, void* value_cache,
+                                     const int64_t* slot_mapping, int32_t num_tokens,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int64_t num_blocks, float k_scale, float v_scale,
+                                     void* stream) {
+  return reshape_impl(key, value, kv_token_stride, key_cache, value_cache, slot_mapping,
+                      num_tokens, num_kv_heads, head_dim, block_size, num_blocks, true, k_scale,
+                      v_scale, stream);
 }
 
 pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, int64_t num_blocks,
@@ -243,12 +279,21 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 }
 }  // namespace
 
-pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
-                      const void* value_cache, int64_t num_blocks, const int32_t* block_tables,
-                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                      int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
+                        const void* value_cache, int64_t num_blocks, const int32_t* block_tables,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                        bool fp8, float k_scale, float v_scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
+    return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if (fp8 && !std::isfinite(scale * k_scale))
+    return fail(PA_ERR_INVALID_ARG, "scale * k_scale overflows");
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
   pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
                                          max_blocks_per_seq, max_seq_len, scale);
@@ -294,12 +339,44 @@ pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
            env_int("PA_DECODE_QUAD", 1, 0, 1);
   p.piece_cost = env_int("PA_DECODE_PIECE_COST", 6, 0, 64);
   p.len_cap = max_seq_len;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  // FP8: the K scale joins the softmax scale and the V scale multiplies the outputs.
+  p.scale_log2 = (fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
+  p.kv_fp8 = fp8;
+  p.v_scale = fp8 ? v_scale : 1.f;
   char* base = static_cast<char*>(workspace);
   p.counter = reinterpret_cast<unsigned*>(base + wl.counter_off);
   p.unit_info = reinterpret_cast<int2*>(base + wl.info_off);
   p.partials = reinterpret_cast<float*>(base + wl.partials_off);
   return hip_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)), "decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode(void* out, const void* query, const void* key_cache,
+                      const void* value_cache, int64_t num_blocks, const int32_t* block_tables,
+                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, max_seq_len, scale, false, 1.f, 1.f, workspace,
+                     workspace_bytes, stream);
+}
+
+pa_status_t pa_decode_fp8(void* out, const void* query, const void* key_cache,
+                          const void* value_cache, int64_t num_blocks,
+                          const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                          float scale, float k_scale, float v_scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, max_seq_len, scale, true, k_scale, v_scale, workspace,
+                     workspace_bytes, stream);
 }
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,

@@ -38,7 +38,11 @@ struct DecodeParams {
   // Lengths are clamped to this (min of max_seq_len and the table width) so a length beyond the
   // caller's bound cannot take a kernel outside the table.
   int len_cap;
-  float scale_log2;  // softmax scale times log2(e)
+  float scale_log2;  // softmax scale times log2(e) (times the K scale for an FP8 cache)
+  // Nonzero: the pools hold FP8 E4M3 codes (one byte per element, same element order) and
+  // every output is multiplied by v_scale; for bf16 pools v_scale is 1.
+  int kv_fp8;
+  float v_scale;
 };
 
 // Waves the decode kernel is launched with for this shape on the current device.
@@ -60,6 +64,9 @@ struct ReshapeParams {
   const int64_t* slots;
   int num_tokens, num_kv_heads, head_dim, block_size;
   int64_t num_blocks;
+  // FP8 pools: write E4M3 codes of value / scale (kpool and vpool then point at bytes).
+  int kv_fp8;
+  float k_scale, v_scale;
 };
 
 hipError_t launch_reshape(const ReshapeParams& p, hipStream_t stream);

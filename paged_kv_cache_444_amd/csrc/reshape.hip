@@ -8,6 +8,11 @@
 // layout those 8 values are contiguous (they sit inside one 32-wide slice), so K is written with
 // one 16-byte store; in the V layout consecutive head-dim values are 16 tokens apart, so V is
 // written as eight 2-byte stores.
+//
+// FP8 pools keep the same element order with one byte per element: each value is divided by its
+// pool's scale (correctly rounded fp32 quotient) and encoded as an OCP E4M3 code, rounding to the
+// nearest value with ties to even and saturating at +-448.  K then takes one 8-byte store, V
+// eight 1-byte stores.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -50,6 +55,70 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeParams p)
   }
 }
 
+// E4M3 code of y, from the format's fields: sign, 4-bit exponent with bias 7, 3-bit mantissa.
+// Magnitudes below 2^-6 are subnormal multiples of 2^-9; larger ones keep the fp32 exponent and
+// the top 3 mantissa bits rounded to nearest even (a carry moves into the exponent).  Finite
+// magnitudes above 448 saturate to 448 (code 0x7E); NaN gives 0x7F.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, y) >> 24) & 0x80u;
+  float a = __builtin_fabsf(y);
+  if (!(a == a)) return sign | 0x7Fu;
+  a = __builtin_fminf(a, 448.f);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = (uint32_t)__builtin_rintf(a * 512.f);  // exact scaling; rint rounds ties to even
+  } else {
+    const uint32_t u = __builtin_bit_cast(uint32_t, a);
+    code = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sign | code;
+}
+
+// Codes of 8 bf16 values (packed in a uint4) divided by `scale`, packed little-endian in a uint2.
+__device__ __forceinline__ uint2 quantize8(const uint4& v, float scale) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t c[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    c[2 * e] = e4m3_code(__fdiv_rn(__builtin_bit_cast(float, w[e] << 16), scale));
+    c[2 * e + 1] = e4m3_code(__fdiv_rn(__builtin_bit_cast(float, w[e] & 0xFFFF0000u), scale));
+  }
+  return make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                    c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+}
+
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeParams p) {
+  const int D = p.head_dim;
+  const int chunks = D / 8;
+  const int64_t per_token = (int64_t)p.num_kv_heads * chunks;
+  const int64_t total = per_token * p.num_tokens;
+  const int64_t pool_slots = p.num_blocks * p.block_size;
+  uint8_t* kpool = reinterpret_cast<uint8_t*>(p.kpool);
+  uint8_t* vpool = reinterpret_cast<uint8_t*>(p.vpool);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(i / per_token);
+    const int rem = (int)(i % per_token);
+    const int h = rem / chunks;
+    const int c = rem % chunks;
+    const int64_t slot = p.slots[t];
+    if (slot < 0 || slot >= pool_slots) continue;
+    const int64_t blk = slot / p.block_size;
+    const int off = (int)(slot % p.block_size);
+    const int sb = off / kSub, tt = off % kSub;
+    const int64_t src = (int64_t)t * p.token_stride + (int64_t)h * D + 8 * c;
+    const uint2 kc = quantize8(*(const uint4*)(p.key + src), p.k_scale);
+    const uint2 vc = quantize8(*(const uint4*)(p.value + src), p.v_scale);
+    const int64_t tile = ((blk * p.num_kv_heads + h) * p.block_size + (int64_t)sb * kSub) * D;
+    const int d0 = 8 * c;
+    *(uint2*)(kpool + tile + (d0 / kSlice) * (kSub * kSlice) + tt * kSlice + d0 % kSlice) = kc;
+    uint8_t* vdst = vpool + tile + (int64_t)d0 * kSub + tt;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vdst[e * kSub] = (uint8_t)(((e < 4 ? vc.x : vc.y) >> (8 * (e & 3))) & 0xFFu);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_reshape(const ReshapeParams& p, hipStream_t stream) {
@@ -58,7 +127,10 @@ hipError_t launch_reshape(const ReshapeParams& p, hipStream_t stream) {
   const int64_t blocks = (total + 255) / 256;
   const int grid = (int)(blocks < 65536 ? blocks : 65536);
   TraceScope t("reshape_and_cache", stream);
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(256), 0, stream, p);
+  if (p.kv_fp8)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel, dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

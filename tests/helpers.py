@@ -70,3 +70,33 @@ def cached_named_case(cfg_id: int) -> Case:
 @functools.lru_cache(maxsize=2)
 def cached_oracle_pools(cfg_id: int):
     return oracle_pools_after_reshape(cached_named_case(cfg_id))
+
+
+def oracle_quantize_pool(pool_u16: np.ndarray, scale: float) -> np.ndarray:
+    """E4M3 codes of a whole bf16 pool by the oracle's quantiser, in chunks on several threads
+    (the result is the same as one call over the whole array)."""
+    import concurrent.futures
+    import os
+
+    from oracle import fp8
+
+    flat = np.ascontiguousarray(pool_u16).reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 23
+    starts = list(range(0, flat.size, step))
+
+    def work(a):
+        out[a:a + step] = fp8.quantize(flat[a:a + step], scale)
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(work, starts))
+    return out.reshape(pool_u16.shape)
+
+
+def dev_u8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def host_u8(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()

@@ -69,4 +69,11 @@ def test_host_side_validation(lib):
     assert lib.pa_copy_blocks(z, z, 10, z, 1, 2, 96, 16, z) == 3                   # head_dim
     assert lib.pa_copy_blocks(z, z, 0, z, 1, 2, 128, 16, z) == 2                   # no blocks
     assert lib.pa_copy_blocks(z, z, 10, z, 0, 2, 128, 16, z) == 0                  # no pairs
+    # FP8 entry points: scales must be finite and positive
+    assert lib.pa_decode_fp8(z, z, z, z, 10, z, z, 1, 8, 2, 128, 16, 4, 64, 0.1, 0.0, 1.0, z, 0, z) == 2
+    assert lib.pa_decode_fp8(z, z, z, z, 10, z, z, 1, 8, 2, 128, 16, 4, 64, 0.1, 1.0, float("nan"),
+                             z, 0, z) == 2
+    assert lib.pa_decode_fp8(z, z, z, z, 10, z, z, 1, 8, 2, 96, 16, 4, 64, 0.1, 1.0, 1.0, z, 0, z) == 3
+    assert lib.pa_reshape_and_cache_fp8(z, z, 256, z, z, z, 1, 2, 128, 16, 10, -1.0, 1.0, z) == 2
+    assert lib.pa_reshape_and_cache_fp8(z, z, 256, z, z, z, 0, 2, 128, 16, 10, 1.0, 1.0, z) == 0
     assert lib.pa_trace_read(b"decode_partition", None, None) == 1

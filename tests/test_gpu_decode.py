@@ -362,3 +362,25 @@ def test_abi_rejects_bad_arguments_without_touching_buffers():
     assert torch.equal(out.view(torch.int16), before.view(torch.int16))
     lib = pa.load_library()
     assert lib.pa_decode(0, 0, 0, 0, 1000, 0, 0, 1, 8, 2, 128, 16, 4, 64, 0.1, 0, 0, 0) == 1
+
+
+# ------------------------------------------------------------------------- matrix-core step
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_decode_matrix_core_step_parity_named(cfg, monkeypatch):
+    """The bf16 decode on the matrix-core step (the one FP8 pools always use) against the oracle."""
+    monkeypatch.setenv("PA_DECODE_MFMA", "1")
+    case = cached_named_case(cfg)
+    d = case.decode
+    say(f"decode (matrix-core step) cfg{cfg}: {case.name}, B={d.num_seqs}, max L={d.max_seq_len}")
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    if case.reshape is not None:
+        gpu_reshape(case, kc, vc)
+    got = gpu_decode(case, kc, vc)
+    assert np.array_equal(got, gpu_decode(case, kc, vc)), "not reproducible"
+    seqs = None if d.num_seqs <= 8 else sorted(
+        {0, d.num_seqs - 1} | set(np.random.default_rng(73).choice(d.num_seqs, 14, replace=False).tolist()))
+    okc, ovc = cached_oracle_pools(cfg)
+    ref = oracle_decode(case, okc, ovc, seqs=seqs)
+    rows = list(range(d.num_seqs)) if seqs is None else seqs
+    assert_close(upcast(got)[rows], ref[rows], f"decode (matrix-core step) cfg{cfg}")

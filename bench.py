@@ -354,6 +354,7 @@ def run_fp8_decode(args, case, pools, q, bt, sl, out, ws, bf16_ms, bf16_kernel_m
         "speedup_vs_bf16_call": round(bf16_ms / ms, 3),
         "roofline": {"bound": "hbm", "kernel": "decode_kernel (fp8)", "achieved": round(kgbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_kernel_fp8"),
                      "launch_us": round(kms * 1e3, 2),
                      "merge_launch_us": round(ms_merge / max(n_merge, 1) * 1e3, 2),
                      "speedup_vs_bf16_kernel": round(bf16_kernel_ms / kms, 3)},

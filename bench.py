@@ -104,7 +104,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over the whole batch until this much CPU time is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["decode", "copy", "mixed", "cow"], default="decode")
+    ap.add_argument("--mode", choices=["decode", "copy", "mixed", "cow", "prefix"], default="decode")
     ap.add_argument("--mixed-steps", type=int, default=30)
     ap.add_argument("--mixed-warmup", type=int, default=60)
     ap.add_argument("--mixed-order", choices=["decode-first", "prefill-first"], default="decode-first",
@@ -112,6 +112,8 @@ def parse():
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-step measurement")
     ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write step measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache decode measurement")
+    ap.add_argument("--no-prefix", action="store_true",
+                    help="skip the prefix-shared (plain vs cascade decode) measurement")
     ap.add_argument("--cow-steps", type=int, default=50)
     ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
@@ -158,6 +160,9 @@ def main():
         return
     if args.mode == "cow":
         print(json.dumps(run_cow(args)), flush=True)
+        return
+    if args.mode == "prefix":
+        print(json.dumps(run_prefix_shared(args)), flush=True)
         return
 
     import paged_kv_cache_444_amd as pa
@@ -243,6 +248,9 @@ def main():
     cow = None
     if not args.no_cow:
         cow = run_cow(args)
+    prefix = None
+    if not args.no_prefix:
+        prefix = run_prefix_shared(args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -286,6 +294,7 @@ def main():
         "fp8_decode": fp8,
         "mixed_step": mixed,
         "cow_step": cow,
+        "prefix_shared": prefix,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -565,6 +574,86 @@ def run_cow(args):
         "copy_blocks_random_pairs": sweep,
         "decode_logical_gbs": round(decode_bytes(d.seq_lens, Hq, Hkv, D, bs)
                                     / (per["decode_partition"] * 1e-6) / 1e9, 1),
+    }
+
+
+def run_prefix_shared(args):
+    """Prefix-shared rollouts at the 70B shape (8 prompts x 16 candidates sharing a 4,096-token
+    prompt's blocks, private tails of 0..1,024 tokens, one new token each): plain decode against
+    the cascade decode that reads each shared prompt once per group.  Rates are given on the
+    logical bytes (every sequence's K/V) and on the unique bytes (each physical block once)."""
+    import torch
+
+    import paged_kv_cache_444_amd as pa
+    from workloads import named_case
+
+    log("generating the prefix-shared rollout workload")
+    case = named_case(5)
+    Hq, Hkv, D, bs = case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+    d, r = case.decode, case.reshape
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    kc, vc = dev(case.key_cache), dev(case.value_cache)
+    pa.reshape_and_cache(dev(r.key), dev(r.value), kc, vc, torch.from_numpy(r.slot_mapping).cuda(),
+                         num_kv_heads=Hkv, head_dim=D, block_size=bs)
+    q, bt, sl = dev(d.query), torch.from_numpy(d.block_tables).cuda(), torch.from_numpy(d.seq_lens).cuda()
+    gs = torch.arange(0, d.num_seqs + 1, 16, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(pa.decode_workspace_bytes(d.num_seqs, Hq, Hkv, D, d.max_seq_len), 1),
+                     dtype=torch.uint8, device="cuda")
+    cws = torch.zeros(max(pa.decode_cascade_workspace_bytes(d.num_seqs, 8, 16, Hq, Hkv, D, 4096), 1),
+                      dtype=torch.uint8, device="cuda")
+    kw = dict(num_kv_heads=Hkv, block_size=bs, scale=float(case.scale), max_seq_len=d.max_seq_len,
+              out=out)
+
+    def plain():
+        pa.decode(q, kc, vc, bt, sl, workspace=ws, **kw)
+
+    def cascade():
+        pa.decode_cascade(q, kc, vc, bt, sl, gs, prefix_len=4096, max_group_size=16, workspace=cws,
+                          **kw)
+
+    def timed(fn):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.cow_steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / args.cow_steps
+
+    us_plain, us_cascade = timed(plain), timed(cascade)
+    us_plain2, us_cascade2 = timed(plain), timed(cascade)
+    names = ("prefill_chunk", "decode_partition", "decode_merge", "prefill_merge")
+    pa.trace_enable(True)
+    for n in names:
+        pa.trace_read(n)
+    for _ in range(args.cow_steps):
+        cascade()
+    torch.cuda.synchronize()
+    per = {}
+    for n in names:
+        k, ms = pa.trace_read(n)
+        per[n] = round(ms / k * 1e3, 2) if k else None
+    pa.trace_enable(False)
+    logical = decode_bytes(d.seq_lens, Hq, Hkv, D, bs)
+    used = np.unique(np.concatenate([d.block_tables[i, :(int(L) + bs - 1) // bs]
+                                     for i, L in enumerate(d.seq_lens)]))
+    unique = int(used.size) * Hkv * bs * D * 2 * 2 + d.num_seqs * 2 * Hq * D * 2
+    best_p, best_c = min(us_plain, us_plain2), min(us_cascade, us_cascade2)
+    log(f"prefix-shared: plain decode {best_p:.1f} us, cascade {best_c:.1f} us")
+    return {
+        "workload": case.name, "logical_bytes": logical, "unique_bytes": unique,
+        "plain_us": [round(us_plain, 2), round(us_plain2, 2)],
+        "cascade_us": [round(us_cascade, 2), round(us_cascade2, 2)],
+        "cascade_speedup": round(best_p / best_c, 3),
+        "cascade_kernel_us": per,
+        "cascade_unique_gbs": round(unique / (best_c * 1e-6) / 1e9, 1),
+        "cascade_logical_gbs": round(logical / (best_c * 1e-6) / 1e9, 1),
+        "plain_logical_gbs": round(logical / (best_p * 1e-6) / 1e9, 1),
     }
 
 

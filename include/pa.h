@@ -191,6 +191,43 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const void* key_cache,
                           size_t workspace_bytes, void* stream);
 
 /*
+ * Cascade decode for sequences that share a prompt (copy-on-write rollouts).
+ *
+ * Source: sequences continuing one prompt reference the same physical blocks for it ("Inference
+ * optimization" lesson, section "Paged attention"; vLLM-on-H100 article, PagedAttention section:
+ * 8 or 16 rollouts of one prompt share its pages).  The result is exactly pa_decode's; only the
+ * order of the work changes: the shared prompt's keys are read once per group, as one matrix-core
+ * chunk of all the group's query rows (the chunked-prefill kernel, non-causal), each sequence's
+ * own later tokens are attended by the decode kernel, and the two softmax states of every row are
+ * combined.
+ *
+ *   group_start    int32 [num_groups+1]: group i is sequences group_start[i] .. group_start[i+1]-1,
+ *                  group_start[0] == 0, group_start[num_groups] == num_seqs, non-decreasing;
+ *                  a sequence that shares nothing can be a group of one
+ *   max_group_size host-side bound of every group's size (1 <= max_group_size <= num_seqs)
+ *   prefix_len     tokens shared within every group: a positive multiple of block_size,
+ *                  <= max_seq_len; every member's first prefix_len / block_size table entries
+ *                  must be those of its group's first member, and every seq_lens entry must be
+ *                  >= prefix_len (otherwise results are unspecified)
+ *   workspace      at least pa_decode_cascade_workspace_bytes(...) bytes, 256-byte aligned,
+ *                  zero-filled before its first use and reusable by later calls on one stream
+ * Other arguments, limits and errors as pa_decode (bf16 pools).  Outputs are fp32-accumulated and
+ * rounded to bf16 once.
+ */
+size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_groups,
+                                         int32_t max_group_size, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t prefix_len);
+pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, int64_t num_blocks,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* group_start, int32_t num_seqs, int32_t num_groups,
+                              int32_t max_group_size, int32_t prefix_len, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of workspace pa_prefill_chunk needs for this batch shape on the current device; 0 means
  * none (workspace may then be NULL).  Long contexts are split into key ranges whose partial softmax
  * states are combined afterwards; the workspace holds those states.  It needs no initialisation.

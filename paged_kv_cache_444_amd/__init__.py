@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "load_library", "reshape_and_cache", "reshape_and_cache_fp8", "copy_blocks", "decode",
-    "decode_fp8", "prefill_chunk",
+    "decode_fp8", "decode_cascade", "decode_cascade_workspace_bytes", "prefill_chunk",
     "mixed_step", "decode_workspace_bytes", "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
     "LIB_PATH",
 ]
@@ -49,6 +49,9 @@ _SIGNATURES = {
                                         ctypes.c_float, ctypes.c_float, _P]),
     "pa_decode_fp8": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                              ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _SZ, _P]),
+    "pa_decode_cascade_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_decode_cascade": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                 _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _SZ, _P]),
     "pa_copy_blocks": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _P]),
     "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pa_decode": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -243,6 +246,46 @@ def decode_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.
                              _ints(seq_lens, torch.int32, "seq_lens"), B, Hq, num_kv_heads, D,
                              block_size, block_tables.shape[1], max_seq_len, float(scale),
                              float(k_scale), float(v_scale), ws, ws_bytes, _stream()))
+    return out
+
+
+def decode_cascade_workspace_bytes(num_seqs: int, num_groups: int, max_group_size: int,
+                                   num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                   prefix_len: int) -> int:
+    """Workspace bytes pa_decode_cascade needs on the current device (0 for unsupported shapes)."""
+    return int(load_library().pa_decode_cascade_workspace_bytes(
+        num_seqs, num_groups, max_group_size, num_q_heads, num_kv_heads, head_dim, prefix_len))
+
+
+def decode_cascade(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                   block_tables: torch.Tensor, seq_lens: torch.Tensor, group_start: torch.Tensor, *,
+                   prefix_len: int, max_group_size: int, num_kv_heads: int, block_size: int,
+                   scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+                   out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode of groups of sequences sharing their first `prefix_len` tokens' blocks (group i is
+    sequences group_start[i] .. group_start[i+1]-1): the same result as `decode`."""
+    lib = load_library()
+    B, Hq, D = query.shape
+    n_groups = group_start.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty_like(query)
+    nbytes = decode_cascade_workspace_bytes(B, n_groups, max_group_size, Hq, num_kv_heads, D,
+                                            prefix_len)
+    ws, ws_bytes = _workspace(nbytes, workspace, query.device)
+    n = _num_blocks(key_cache, num_kv_heads, block_size, D)
+    _check(lib.pa_decode_cascade(_bf16(out, "out"), _bf16(query, "query"), _bf16(key_cache, "key_cache"),
+                                 _bf16(value_cache, "value_cache"), n,
+                                 _ints(block_tables, torch.int32, "block_tables"),
+                                 _ints(seq_lens, torch.int32, "seq_lens"),
+                                 _ints(group_start, torch.int32, "group_start"), B, n_groups,
+                                 max_group_size, prefix_len, Hq, num_kv_heads, D, block_size,
+                                 block_tables.shape[1], max_seq_len, float(scale), ws, ws_bytes,
+                                 _stream()))
     return out
 
 

@@ -69,8 +69,14 @@ constexpr int kPrefixLdsBytes = (kMaxPrefixSeqs + 1) * 4;
 constexpr int kDynSlotsPerWorker = 2;
 constexpr int kBlocksPerCU = 1;
 
+// Tokens of sequence s this call attends: its length, clamped, less the skipped prefix.
 __device__ __forceinline__ int clamped_len(const DecodeParams& p, int s) {
-  return min(max(p.seq_lens[s], 0), p.len_cap);
+  return max(min(max(p.seq_lens[s], 0), p.len_cap) - p.kv_skip, 0);
+}
+
+// Slot of (sequence, query head) row `row` in the prefill-layout state workspace.
+__device__ __forceinline__ size_t state_slot(const DecodeParams& p, size_t row) {
+  return row * p.state_stride + p.state_split;
 }
 
 __device__ __forceinline__ int steps_of(const DecodeParams& p, int s) {
@@ -225,7 +231,7 @@ __device__ __forceinline__ void load_step(StepRegs<D, Fp8>& r, int i, const Deco
   const int b = t0 >> (bs == 32 ? 5 : 4);
   if (b - win >= 64) {  // rare: refill the block-id window
     win = b;
-    const int id = (win + lane < p.max_blocks_per_seq) ? bt[win + lane] : 0;
+    const int id = (win + lane < p.table_cols) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const int id = __builtin_amdgcn_readlane(ids, b - win);
@@ -407,7 +413,7 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   {
     // Read without waiting for the length: entries past the sequence's blocks are padding, and
     // the steps below only ever use the sequence's own blocks.
-    const int id = (win + lane < p.max_blocks_per_seq) ? bt[win + lane] : 0;
+    const int id = (win + lane < p.table_cols) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const size_t tile = (size_t)bs * D;
@@ -495,6 +501,11 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
       slot[g] = st.m[g] * c;  // the merge works in the log2 domain
       slot[G + g] = lt;
     }
+    if (whole && p.state_ml && lane == 0) {
+      const size_t u = state_slot(p, (size_t)s * Hq + (size_t)h * G + g);
+      p.state_ml[2 * u] = st.m[g] * c;
+      p.state_ml[2 * u + 1] = lt;
+    }
     // Half 0 finishes rows vd + 32k for k < R/2, half 1 the rest; each sends the other half's.
 #pragma unroll
     for (int k = 0; k < R / 2; ++k) {
@@ -502,7 +513,9 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
       const float send = vo ? st.acc[g][k] : st.acc[g][k + R / 2];
       const float a = mine + __shfl_xor(send, 32, 64);
       const int d = vd + 32 * (k + (vo ? R / 2 : 0));
-      if (whole) orow[g * D + d] = to_bf16(a * p.v_scale / lt);
+      if (whole && p.state_ml)
+        p.state_acc[state_slot(p, (size_t)s * Hq + (size_t)h * G + g) * D + d] = a * p.v_scale;
+      else if (whole) orow[g * D + d] = to_bf16(a * p.v_scale / lt);
       else slot[2 * G + g * D + d] = a;
     }
   }
@@ -559,7 +572,7 @@ __device__ __forceinline__ void load_mstep(MStepRegs<D, Fp8>& r, int i, const De
   const int b = t0 >> (bs == 32 ? 5 : 4);
   if (b - win >= 64) {  // rare: refill the block-id window
     win = b;
-    const int id = (win + lane < p.max_blocks_per_seq) ? bt[win + lane] : 0;
+    const int id = (win + lane < p.table_cols) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const int id = __builtin_amdgcn_readlane(ids, b - win);
@@ -668,7 +681,7 @@ __device__ __forceinline__ void decode_piece_mfma(const DecodeParams& p, int s, 
   int win = (j0 * kSub) / bs;
   int ids;
   {
-    const int id = (win + lane < p.max_blocks_per_seq) ? bt[win + lane] : 0;
+    const int id = (win + lane < p.table_cols) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const size_t tile = (size_t)bs * D;
@@ -724,6 +737,18 @@ __device__ __forceinline__ void decode_piece_mfma(const DecodeParams& p, int s, 
   const int g = r16;
   float* slot = coop ? coop : p.partials + slot_of(p, w, u) * (G * (2 + D));
   uint16_t* orow = p.out + ((size_t)s * Hq + (size_t)h * G + g) * D;
+  if (whole && p.state_ml) {
+    const size_t u = state_slot(p, (size_t)s * Hq + (size_t)h * G + g);
+    if (q4 == 0) {
+      p.state_ml[2 * u] = st.m * c;
+      p.state_ml[2 * u + 1] = lt;
+    }
+#pragma unroll
+    for (int m = 0; m < D / kSub; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p.state_acc[u * D + kSub * m + 4 * q4 + e] = st.acc[m][e] * p.v_scale;
+    return;
+  }
   if (whole) {
 #pragma unroll
     for (int m = 0; m < D / kSub; ++m) {
@@ -791,7 +816,14 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
         acc += e * st[r][2 * G + i];
       }
     }
-    if (whole) {
+    if (whole && p.state_ml) {
+      const size_t su = state_slot(p, (size_t)s * p.num_q_heads + (size_t)h * G + g);
+      if (i % D == 0) {
+        p.state_ml[2 * su] = M;
+        p.state_ml[2 * su + 1] = lt;
+      }
+      p.state_acc[su * D + i % D] = acc * p.v_scale;
+    } else if (whole) {
       orow[i] = to_bf16(acc * p.v_scale / lt);
     } else {
       if (i % D == 0) {
@@ -885,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // batch re-reads blocks, so its K/V loads stay ordinary; any other batch streams them.
   int shares = 0;
   const size_t row = (size_t)p.max_blocks_per_seq;
-  for (int s = threadIdx.x; s + 1 < B; s += kThreads)
+  for (int s = threadIdx.x; s + 1 < B && p.table_cols > 0; s += kThreads)
     shares |= p.block_tables[(size_t)s * row] == p.block_tables[(size_t)(s + 1) * row];
   shares = __any(shares);
 #pragma unroll
@@ -1047,7 +1079,19 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int h = u % p.num_kv_heads;
   if (u == 0 && threadIdx.x == 0) *p.counter = 0u;  // ready for the next call
   uint16_t* orow = p.out + ((size_t)s * p.num_q_heads + (size_t)h * G) * D;
+  const size_t row0 = (size_t)s * p.num_q_heads + (size_t)h * G;
   if (clamped_len(p, s) == 0) {
+    if (p.state_ml) {  // no keys here: an empty state
+      for (int i = threadIdx.x; i < G * D; i += 256) {
+        const size_t su = state_slot(p, row0 + i / D);
+        if (i % D == 0) {
+          p.state_ml[2 * su] = kNegInf;
+          p.state_ml[2 * su + 1] = 0.f;
+        }
+        p.state_acc[su * D + i % D] = 0.f;
+      }
+      return;
+    }
     for (int i = threadIdx.x; i < G * D; i += 256) orow[i] = 0;
     return;
   }
@@ -1095,7 +1139,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int i = threadIdx.x + 256 * k;
-    if (i < G * D) orow[i] = to_bf16(a[k] * p.v_scale / lt[k]);
+    if (i >= G * D) continue;
+    if (p.state_ml) {
+      const size_t su = state_slot(p, row0 + i / D);
+      if (i % D == 0) {
+        p.state_ml[2 * su] = M[k];
+        p.state_ml[2 * su + 1] = lt[k];
+      }
+      p.state_acc[su * D + i % D] = a[k] * p.v_scale;
+    } else {
+      orow[i] = to_bf16(a[k] * p.v_scale / lt[k]);
+    }
   }
 }
 

@@ -289,7 +289,9 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                         int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
                         bool fp8, float k_scale, float v_scale, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, int kv_skip = 0,
+                        float* state_ml = nullptr, float* state_acc = nullptr,
+                        int state_stride = 0, int state_split = 0) {
   if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (fp8 && !std::isfinite(scale * k_scale))
@@ -321,7 +323,14 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
   p.query = static_cast<const uint16_t*>(query);
   p.kpool = static_cast<const uint16_t*>(key_cache);
   p.vpool = static_cast<const uint16_t*>(value_cache);
-  p.block_tables = block_tables;
+  // A skipped prefix of kv_skip tokens (whole blocks) starts every row that many entries in.
+  p.kv_skip = kv_skip;
+  p.block_tables = block_tables + kv_skip / block_size;
+  p.table_cols = max_blocks_per_seq - kv_skip / block_size;
+  p.state_ml = state_ml;
+  p.state_acc = state_acc;
+  p.state_stride = state_stride;
+  p.state_split = state_split;
   p.seq_lens = seq_lens;
   p.num_blocks = num_blocks;
   p.num_seqs = num_seqs;
@@ -377,6 +386,137 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const void* key_cache,
                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      max_blocks_per_seq, max_seq_len, scale, true, k_scale, v_scale, workspace,
                      workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of pa_decode_cascade: split states in the prefill layout (prompt splits plus one for
+// the tails) for every (sequence, query head) row, then the decode workspace.
+struct CascadeLayout {
+  pa::PrefillSplit split;
+  size_t ml_bytes, acc_off, dec_off, bytes;
+};
+
+CascadeLayout cascade_layout(int num_seqs, int num_groups, int max_group_size, int num_q_heads,
+                             int num_kv_heads, int head_dim, int prefix_len) {
+  CascadeLayout c{};
+  const int g = num_q_heads / num_kv_heads;
+  c.split = pa::prefill_split(num_groups, max_group_size, num_kv_heads, g, head_dim, prefix_len);
+  const size_t slots = (size_t)num_seqs * num_q_heads * (c.split.splits + 1);
+  c.ml_bytes = align_up(slots * 2 * sizeof(float), 256);
+  c.acc_off = c.ml_bytes;
+  c.dec_off = align_up(c.acc_off + slots * head_dim * sizeof(float), 256);
+  const size_t dec = pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g).bytes;
+  c.bytes = dec ? c.dec_off + dec : 0;
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_groups,
+                                         int32_t max_group_size, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t prefix_len) {
+  if (num_seqs <= 0 || num_groups <= 0 || max_group_size <= 0 || prefix_len <= 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return 0;
+  const int g = num_q_heads / num_kv_heads;
+  if (!supported_head_dim(head_dim) || !supported_group(g, head_dim)) return 0;
+  return cascade_layout(num_seqs, num_groups, max_group_size, num_q_heads, num_kv_heads, head_dim,
+                        prefix_len).bytes;
+}
+
+pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, int64_t num_blocks,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* group_start, int32_t num_seqs, int32_t num_groups,
+                              int32_t max_group_size, int32_t prefix_len, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_groups < 0 || max_group_size < 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size (num_seqs %d, num_groups %d, max_group_size %d)",
+                num_seqs, num_groups, max_group_size);
+  pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
+                                         max_blocks_per_seq, max_seq_len, scale);
+  if (st != PA_OK) return st;
+  if (num_blocks <= 0 || num_blocks > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks %lld out of range", (long long)num_blocks);
+  if (prefix_len <= 0 || prefix_len % block_size || prefix_len > max_seq_len)
+    return fail(PA_ERR_INVALID_ARG,
+                "prefix_len %d must be a positive multiple of block_size %d and <= max_seq_len %d",
+                prefix_len, block_size, max_seq_len);
+  if (num_seqs == 0) return ok();
+  if (num_groups == 0 || max_group_size == 0 || max_group_size > num_seqs)
+    return fail(PA_ERR_INVALID_ARG, "num_groups %d / max_group_size %d do not cover %d sequences",
+                num_groups, max_group_size, num_seqs);
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !group_start)
+    return fail(PA_ERR_NULL_POINTER, "null pointer argument");
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4) ||
+      !aligned(group_start, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for bf16 arrays)");
+  if (out == query) return fail(PA_ERR_INVALID_ARG, "out must not alias query");
+  const CascadeLayout c = cascade_layout(num_seqs, num_groups, max_group_size, num_q_heads,
+                                         num_kv_heads, head_dim, prefix_len);
+  if (c.bytes == 0) return fail(PA_ERR_HIP, "cannot query the device for the launch shapes");
+  if (!workspace || workspace_bytes < c.bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                c.bytes);
+  if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  float* ml = reinterpret_cast<float*>(ws);
+  float* acc = reinterpret_cast<float*>(ws + c.acc_off);
+  const int S = c.split.splits;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  // 1. The shared prompt, once per group: the group's decode queries are one non-causal chunk
+  //    over the first prefix_len tokens, read through the table row of the group's first member.
+  pa::PrefillParams a{};
+  a.out = static_cast<uint16_t*>(out);
+  a.query = static_cast<const uint16_t*>(query);
+  a.kpool = static_cast<const uint16_t*>(key_cache);
+  a.vpool = static_cast<const uint16_t*>(value_cache);
+  a.block_tables = block_tables;
+  a.query_start_loc = group_start;
+  a.seq_lens = seq_lens;
+  a.ws_ml = ml;
+  a.ws_acc = acc;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_groups;
+  a.total_q = num_seqs;
+  a.max_q_len = max_group_size;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_seq_len = prefix_len;
+  a.splits = S;
+  a.split_keys = S > 1 ? c.split.split_keys : prefix_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.noncausal = 1;
+  a.table_from_qsl = 1;
+  a.fixed_len = prefix_len;
+  a.ws_splits = S + 1;
+  a.defer_merge = 1;
+  if (S > 1 && a.split_keys % 32)
+    return fail(PA_ERR_HIP, "internal: prompt split of %d keys", a.split_keys);
+  hipError_t e = pa::launch_prefill(a, hs);
+  if (e != hipSuccess) return hip_status(e, "decode_cascade (prompt)");
+  // 2. Each sequence's own tokens past the prompt, as decode with the prompt's blocks skipped;
+  //    the per-row state goes to the last split.
+  st = decode_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
+                   num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                   max_seq_len, scale, false, 1.f, 1.f, ws + c.dec_off, workspace_bytes - c.dec_off,
+                   stream, prefix_len, ml, acc, S + 1, S);
+  if (st != PA_OK) return st;
+  // 3. Combine the prompt splits with the tail split of every row.
+  return hip_status(pa::launch_prefill_merge(a, hs), "decode_cascade (merge)");
 }
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
@@ -451,6 +591,8 @@ pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache
   p.max_seq_len = max_seq_len;
   p.splits = need > 0 ? sp.splits : 1;
   p.split_keys = need > 0 ? sp.split_keys : max_seq_len;
+  p.ws_splits = p.splits;
+  p.fixed_len = -1;  // lengths from seq_lens; causal; merged here
   p.scale_log2 = scale * 1.4426950408889634f;
   if (need > 0) {
     const size_t rows = (size_t)total_q * num_q_heads * p.splits;

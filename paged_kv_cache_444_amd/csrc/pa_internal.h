@@ -43,6 +43,16 @@ struct DecodeParams {
   // every output is multiplied by v_scale; for bf16 pools v_scale is 1.
   int kv_fp8;
   float v_scale;
+  // Shared-prefix (cascade) use.  kv_skip: leading tokens of every sequence left out (a multiple
+  // of block_size; block_tables then points kv_skip / block_size entries into each row and
+  // table_cols is the entries left per row).  state_ml non-null: each (sequence, query head) row's
+  // final (m in the log2 domain, l) and unnormalised acc go to split state_split of the prefill
+  // workspace layout (state_ml[2u], state_ml[2u+1], state_acc[u*D..], u = row*state_stride +
+  // state_split) instead of the output.
+  int kv_skip, table_cols;
+  float* state_ml;
+  float* state_acc;
+  int state_stride, state_split;
 };
 
 // Waves the decode kernel is launched with for this shape on the current device.
@@ -86,6 +96,12 @@ struct PrefillParams {
   int max_blocks_per_seq, max_seq_len;
   int splits, split_keys;  // context split: `splits` key ranges of split_keys keys (multiple of 32)
   float scale_log2;
+  // Shared-prefix (cascade) use.  noncausal: every row sees all L keys.  table_from_qsl: sequence
+  // i's block-table row is query_start_loc[i] (its first query row's sequence).  fixed_len >= 0:
+  // every sequence's L.  ws_splits: split count of the workspace layout (>= splits; split j of
+  // row u is slot u * ws_splits + j).  defer_merge: always write split states, never the output;
+  // the caller merges later.
+  int noncausal, table_from_qsl, fixed_len, ws_splits, defer_merge;
 };
 
 // Context split chosen for a prefill launch (it sizes the workspace).
@@ -95,6 +111,8 @@ struct PrefillSplit {
 PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int group, int head_dim,
                            int max_seq_len);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+// Combine p.ws_splits split states of each of p.total_q rows into p.out.
+hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t stream);
 
 // Kernel timing: when tracing is on, launches are bracketed by events on their stream.
 struct TraceScope {

@@ -181,8 +181,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   const int q_len = p.query_start_loc[s + 1] - qs;
   const int q0 = blockIdx.x * TQ;
   if (q_len <= 0 || q0 >= q_len) return;  // block-uniform
-  const int L = min(max(p.seq_lens[s], 0), p.max_seq_len);
-  const int ctx = max(L - q_len, 0);
+  const int L = p.fixed_len >= 0 ? min(p.fixed_len, p.max_seq_len)
+                                  : min(max(p.seq_lens[s], 0), p.max_seq_len);
+  // Non-causal rows see every key: ctx = L makes each row's last visible key L - 1.
+  const int ctx = p.noncausal ? L : max(L - q_len, 0);
   const int tq = min(TQ, q_len - q0);
   const int kv_end = min(L, ctx + q0 + tq);
   const int kb = split * p.split_keys;
@@ -236,10 +238,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  // With table_from_qsl the row is the first query row's sequence, clamped into the table (whose
+  // rows are the total_q query rows) so a malformed query_start_loc cannot leave it.
+  const int trow = p.table_from_qsl ? min(max(qs, 0), p.total_q - 1) : s;
+  const int* bt = p.block_tables + (size_t)trow * p.max_blocks_per_seq;
   const int t_first = kb / kKeyTile;
   const int t_end = (ke + kKeyTile - 1) / kKeyTile;  // empty range: t_end <= t_first
-  const int diag = ctx + q0;  // keys above this need a per-row mask
+  // Keys above this need a per-row mask (non-causal: only keys at or past L, in the last tile).
+  const int diag = p.noncausal ? L - 1 : ctx + q0;
   // Table slice of this workgroup's keys [32*t_first, 32*t_end), clamped into the pool.
   const int bs = p.block_size;
   const int blk0 = (t_first * kKeyTile) / bs;
@@ -398,7 +404,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     if (!row_ok[rt]) continue;
     const int r = wave * 16 * RT + 16 * rt + (lane & 15);
     const size_t orow = (size_t)(qs + row_tok[rt]) * Hq + (size_t)h * G + r % G;
-    if (p.splits == 1) {
+    if (p.splits == 1 && !p.defer_merge) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
         *(uint2*)(p.out + orow * D + 16 * dt + 4 * (lane >> 4)) = o;
       }
     } else {
-      const size_t u = orow * p.splits + split;
+      const size_t u = orow * p.ws_splits + split;
       if (lane < 16) {
         p.ws_ml[2 * u] = m[rt] * c;  // log2 domain; -inf for an empty or fully masked range
         p.ws_ml[2 * u + 1] = lt;
@@ -428,13 +434,13 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
   const size_t unit = (size_t)blockIdx.x * (256 / TPH) + threadIdx.x / TPH;  // row * Hq + head
   if (unit >= (size_t)p.total_q * p.num_q_heads) return;
   const int d = 4 * (threadIdx.x % TPH);
-  const size_t u0 = unit * p.splits;
+  const size_t u0 = unit * p.ws_splits;
   float M = kNegInf;
-  for (int j = 0; j < p.splits; ++j) M = fmaxf(M, p.ws_ml[2 * (u0 + j)]);
+  for (int j = 0; j < p.ws_splits; ++j) M = fmaxf(M, p.ws_ml[2 * (u0 + j)]);
   float lt = 0.f;
   f32x4_t a = {0.f, 0.f, 0.f, 0.f};
   if (M != kNegInf) {
-    for (int j = 0; j < p.splits; ++j) {
+    for (int j = 0; j < p.ws_splits; ++j) {
       const float mj = p.ws_ml[2 * (u0 + j)];
       if (mj == kNegInf) continue;  // empty range for this row
       const float w = fast_exp2(mj - M);
@@ -447,6 +453,16 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
       make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
 }
 
+template <int D>
+hipError_t merge_d(const PrefillParams& p, hipStream_t stream) {
+  TraceScope t("prefill_merge", stream);
+  constexpr int UPB = 256 / (D / 4);  // (row, head) units per block
+  const size_t units = (size_t)p.total_q * p.num_q_heads;
+  const dim3 grid((unsigned)((units + UPB - 1) / UPB));
+  hipLaunchKernelGGL((prefill_merge_kernel<D>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_dg(const PrefillParams& p, hipStream_t stream) {
   constexpr int TQ = kPWaves * 16 * kRowTiles<D> / G;
@@ -456,15 +472,8 @@ hipError_t launch_dg(const PrefillParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kPThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  {
-    TraceScope t("prefill_merge", stream);
-    constexpr int UPB = 256 / (D / 4);  // (row, head) units per block
-    const size_t units = (size_t)p.total_q * p.num_q_heads;
-    const dim3 grid((unsigned)((units + UPB - 1) / UPB));
-    hipLaunchKernelGGL((prefill_merge_kernel<D>), grid, dim3(256), 0, stream, p);
-  }
-  return hipGetLastError();
+  if (e != hipSuccess || p.splits == 1 || p.defer_merge) return e;
+  return merge_d<D>(p, stream);
 }
 
 template <int D>
@@ -551,12 +560,23 @@ PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int gr
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  if (p.splits < 1 || (p.splits > 1 && p.split_keys % kKeyTile)) return hipErrorInvalidValue;
+  if (p.splits < 1 || (p.splits > 1 && p.split_keys % kKeyTile) || p.ws_splits < p.splits)
+    return hipErrorInvalidValue;
   const int G = p.num_q_heads / p.num_kv_heads;
   switch (p.head_dim) {
     case 64: return launch_d<64>(p, G, stream);
     case 128: return launch_d<128>(p, G, stream);
     case 256: return launch_d<256>(p, G, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t stream) {
+  if (p.ws_splits < 1) return hipErrorInvalidValue;
+  switch (p.head_dim) {
+    case 64: return merge_d<64>(p, stream);
+    case 128: return merge_d<128>(p, stream);
+    case 256: return merge_d<256>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

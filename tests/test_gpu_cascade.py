@@ -1,0 +1,85 @@
+"""GPU parity of pa_decode_cascade (decode of sequences sharing a prompt's blocks) against the
+fp64 CPU oracle's plain decode: the cascade only reorders the same attention, so every output
+element must satisfy |gpu - oracle| <= 1e-2 + 1e-2*|oracle|."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_444_amd as pa
+from helpers import (assert_close, cached_named_case, cached_oracle_pools, dev_i32, dev_i64,
+                     dev_u16, host_u16, upcast)
+from oracle import paged_attention as oracle
+from workloads import Spec, build_case
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _cascade(case, kc, vc, group_start, prefix_len, seq_lens=None):
+    d = case.decode
+    sl = d.seq_lens if seq_lens is None else seq_lens
+    gs = np.asarray(group_start, dtype=np.int32)
+    out = pa.decode_cascade(dev_u16(d.query), kc, vc, dev_i32(d.block_tables), dev_i32(sl),
+                            dev_i32(gs), prefix_len=prefix_len,
+                            max_group_size=int(np.diff(gs).max()), num_kv_heads=case.num_kv_heads,
+                            block_size=case.block_size, scale=float(case.scale),
+                            max_seq_len=int(np.max(sl)))
+    torch.cuda.synchronize()
+    return host_u16(out)
+
+
+def test_cascade_parity_prefix_shared_rollouts():
+    """8 prompts x 16 candidates sharing a 4,096-token prompt's blocks, private tails of 0..1,024
+    tokens, one new token each (Llama-3.3-70B shapes)."""
+    case = cached_named_case(5)
+    d = case.decode
+    say(f"cascade cfg5: {case.name}, B={d.num_seqs}, max L={d.max_seq_len}")
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    r = case.reshape
+    pa.reshape_and_cache(dev_u16(r.key), dev_u16(r.value), kc, vc, dev_i64(r.slot_mapping),
+                         num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                         block_size=case.block_size)
+    gs = np.arange(0, 129, 16)
+    got = _cascade(case, kc, vc, gs, 4096)
+    assert np.array_equal(got, _cascade(case, kc, vc, gs, 4096)), "not reproducible"
+    okc, ovc = cached_oracle_pools(5)
+    seqs = sorted({0, 15, 16, 127} | set(np.random.default_rng(80).choice(128, 12, replace=False).tolist()))
+    ref = oracle.decode(d.query, okc, ovc, d.block_tables, d.seq_lens, case.num_kv_heads,
+                        case.head_dim, case.block_size, case.scale, seqs=seqs)
+    assert_close(upcast(got)[seqs], ref[seqs], "cascade decode cfg5")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(8, 2, 64, 16), (16, 1, 64, 32), (64, 8, 128, 16),
+                                         (16, 4, 256, 32), (4, 4, 128, 16)])
+def test_cascade_groups_tails_and_edges(Hq, Hkv, D, bs):
+    # Groups of 3, 1, 5 and 2 sequences sharing 2*bs (or, for the group of one, its own) first
+    # tokens; tails of 0 .. 300 tokens, including an empty tail and a tail inside one block.
+    P = 2 * bs
+    lens = [P + t for t in (0, 1, 17, 300, 5, 64, 33, 2, P, 9, 150)]
+    groups = [(0, 3), (3, 4), (4, 9), (9, 11)]
+    spec = Spec(name="cascade", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                seed=(444, 81, Hq, D, bs), decode_lens=lens,
+                share_groups=[(list(range(a, b)), P) for a, b in groups if b - a > 1])
+    case = build_case(spec)
+    d = case.decode
+    for a, b in groups:
+        assert all(np.array_equal(d.block_tables[a, :2], d.block_tables[m, :2]) for m in range(a, b))
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    gs = [0] + [b for _, b in groups]
+    got = upcast(_cascade(case, kc, vc, gs, P))
+    ref = oracle.decode(d.query, case.key_cache, case.value_cache, d.block_tables, d.seq_lens, Hkv,
+                        D, bs, case.scale)
+    assert_close(got, ref, f"cascade decode {Hq}/{Hkv}/{D}/{bs}")
+    # equal to plain decode within the same tolerance
+    plain = pa.decode(dev_u16(d.query), kc, vc, dev_i32(d.block_tables), dev_i32(d.seq_lens),
+                      num_kv_heads=Hkv, block_size=bs, scale=float(case.scale),
+                      max_seq_len=d.max_seq_len)
+    torch.cuda.synchronize()
+    assert_close(upcast(host_u16(plain)), ref, "plain decode")

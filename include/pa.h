@@ -273,6 +273,22 @@ pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache
                              size_t workspace_bytes, void* stream);
 
 /*
+ * pa_prefill_chunk_fp8 — pa_prefill_chunk over FP8 pools written by pa_reshape_and_cache_fp8
+ * (the chunk's own K/V included), with the same k_scale and v_scale.  The attention is that of
+ * pa_prefill_chunk on the dequantised cache; codes are widened to bf16 exactly before both
+ * matrix-core products.  Workspace (same size query), limits and errors as pa_prefill_chunk;
+ * k_scale and v_scale must be finite and positive.
+ */
+pa_status_t pa_prefill_chunk_fp8(void* out, const void* query, const void* key_cache,
+                                 const void* value_cache, int64_t num_blocks,
+                                 const int32_t* block_tables, const int32_t* query_start_loc,
+                                 const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
+                                 int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                 int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing (tracing).  While enabled, every kernel the library launches is bracketed by a
  * pair of HIP events recorded on its stream.  pa_trace_read synchronises on the recorded events,
  * returns the number of launches and their summed duration (milliseconds) for one kernel name, and

@@ -298,3 +298,25 @@ def decode_fp8(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray
                              num_kv_heads, head_dim, block_size, k_scale, v_scale)
         out[s] = attention(bf16_to_f64(query[s])[None], k, v, scale)[0]
     return out
+
+
+def prefill_chunk_fp8(query: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+                      block_tables: np.ndarray, query_start_loc: np.ndarray, seq_lens: np.ndarray,
+                      num_kv_heads: int, head_dim: int, block_size: int, scale: float,
+                      k_scale: float, v_scale: float,
+                      rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Chunked prefill over an FP8 cache: the attention of `prefill_chunk` on the dequantised
+    keys and values."""
+    total_q, Hq, D = query.shape
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    want = np.arange(total_q) if rows is None else np.asarray(list(rows), dtype=np.int64)
+    out = np.zeros((len(want), Hq, D))
+    for i in range(len(qsl) - 1):
+        lo, hi = int(qsl[i]), int(qsl[i + 1])
+        sel = np.nonzero((want >= lo) & (want < hi))[0]
+        if sel.size == 0:
+            continue
+        k, v = gather_kv_fp8(key_cache, value_cache, block_tables[i], int(seq_lens[i]),
+                             num_kv_heads, head_dim, block_size, k_scale, v_scale)
+        out[sel] = attention(bf16_to_f64(query[lo:hi]), k, v, scale, rows=(want[sel] - lo).tolist())
+    return out

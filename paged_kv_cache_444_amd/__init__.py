@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "load_library", "reshape_and_cache", "reshape_and_cache_fp8", "copy_blocks", "decode",
     "decode_fp8", "decode_cascade", "decode_cascade_workspace_bytes", "prefill_chunk",
+    "prefill_chunk_fp8",
     "mixed_step", "decode_workspace_bytes", "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
     "LIB_PATH",
 ]
@@ -59,6 +60,9 @@ _SIGNATURES = {
     "pa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_prefill_chunk": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                 _I32, _I32, _I32, _I32, ctypes.c_float, _P, _SZ, _P]),
+    "pa_prefill_chunk_fp8": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                    _I32, _I32, _I32, _I32, ctypes.c_float, ctypes.c_float,
+                                    ctypes.c_float, _P, _SZ, _P]),
     "pa_trace_enable": (_I32, [_I32]),
     "pa_trace_read": (_I32, [ctypes.c_char_p, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double)]),
 }
@@ -344,6 +348,35 @@ def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None):
     # The decode output (and a caller's tensors) are used on the current stream from here on.
     dout.record_stream(main)
     return pout, dout
+
+
+def prefill_chunk_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      block_tables: torch.Tensor, query_start_loc: torch.Tensor,
+                      seq_lens: torch.Tensor, *, num_kv_heads: int, block_size: int, max_q_len: int,
+                      max_seq_len: int, k_scale: float, v_scale: float,
+                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunked-prefill attention over uint8 pools of E4M3 codes (reshape_and_cache_fp8)."""
+    lib = load_library()
+    total_q, Hq, D = query.shape
+    n = seq_lens.numel()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(query)
+    ws, ws_bytes = _workspace(prefill_workspace_bytes(n, total_q, max_q_len, Hq, num_kv_heads, D,
+                                                      max_seq_len), workspace, query.device)
+    nb = _num_blocks_fp8(key_cache, num_kv_heads, block_size, D)
+    _check(lib.pa_prefill_chunk_fp8(_bf16(out, "out"), _bf16(query, "query"),
+                                    _fp8_pool(key_cache, "key_cache"),
+                                    _fp8_pool(value_cache, "value_cache"), nb,
+                                    _ints(block_tables, torch.int32, "block_tables"),
+                                    _ints(query_start_loc, torch.int32, "query_start_loc"),
+                                    _ints(seq_lens, torch.int32, "seq_lens"), n, total_q, max_q_len,
+                                    Hq, num_kv_heads, D, block_size, block_tables.shape[1],
+                                    max_seq_len, float(scale), float(k_scale), float(v_scale), ws,
+                                    ws_bytes, _stream()))
+    return out
 
 
 def trace_enable(on: bool = True) -> None:

@@ -504,6 +504,7 @@ pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cach
   a.fixed_len = prefix_len;
   a.ws_splits = S + 1;
   a.defer_merge = 1;
+  a.v_scale = 1.f;
   if (S > 1 && a.split_keys % 32)
     return fail(PA_ERR_HIP, "internal: prompt split of %d keys", a.split_keys);
   hipError_t e = pa::launch_prefill(a, hs);
@@ -534,14 +535,22 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max
   return align_up(rows * 2 * sizeof(float), 256) + rows * head_dim * sizeof(float);
 }
 
-pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache,
-                             const void* value_cache, int64_t num_blocks,
-                             const int32_t* block_tables, const int32_t* query_start_loc,
-                             const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
-                             int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
-                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                             int32_t max_seq_len, float scale, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status_t prefill_impl(void* out, const void* query, const void* key_cache,
+                         const void* value_cache, int64_t num_blocks,
+                         const int32_t* block_tables, const int32_t* query_start_loc,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
+                         int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                         int32_t max_seq_len, float scale, bool fp8, float k_scale,
+                         float v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
+    return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if (fp8 && !std::isfinite(scale * k_scale))
+    return fail(PA_ERR_INVALID_ARG, "scale * k_scale overflows");
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0)
     return fail(PA_ERR_INVALID_ARG, "negative size (num_seqs %d, total_q %d, max_q_len %d)",
                 num_seqs, total_q, max_q_len);
@@ -593,7 +602,10 @@ pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache
   p.split_keys = need > 0 ? sp.split_keys : max_seq_len;
   p.ws_splits = p.splits;
   p.fixed_len = -1;  // lengths from seq_lens; causal; merged here
-  p.scale_log2 = scale * 1.4426950408889634f;
+  // FP8: the K scale joins the softmax scale and the V scale multiplies the outputs.
+  p.scale_log2 = (fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
+  p.kv_fp8 = fp8;
+  p.v_scale = fp8 ? v_scale : 1.f;
   if (need > 0) {
     const size_t rows = (size_t)total_q * num_q_heads * p.splits;
     p.ws_ml = static_cast<float*>(workspace);
@@ -601,6 +613,38 @@ pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache
                                         align_up(rows * 2 * sizeof(float), 256));
   }
   return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill_chunk");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_prefill_chunk(void* out, const void* query, const void* key_cache,
+                             const void* value_cache, int64_t num_blocks,
+                             const int32_t* block_tables, const int32_t* query_start_loc,
+                             const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
+                             int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int32_t max_seq_len, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return prefill_impl(out, query, key_cache, value_cache, num_blocks, block_tables,
+                      query_start_loc, seq_lens, num_seqs, total_q, max_q_len, num_q_heads,
+                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len, scale,
+                      false, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_prefill_chunk_fp8(void* out, const void* query, const void* key_cache,
+                                 const void* value_cache, int64_t num_blocks,
+                                 const int32_t* block_tables, const int32_t* query_start_loc,
+                                 const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
+                                 int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                 int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(out, query, key_cache, value_cache, num_blocks, block_tables,
+                      query_start_loc, seq_lens, num_seqs, total_q, max_q_len, num_q_heads,
+                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len, scale,
+                      true, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

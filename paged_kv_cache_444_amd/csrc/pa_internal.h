@@ -102,6 +102,10 @@ struct PrefillParams {
   // row u is slot u * ws_splits + j).  defer_merge: always write split states, never the output;
   // the caller merges later.
   int noncausal, table_from_qsl, fixed_len, ws_splits, defer_merge;
+  // FP8 pools (E4M3 codes, same element order, one byte each); outputs and split states are
+  // multiplied by v_scale (1 for bf16 pools).
+  int kv_fp8;
+  float v_scale;
 };
 
 // Context split chosen for a prefill launch (it sizes the workspace).

@@ -71,6 +71,14 @@ __device__ __forceinline__ float xor32_f32(float x) { return __shfl_xor(x, 32, 6
 // issues the same number of loads per tile, so a vmcnt wait releases exactly one tile without
 // touching registers.  Physical block ids come from an LDS copy of the table slice, so no other
 // vector-memory load is in flight inside the walk.
+//
+// FP8 pools (E4M3 codes, one byte per element): an operand is 8 bytes, and the operands of lanes
+// l and l+16 (l/16 even) are contiguous in the pool: the two 8-dim halves of one 32-byte K row
+// of a slice, or the two 8-key halves of one 16-byte V row.  So one 16-byte direct load fetches
+// a lane pair's operands, a wave's load covers two 512-byte pieces, and each wave issues half as
+// many loads per tile.  In LDS pair q of a piece sits at 16*q (q = l%16 + 16*(l/32) for the
+// reading lane l, which takes the half (l/16)%2); the reads are 8 bytes, widened to bf16 by
+// v_cvt_scalef32_pk_bf16_fp8 (exact).
 #ifndef PA_PREFILL_STAGES
 #define PA_PREFILL_STAGES 3
 #endif
@@ -101,6 +109,7 @@ __device__ __forceinline__ void lds_dma_16(const uint16_t* src, unsigned m0) {
 // wave-uniform.
 struct TileSrc {
   const uint16_t* pool;    // K or V pool + KV head h + this lane's offset inside a piece
+  const uint8_t* pool8;    // the same for FP8 pools (byte addressing)
   long long block_stride;  // elements per physical block (all KV heads)
   unsigned lds;            // LDS byte address of this wave's first piece in stage 0
   int sb;                  // sub-block (0: keys 0-15 of the tile, 1: keys 16-31) of this lane
@@ -110,7 +119,7 @@ struct TileSrc {
 
 // Lane l of K piece (kt, ks): key kappa = 8*((l%16)/4) + l%4 + 4*kt of the tile, dims
 // 32*ks + 8*(l/16) .. +7.  Lane l of V piece dt: dim 16*dt + l%16, keys 8*(l/16) .. +7.
-template <int D>
+template <int D, bool Fp8>
 __device__ __forceinline__ TileSrc tile_src(const PrefillParams& p, int h, const void* lds0) {
   constexpr int KS = D / 32, DT = D / 16;
   const int lane = threadIdx.x & 63;
@@ -121,6 +130,30 @@ __device__ __forceinline__ TileSrc tile_src(const PrefillParams& p, int h, const
   ts.max_id = (int)(p.num_blocks - 1);
   ts.block_stride = (long long)p.num_kv_heads * p.block_size * D;
   int off, first_piece;
+  if constexpr (Fp8) {
+    // Fetching lane j: piece (j/32) of the load's two, lane pair q = j%32, whose first lane is
+    // l = q%16 + 32*(q/16).
+    const int q = lane & 31, half_piece = lane >> 5;
+    const int l = (q & 15) + 32 * (q >> 4);
+    if (r < 2) {  // K pieces (kt = r, ks = 2*load + half_piece): 16 bytes of key kappa's row
+      const int key = 8 * ((l & 15) >> 2) + (l & 3) + 4 * r;
+      ts.sb = key >> 4;
+      off = half_piece * 512 + (key & 15) * 32 + 8 * (l >> 4);
+      ts.piece_step = 1024;  // bytes between a wave's loads: two 32-dim slices
+      first_piece = r * KS;
+    } else {  // V pieces dt = (r-2)*DT/2 + 2*load + half_piece: the 16-byte row of dim 16dt + l%16
+      ts.sb = l >> 5;
+      off = ((r - 2) * (DT / 2) * 16 + half_piece * 16 + (l & 15)) * 16;
+      ts.piece_step = 512;  // two pieces of 16 dims x 16 keys
+      first_piece = 2 * KS + (r - 2) * (DT / 2);
+    }
+    ts.pool = nullptr;
+    ts.pool8 = reinterpret_cast<const uint8_t*>((r < 2) ? p.kpool : p.vpool) +
+               (size_t)h * p.block_size * D + off;
+    const unsigned l0 = (unsigned)(uintptr_t)(const lds_u16*)lds0;
+    ts.lds = __builtin_amdgcn_readfirstlane(l0 + (unsigned)first_piece * 512);
+    return ts;
+  }
   if (r < 2) {  // K of product kt = r; the pool sub-block layout is [D/32][16 keys][32 dims]
     const int key = 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * r;
     ts.sb = key >> 4;
@@ -135,15 +168,16 @@ __device__ __forceinline__ TileSrc tile_src(const PrefillParams& p, int h, const
     first_piece = 2 * KS + (r - 2) * (DT / 2);
   }
   ts.pool = ((r < 2) ? p.kpool : p.vpool) + (size_t)h * p.block_size * D + off;
+  ts.pool8 = nullptr;
   const unsigned l0 = (unsigned)(uintptr_t)(const lds_u16*)lds0;
   ts.lds = __builtin_amdgcn_readfirstlane(l0 + (unsigned)first_piece * 1024);
   return ts;
 }
 
-template <int D>
+template <int D, bool Fp8>
 __device__ __forceinline__ void issue_tile(const TileSrc& ts, const int* ids_lds, int blk0,
                                            int tile, int L, int stage) {
-  constexpr int NP = D / 32;
+  constexpr int NP = Fp8 ? D / 64 : D / 32;  // loads per wave
   // Physical blocks of the tile's two sub-blocks.  Keys at or past L fetch block 0 (always
   // inside the pool): their V rows are zeroed before use and their scores are masked.
   long long base[2];
@@ -155,13 +189,30 @@ __device__ __forceinline__ void issue_tile(const TileSrc& ts, const int* ids_lds
     id = min(max(__builtin_amdgcn_readfirstlane(id), 0), ts.max_id);  // stays inside the pool
     base[sb] = (long long)id * ts.block_stride + (long long)(key0 & ts.bmask) * D;
   }
-  const uint16_t* src = ts.pool + (ts.sb ? base[1] : base[0]);
   const unsigned m0 = ts.lds + (unsigned)stage * (4 * 16 * D * 2);
+  if constexpr (Fp8) {
+    const uint8_t* src = ts.pool8 + (ts.sb ? base[1] : base[0]);  // one byte per element
 #pragma unroll
-  for (int pc = 0; pc < NP; ++pc) lds_dma_16(src + pc * ts.piece_step, m0 + pc * 1024);
+    for (int pc = 0; pc < NP; ++pc)
+      lds_dma_16(reinterpret_cast<const uint16_t*>(src + pc * ts.piece_step), m0 + pc * 1024);
+  } else {
+    const uint16_t* src = ts.pool + (ts.sb ? base[1] : base[0]);
+#pragma unroll
+    for (int pc = 0; pc < NP; ++pc) lds_dma_16(src + pc * ts.piece_step, m0 + pc * 1024);
+  }
 }
 
-template <int D, int G>
+// Eight E4M3 codes -> eight bf16 values, same order.
+template <bool Hi>
+__device__ __forceinline__ uint32_t fp8_pair_to_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, Hi));
+}
+__device__ __forceinline__ uint4 widen8(const uint2& w) {
+  return make_uint4(fp8_pair_to_bf16<false>(w.x), fp8_pair_to_bf16<true>(w.x),
+                    fp8_pair_to_bf16<false>(w.y), fp8_pair_to_bf16<true>(w.y));
+}
+
+template <int D, int G, bool Fp8>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   constexpr int RT = kRowTiles<D>;
   constexpr int KS = D / 32;       // k-steps of the score product
@@ -270,11 +321,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   wait_vmcnt<0>();
   __syncthreads();
   if (t_first < t_end) {
-    constexpr int NP = D / 32;
-    const TileSrc ts = tile_src<D>(p, h, &lds[0][0]);
+    constexpr int NP = Fp8 ? D / 64 : D / 32;  // tile loads per wave
+    const TileSrc ts = tile_src<D, Fp8>(p, h, &lds[0][0]);
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k)
-      issue_tile<D>(ts, ids_lds, blk0, min(t_first + k, t_end - 1), L, k);
+      issue_tile<D, Fp8>(ts, ids_lds, blk0, min(t_first + k, t_end - 1), L, k);
     // One key tile.  kMasked: the tile reaches past the first row's diagonal and the causal mask
     // is applied per score; those tiles are the last ones of the walk, so the two variants run
     // as two loops and the other tiles carry no per-score selects.
@@ -285,18 +336,32 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       const int prev = (cur == 0) ? kStages - 1 : cur - 1;  // tile t-1's stage, free below
       wait_vmcnt<NP * (kStages - 2)>();  // this wave's part of tile t has landed
       __syncthreads();                   // all parts landed; every wave is done with tile t-1
-      issue_tile<D>(ts, ids_lds, blk0, min(t + kStages - 1, t_end - 1), L, prev);
+      issue_tile<D, Fp8>(ts, ids_lds, blk0, min(t + kStages - 1, t_end - 1), L, prev);
       if (t * kKeyTile + kKeyTile > L) {  // block-uniform: zero V rows of keys at or past L
-        uint16_t* vz = &lds[cur][2 * 16 * D];
-        for (int i = threadIdx.x; i < 2 * 16 * D; i += kPThreads) {
-          // piece i / 512, lane (i % 512) / 8 holding keys 8 * (lane / 16) .., element i % 8
-          const int key = t * kKeyTile + 8 * ((i >> 7) & 3) + (i & 7);
-          if (key >= L) vz[i] = 0;
+        if constexpr (Fp8) {
+          uint8_t* vz = reinterpret_cast<uint8_t*>(&lds[cur][0]) + 32 * D;
+          for (int i = threadIdx.x; i < 32 * D; i += kPThreads) {
+            // byte i of piece i / 512: pair (i % 512) / 16, half (i / 8) % 2, code i % 8, which
+            // is key 16 * ((i / 256) % 2) + i % 16 of the tile
+            const int key = t * kKeyTile + 16 * ((i >> 8) & 1) + (i & 15);
+            if (key >= L) vz[i] = 0;  // code 0 is +0
+          }
+        } else {
+          uint16_t* vz = &lds[cur][2 * 16 * D];
+          for (int i = threadIdx.x; i < 2 * 16 * D; i += kPThreads) {
+            // piece i / 512, lane (i % 512) / 8 holding keys 8 * (lane / 16) .., element i % 8
+            const int key = t * kKeyTile + 8 * ((i >> 7) & 3) + (i & 7);
+            if (key >= L) vz[i] = 0;
+          }
         }
         __syncthreads();
       }
       const uint16_t* kl = lds[cur];
       const uint16_t* vl = lds[cur] + 2 * 16 * D;
+      const uint8_t* kl8 = reinterpret_cast<const uint8_t*>(lds[cur]);
+      const uint8_t* vl8 = kl8 + 32 * D;
+      // FP8: this lane's operand in a 512-byte piece: pair q, half (lane/16)%2.
+      const int op8 = 16 * ((lane & 15) + 16 * (lane >> 5)) + 8 * ((lane >> 4) & 1);
 
       // K fragments, the A operands of the score product, shared by the row tiles.  Row m of
       // product kt is key 8*(m/4) + m%4 + 4*kt of the tile, so lane l gets keys
@@ -307,11 +372,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          kf[kt][ks] = *(const uint4*)(kl + ((kt * KS + ks) * 64 + lane) * 8);
+          kf[kt][ks] = Fp8 ? widen8(*(const uint2*)(kl8 + (kt * KS + ks) * 512 + op8))
+                           : *(const uint4*)(kl + ((kt * KS + ks) * 64 + lane) * 8);
       // V fragments, the A operands of the second product: dim 16dt + lane%16, keys 8g .. 8g+7
       // (g = lane/16).
       auto v_frag = [&](int dt) __attribute__((always_inline)) {
-        return *(const uint4*)(vl + (dt * 64 + lane) * 8);
+        if constexpr (Fp8) return widen8(*(const uint2*)(vl8 + dt * 512 + op8));
+        else return *(const uint4*)(vl + (dt * 64 + lane) * 8);
       };
       auto scores = [&](int rt, f32x4_t (&sc)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -405,7 +472,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     const int r = wave * 16 * RT + 16 * rt + (lane & 15);
     const size_t orow = (size_t)(qs + row_tok[rt]) * Hq + (size_t)h * G + r % G;
     if (p.splits == 1 && !p.defer_merge) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f32x4_t a = acc[dt][rt];
@@ -421,7 +488,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        *(f32x4_t*)(p.ws_acc + u * D + 16 * dt + 4 * (lane >> 4)) = acc[dt][rt];
+        *(f32x4_t*)(p.ws_acc + u * D + 16 * dt + 4 * (lane >> 4)) = acc[dt][rt] * p.v_scale;
     }
   }
 }
@@ -469,7 +536,10 @@ hipError_t launch_dg(const PrefillParams& p, hipStream_t stream) {
   {
     TraceScope t("prefill_chunk", stream);
     const dim3 grid((p.max_q_len + TQ - 1) / TQ, p.num_kv_heads * p.splits, p.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kPThreads), 0, stream, p);
+    if (p.kv_fp8)
+      hipLaunchKernelGGL((prefill_kernel<D, G, true>), grid, dim3(kPThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, G, false>), grid, dim3(kPThreads), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1 || p.defer_merge) return e;
@@ -500,11 +570,15 @@ int cu_count() {
 template <int D>
 const void* kernel_of(int G) {
   switch (G) {
-    case 1: return reinterpret_cast<const void*>(&prefill_kernel<D, 1>);
-    case 2: return reinterpret_cast<const void*>(&prefill_kernel<D, 2>);
-    case 4: return reinterpret_cast<const void*>(&prefill_kernel<D, 4>);
-    case 8: if constexpr (D <= 128) return reinterpret_cast<const void*>(&prefill_kernel<D, 8>); break;
-    case 16: if constexpr (D <= 64) return reinterpret_cast<const void*>(&prefill_kernel<D, 16>); break;
+    case 1: return reinterpret_cast<const void*>(&prefill_kernel<D, 1, false>);
+    case 2: return reinterpret_cast<const void*>(&prefill_kernel<D, 2, false>);
+    case 4: return reinterpret_cast<const void*>(&prefill_kernel<D, 4, false>);
+    case 8:
+      if constexpr (D <= 128) return reinterpret_cast<const void*>(&prefill_kernel<D, 8, false>);
+      break;
+    case 16:
+      if constexpr (D <= 64) return reinterpret_cast<const void*>(&prefill_kernel<D, 16, false>);
+      break;
     default: break;
   }
   return nullptr;

@@ -133,3 +133,43 @@ def test_decode_fp8_shapes_and_ragged_lengths(Hq, Hkv, D, bs):
     ref = oracle.decode_fp8(d.query, kc8, vc8, d.block_tables, d.seq_lens, Hkv, D, bs, case.scale,
                             0.02, 0.03)
     assert_close(upcast(host_u16(out)), ref, f"FP8 decode {Hq}/{Hkv}/{D}/{bs}")
+
+
+def _gpu_prefill_fp8(case, kc8, vc8, k_scale, v_scale):
+    p = case.prefill
+    out = pa.prefill_chunk_fp8(dev_u16(p.query), dev_u8(kc8), dev_u8(vc8), dev_i32(p.block_tables),
+                               dev_i32(p.query_start_loc), dev_i32(p.seq_lens),
+                               num_kv_heads=case.num_kv_heads, block_size=case.block_size,
+                               max_q_len=p.max_q_len, max_seq_len=p.max_seq_len, k_scale=k_scale,
+                               v_scale=v_scale, scale=float(case.scale))
+    torch.cuda.synchronize()
+    return host_u16(out)
+
+
+def test_prefill_fp8_parity_long_context_chunk():
+    """The mixed workload's 512-token chunk over 31,744 cached tokens, over an FP8 cache."""
+    case, kc8, vc8 = _fp8_case_pools(4)
+    p = case.prefill
+    say(f"prefill fp8 cfg4: q_len={p.max_q_len}, L={p.max_seq_len}")
+    got = upcast(_gpu_prefill_fp8(case, kc8, vc8, K_SCALE, V_SCALE))
+    rows = [0, 1, 15, 16, 31, 127, 128, 255, 256, 383, 384, 500, 510, 511]
+    rows += sorted(np.random.default_rng(74).choice(512, size=6, replace=False).tolist())
+    ref = oracle.prefill_chunk_fp8(p.query, kc8, vc8, p.block_tables, p.query_start_loc,
+                                   p.seq_lens, case.num_kv_heads, case.head_dim, case.block_size,
+                                   case.scale, K_SCALE, V_SCALE, rows=rows)
+    assert_close(got[rows], ref, "FP8 prefill 512-token chunk over 31,744 cached tokens")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(8, 2, 64, 16), (16, 1, 64, 32), (64, 8, 128, 16),
+                                         (16, 2, 128, 32), (16, 4, 256, 32), (2, 2, 256, 16)])
+def test_prefill_fp8_shapes_and_ragged_chunks(Hq, Hkv, D, bs):
+    chunks = [(0, 1), (0, 37), (70, 33), (5, 16), (1000, 129), (40, 512)]
+    case = build_case(Spec(name="fp8p", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                           seed=(444, 75, Hq, Hkv, D, bs), prefill=chunks))
+    kc8 = oracle_quantize_pool(case.key_cache, 0.02)
+    vc8 = oracle_quantize_pool(case.value_cache, 0.03)
+    got = upcast(_gpu_prefill_fp8(case, kc8, vc8, 0.02, 0.03))
+    p = case.prefill
+    ref = oracle.prefill_chunk_fp8(p.query, kc8, vc8, p.block_tables, p.query_start_loc,
+                                   p.seq_lens, Hkv, D, bs, case.scale, 0.02, 0.03)
+    assert_close(got, ref, f"FP8 prefill {Hq}/{Hkv}/{D}/{bs}")

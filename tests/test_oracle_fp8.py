@@ -145,3 +145,24 @@ def test_fp8_pins_catch_planted_mistakes(monkeypatch):
     with monkeypatch.context() as m:
         m.setattr(fp8, "decode_table", lambda: bias8)
         assert not _fp8_pins_pass()
+
+
+def test_fp8_prefill_equals_bf16_prefill_on_exact_values():
+    case = build_case(Spec(name="fp8p", num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                           seed=(6,), prefill=[(40, 9), (0, 5)]))
+    rng = np.random.default_rng(6)
+    t = fp8.decode_table()
+    finite = t[~np.isnan(t)]
+    finite = finite[np.abs(finite) <= 8]
+    kc8 = rng.integers(0, len(finite), size=case.key_cache.shape)
+    vc8 = rng.integers(0, len(finite), size=case.value_cache.shape)
+    p = case.prefill
+    for scale in (1.0, 0.5):
+        kc16 = bf16_bits((finite[kc8] * scale).astype(np.float32))
+        vc16 = bf16_bits((finite[vc8] * scale).astype(np.float32))
+        ref = pa.prefill_chunk(p.query, kc16, vc16, p.block_tables, p.query_start_loc, p.seq_lens,
+                               2, 64, 16, case.scale)
+        got = pa.prefill_chunk_fp8(p.query, fp8.encode(finite[kc8]), fp8.encode(finite[vc8]),
+                                   p.block_tables, p.query_start_loc, p.seq_lens, 2, 64, 16,
+                                   case.scale, scale, scale)
+        assert np.array_equal(got, ref)

@@ -464,6 +464,40 @@ def run_mixed(args):
         k, ms = pa.trace_read(n)
         per[n] = round(ms / k * 1e3, 2) if k else None
     pa.trace_enable(False)
+    # The same step over an FP8 cache (pools converted on the device with torch's float8_e4m3fn
+    # cast after a clamp to +-448: input preparation, outside the timed region).
+    ks, vs = 6.0 / 448.0, 5.5 / 448.0
+    kc8 = (kc.float() / ks).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc8 = (vc.float() / vs).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    pre8 = dict(pre_args, key_cache=kc8, value_cache=vc8, k_scale=ks, v_scale=vs)
+    dec8 = dict(dec_args, key_cache=kc8, value_cache=vc8, k_scale=ks, v_scale=vs)
+
+    def fp8_serial():
+        pa.reshape_and_cache_fp8(rk, rv, kc8, vc8, slots, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                                 k_scale=ks, v_scale=vs)
+        pa.prefill_chunk_fp8(**pre8)
+        pa.decode_fp8(**dec8)
+
+    def fp8_overlapped():
+        pa.reshape_and_cache_fp8(rk, rv, kc8, vc8, slots, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                                 k_scale=ks, v_scale=vs)
+        pa.mixed_step(pre8, dec8, side_stream=side, fp8=True)
+
+    ms8_serial = timed(fp8_serial)
+    ms8_overlap = timed(fp8_overlapped)
+    pa.trace_enable(True)
+    for n in names:
+        pa.trace_read(n)
+    for _ in range(args.mixed_steps):
+        fp8_serial()
+    torch.cuda.synchronize()
+    per8 = {}
+    for n in names:
+        k, ms = pa.trace_read(n)
+        per8[n] = round(ms / k * 1e3, 2) if k else None
+    pa.trace_enable(False)
+    del kc8, vc8
+
     flops = prefill_flops(pf.query_start_loc, pf.seq_lens, Hq, D)
     pre_us = per["prefill_chunk"]
     tflops = flops / (pre_us * 1e-6) / 1e12
@@ -482,6 +516,9 @@ def run_mixed(args):
                              "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                              "flops_per_launch": flops},
         "decode_gbs": round(dbytes / (per["decode_partition"] * 1e-6) / 1e9, 1),
+        "fp8": {"us_per_step_serial": round(ms8_serial * 1e3, 2),
+                "us_per_step_overlapped": round(ms8_overlap * 1e3, 2), "kernel_us": per8,
+                "prefill_tflops": round(flops / (per8["prefill_chunk"] * 1e-6) / 1e12, 1)},
         "reshape_gbs": round(rbytes / (per["reshape_and_cache"] * 1e-6) / 1e9, 1),
         "reshape_bytes": rbytes, "decode_bytes": dbytes,
     }

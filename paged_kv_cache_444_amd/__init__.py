@@ -322,7 +322,7 @@ def prefill_chunk(query: torch.Tensor, key_cache: torch.Tensor, value_cache: tor
 _side_streams = {}
 
 
-def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None):
+def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None, fp8: bool = False):
     """One chunked-prefill batch step: the prefill chunk and the decode of the other sequences run
     side by side on two streams, so decode's HBM-bound work overlaps the matrix-core-bound chunk.
 
@@ -332,7 +332,8 @@ def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None):
     Decode is launched first, on `side_stream` (default: one stream per device, kept for reuse),
     so its workgroups are resident before the prefill chunk's fill the remaining room.  Returns
     (prefill output, decode output); the results are those of the two calls made one after the
-    other.
+    other.  With `fp8` the halves are prefill_chunk_fp8 and decode_fp8 (the dicts then carry the
+    uint8 pools and k_scale / v_scale).
     """
     main = torch.cuda.current_stream()
     if side_stream is None:
@@ -342,8 +343,8 @@ def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None):
             side_stream = _side_streams[dev] = torch.cuda.Stream(device=dev)
     side_stream.wait_stream(main)
     with torch.cuda.stream(side_stream):
-        dout = decode(**decode_call)
-    pout = prefill_chunk(**prefill)
+        dout = (decode_fp8 if fp8 else decode)(**decode_call)
+    pout = (prefill_chunk_fp8 if fp8 else prefill_chunk)(**prefill)
     main.wait_stream(side_stream)
     # The decode output (and a caller's tensors) are used on the current stream from here on.
     dout.record_stream(main)

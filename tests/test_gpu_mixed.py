@@ -58,3 +58,41 @@ def test_overlapped_mixed_step_equals_serial_and_oracle():
     ref_p = oracle.prefill_chunk(p.query, okc, ovc, p.block_tables, p.query_start_loc, p.seq_lens,
                                  Hkv, D, bs, case.scale, rows=rows)
     assert_close(upcast(serial_p)[rows], ref_p, "prefill in the mixed step")
+
+
+def test_overlapped_mixed_step_fp8_equals_serial_and_oracle():
+    """The same mixed step over an FP8 cache quantised by the oracle (chunk tokens included)."""
+    from helpers import dev_u8, oracle_quantize_pool
+
+    case = cached_named_case(4)
+    p, d = case.prefill, case.decode
+    Hkv, D, bs = case.num_kv_heads, case.head_dim, case.block_size
+    ks, vs = 6.0 / 448.0, 5.5 / 448.0
+    okc, ovc = cached_oracle_pools(4)
+    kc8, vc8 = oracle_quantize_pool(okc, ks), oracle_quantize_pool(ovc, vs)
+    say(f"mixed step fp8: {case.name}")
+    gk, gv = dev_u8(kc8), dev_u8(vc8)
+    pre = dict(query=dev_u16(p.query), key_cache=gk, value_cache=gv,
+               block_tables=dev_i32(p.block_tables), query_start_loc=dev_i32(p.query_start_loc),
+               seq_lens=dev_i32(p.seq_lens), num_kv_heads=Hkv, block_size=bs,
+               max_q_len=p.max_q_len, max_seq_len=p.max_seq_len, scale=float(case.scale),
+               k_scale=ks, v_scale=vs)
+    dec = dict(query=dev_u16(d.query), key_cache=gk, value_cache=gv,
+               block_tables=dev_i32(d.block_tables), seq_lens=dev_i32(d.seq_lens),
+               num_kv_heads=Hkv, block_size=bs, scale=float(case.scale),
+               max_seq_len=d.max_seq_len, k_scale=ks, v_scale=vs)
+    serial_p = host_u16(pa.prefill_chunk_fp8(**pre))
+    serial_d = host_u16(pa.decode_fp8(**dec))
+    for rep in range(2):
+        pout, dout = pa.mixed_step(pre, dec, fp8=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(pout), serial_p), f"prefill differs (repeat {rep})"
+        assert np.array_equal(host_u16(dout), serial_d), f"decode differs (repeat {rep})"
+    seqs = [0, 70, 126]
+    ref_d = oracle.decode_fp8(d.query, kc8, vc8, d.block_tables, d.seq_lens, Hkv, D, bs,
+                              case.scale, ks, vs, seqs=seqs)
+    assert_close(upcast(serial_d)[seqs], ref_d[seqs], "FP8 decode in the mixed step")
+    rows = [0, 511]
+    ref_p = oracle.prefill_chunk_fp8(p.query, kc8, vc8, p.block_tables, p.query_start_loc,
+                                     p.seq_lens, Hkv, D, bs, case.scale, ks, vs, rows=rows)
+    assert_close(upcast(serial_p)[rows], ref_p, "FP8 prefill in the mixed step")

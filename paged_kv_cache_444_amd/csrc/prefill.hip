@@ -31,6 +31,7 @@
 // prefill_merge combines them in split order.  With one split the output is written directly.
 
 #include "pa_device.h"
+#include "cascade.h"
 #include "pa_internal.h"
 
 #include <algorithm>
@@ -607,8 +608,10 @@ int resident_per_cu(int head_dim, int group) {
 
 }  // namespace
 
-PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int group, int head_dim,
-                           int max_seq_len) {
+namespace {
+
+PrefillSplit split_for(int num_seqs, int max_q_len, int num_kv_heads, int group, int head_dim,
+                       int max_seq_len, bool one_per_cu) {
   PrefillSplit r{1, std::max(max_seq_len, 1)};
   if (num_seqs <= 0 || max_q_len <= 0 || max_seq_len <= 0) return r;
   // One range's table slice must fit the LDS copy (kMaxTableLds entries of 16-token blocks).
@@ -619,7 +622,9 @@ PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int gr
   const long long base = (long long)((max_q_len + tq - 1) / tq) * num_kv_heads * num_seqs;
   // Enough workgroups for one round of every CU's resident slots (more rounds only add merge
   // work), each range at least 256 keys, at most 16 ranges.
-  const long long slots = (long long)resident_per_cu(head_dim, group) * cu_count();
+  // one_per_cu: a bandwidth-bound chunk (few query rows over a long context) gains nothing from a
+  // second resident round, and every extra range adds merge traffic.
+  const long long slots = (long long)(one_per_cu ? 1 : resident_per_cu(head_dim, group)) * cu_count();
   long long want = (slots + base - 1) / base;
   if (const char* e = std::getenv("PA_PREFILL_SPLITS"); e && *e) want = std::atoi(e);
   want = std::min<long long>(std::max<long long>(want, 1), 16);
@@ -631,6 +636,18 @@ PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int gr
   r.split_keys = keys;
   r.splits = (max_seq_len + keys - 1) / keys;
   return r;
+}
+
+}  // namespace
+
+PrefillSplit prefill_split(int num_seqs, int max_q_len, int num_kv_heads, int group, int head_dim,
+                           int max_seq_len) {
+  return split_for(num_seqs, max_q_len, num_kv_heads, group, head_dim, max_seq_len, false);
+}
+
+PrefillSplit prompt_split(int num_groups, int max_group_size, int num_kv_heads, int group,
+                          int head_dim, int prefix_len) {
+  return split_for(num_groups, max_group_size, num_kv_heads, group, head_dim, prefix_len, true);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {

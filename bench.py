@@ -240,7 +240,6 @@ def main():
     if not args.no_fp8:
         fp8 = run_fp8_decode(args, case, pools, q, bt, sl, out, ws, ms_per_step, main_ms)
     n_pools = len(pools)
-    ceiling = stream_read_ceiling()
     mixed = None
     if not args.no_mixed:
         del pools, kc0, vc0
@@ -292,8 +291,6 @@ def main():
             "ms_per_step_with_events": round((t3 - t2) * 1e3 / args.steps, 5),
         },
         "warm_single_pool_us_per_step": None if warm_us is None else round(warm_us, 2),
-        "stream_read_ceiling": dict(ceiling, decode_kernel_frac=round(main_gbs / ceiling["gbs"], 4),
-                                    decode_call_frac=round(gbs / ceiling["gbs"], 4)),
         "fp8_decode": fp8,
         "mixed_step": mixed,
         "cow_step": cow,
@@ -301,28 +298,6 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
-
-
-def stream_read_ceiling(gib=4, reps=10):
-    """A plain streaming read of known size on the same GPU: torch's float32 sum over `gib` GiB
-    (one pass, contiguous).  The rate it reaches is the practical read ceiling the decode kernel
-    is compared against, beside the 8 TB/s spec."""
-    import torch
-
-    x = torch.ones((gib << 30) // 4, dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        x.sum()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        x.sum()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
-    n = x.numel() * 4
-    del x
-    torch.cuda.empty_cache()
-    return {"kernel": "torch float32 sum (contiguous read)", "bytes": n, "us": round(dt * 1e6, 1),
-            "gbs": round(n / dt / 1e9, 1)}
 
 
 def fp8_decode_bytes(seq_lens, Hq, Hkv, D, bs):

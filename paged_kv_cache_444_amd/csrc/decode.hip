@@ -37,11 +37,11 @@
 // The next step's K and V are loaded into a second register set while the current step is
 // computed.
 //
-// FP8 cache.  Pools of E4M3 codes keep the bf16 element order with one byte per element, so every
-// lane loads the same elements as above with 8-byte instead of 16-byte loads, and widens them to
-// bf16 pairs (v_cvt_scalef32_pk_bf16_fp8 with scale 1, exact: every E4M3 value is a bf16 value)
-// before the same step arithmetic.  The K scale is folded into the softmax scale and the V scale
-// multiplies each output row, so the codes are never rescaled one by one.
+// FP8 cache.  Pools of E4M3 codes keep the bf16 element order with one byte per element; their
+// steps run on the matrix cores (see the matrix-core step below), widening the codes to bf16
+// pairs (v_cvt_scalef32_pk_bf16_fp8 with scale 1, exact: every E4M3 value is a bf16 value).  The
+// K scale is folded into the softmax scale and the V scale multiplies each output row, so the
+// codes are never rescaled one by one.
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -121,11 +121,10 @@ struct Plan {
 // with three DPP adds.  Load (p, x) of the wave covers rows 8p .. 8p+7 of slices 2x and 2x+1:
 // two 512-byte runs of whole cache lines.  V-side: lane l holds head-dim rows l%32 + 32x of
 // octet l/32, so load x is 1 KB contiguous.
-template <int D, bool Fp8 = false>
+template <int D>
 struct StepRegs {
-  using T = std::conditional_t<Fp8, uint2, uint4>;  // 8 elements: bf16 or E4M3 codes
-  T k[2][D / 64];
-  T v[D / kSlice];
+  uint4 k[2][D / 64];
+  uint4 v[D / kSlice];
 };
 
 // Eight E4M3 codes -> eight bf16 values, same order (two per conversion).
@@ -136,21 +135,6 @@ __device__ __forceinline__ uint32_t fp8_pair_to_bf16(uint32_t w) {
 __device__ __forceinline__ uint4 widen8(const uint2& w) {
   return make_uint4(fp8_pair_to_bf16<false>(w.x), fp8_pair_to_bf16<true>(w.x),
                     fp8_pair_to_bf16<false>(w.y), fp8_pair_to_bf16<true>(w.y));
-}
-template <int D>
-__device__ __forceinline__ const StepRegs<D>& as_bf16(const StepRegs<D>& r) {
-  return r;
-}
-template <int D>
-__device__ __forceinline__ StepRegs<D> as_bf16(const StepRegs<D, true>& r) {
-  StepRegs<D> o;
-#pragma unroll
-  for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-    for (int x = 0; x < D / 64; ++x) o.k[pp][x] = widen8(r.k[pp][x]);
-#pragma unroll
-  for (int x = 0; x < D / kSlice; ++x) o.v[x] = widen8(r.v[x]);
-  return o;
 }
 
 // Query heads a lane computes probabilities for: heads c + 8j (j < kOwn) of the G sharing the
@@ -214,14 +198,14 @@ __device__ __forceinline__ uint2 load8(const uint8_t* ptr) {
 }
 // Eight elements at element offset `off` of a pool: 16 bytes of bf16 or 8 bytes of codes.
 template <bool Stream, bool Fp8>
-__device__ __forceinline__ typename StepRegs<64, Fp8>::T load_elems(const uint16_t* pool,
-                                                                    size_t off) {
+__device__ __forceinline__ std::conditional_t<Fp8, uint2, uint4> load_elems(const uint16_t* pool,
+                                                                            size_t off) {
   if constexpr (Fp8) return load8<Stream>(reinterpret_cast<const uint8_t*>(pool) + off);
   else return load16<Stream>(pool + off);
 }
 
-template <int D, bool Stream, bool Fp8>
-__device__ __forceinline__ void load_step(StepRegs<D, Fp8>& r, int i, const DecodeParams& p,
+template <int D, bool Stream>
+__device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodeParams& p,
                                           const int* bt, int& win, int& ids,
                                           size_t head_off, size_t block_elems) {
   constexpr int R = D / kSlice;
@@ -242,13 +226,13 @@ __device__ __forceinline__ void load_step(StepRegs<D, Fp8>& r, int i, const Deco
 #pragma unroll
     for (int x = 0; x < D / 64; ++x) {
       const int d = 8 * c + 64 * x;
-      r.k[pp][x] = load_elems<Stream, Fp8>(
-          p.kpool, off + (d >> 5) * (kSub * kSlice) + (8 * pp + tt) * kSlice + (d & 31));
+      r.k[pp][x] = load16<Stream>(p.kpool + off + (d >> 5) * (kSub * kSlice) +
+                                  (8 * pp + tt) * kSlice + (d & 31));
     }
   const int vd = lane & 31, vo = lane >> 5;
 #pragma unroll
   for (int x = 0; x < R; ++x)
-    r.v[x] = load_elems<Stream, Fp8>(p.vpool, off + (vd + 32 * x) * kSub + 8 * vo);
+    r.v[x] = load16<Stream>(p.vpool + off + (vd + 32 * x) * kSub + 8 * vo);
 }
 
 // One 16-token step: scores, online softmax, P·V.  nvalid = tokens of the step inside the piece
@@ -379,7 +363,7 @@ __device__ __forceinline__ void compute_step(const StepRegs<D>& r, const uint4 (
 // Depth is the number of steps whose loads are in flight while one step is computed.  With
 // `coop` set the wave's (m, l, acc) always goes to `coop` (its slot in LDS) and the workgroup
 // combines the slots; otherwise the piece is finished here.
-template <int D, int G, int Depth, bool Stream, bool Fp8>
+template <int D, int G, int Depth, bool Stream>
 __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h, int j0, int take,
                                              int n_s, long long w, long long x, long long jn,
                                              const Plan& plan, uint16_t (*p_sh)[G][8],
@@ -446,35 +430,35 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   int i = j0;
   if constexpr (Depth == 0) {  // no prefetch: fewer registers, more resident waves
     while (true) {
-      StepRegs<D, Fp8> ra;
-      load_step<D, Stream, Fp8>(ra, i, p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(as_bf16<D>(ra), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      StepRegs<D> ra;
+      load_step<D, Stream>(ra, i, p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else if constexpr (Depth == 1) {
-    StepRegs<D, Fp8> ra, rb;
-    load_step<D, Stream, Fp8>(ra, i, p, bt, win, ids, head_off, block_elems);
+    StepRegs<D> ra, rb;
+    load_step<D, Stream>(ra, i, p, bt, win, ids, head_off, block_elems);
     while (true) {
-      load_step<D, Stream, Fp8>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(as_bf16<D>(ra), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D, Stream, Fp8>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(as_bf16<D>(rb), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(rb, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else {  // two steps in flight while one is computed
-    StepRegs<D, Fp8> r0, r1, r2;
-    load_step<D, Stream, Fp8>(r0, i, p, bt, win, ids, head_off, block_elems);
-    load_step<D, Stream, Fp8>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+    StepRegs<D> r0, r1, r2;
+    load_step<D, Stream>(r0, i, p, bt, win, ids, head_off, block_elems);
+    load_step<D, Stream>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
     while (true) {
-      load_step<D, Stream, Fp8>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(as_bf16<D>(r0), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(r0, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D, Stream, Fp8>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(as_bf16<D>(r1), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(r1, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D, Stream, Fp8>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
-      compute_step<D, G>(as_bf16<D>(r2), q, tok_end - i * kSub, c, slack_raw, p_sh, st);
+      load_step<D, Stream>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      compute_step<D, G>(r2, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   }
@@ -580,7 +564,8 @@ __device__ __forceinline__ void load_mstep(MStepRegs<D, Fp8>& r, int i, const De
   const int r16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
   for (int sl = 0; sl < D / kSlice; ++sl)
-    r.k[sl] = load_elems<Stream, Fp8>(p.kpool, off + sl * (kSub * kSlice) + r16 * kSlice + 8 * q4);
+    r.k[sl] =
+        load_elems<Stream, Fp8>(p.kpool, off + sl * (kSub * kSlice) + r16 * kSlice + 8 * q4);
 #pragma unroll
   for (int m = 0; m < D / kSub; ++m) {
     const size_t e = off + (size_t)(kSub * m + r16) * kSub + 4 * q4;
@@ -738,15 +723,16 @@ __device__ __forceinline__ void decode_piece_mfma(const DecodeParams& p, int s, 
   float* slot = coop ? coop : p.partials + slot_of(p, w, u) * (G * (2 + D));
   uint16_t* orow = p.out + ((size_t)s * Hq + (size_t)h * G + g) * D;
   if (whole && p.state_ml) {
-    const size_t u = state_slot(p, (size_t)s * Hq + (size_t)h * G + g);
+    const size_t su = state_slot(p, (size_t)s * Hq + (size_t)h * G + g);
     if (q4 == 0) {
-      p.state_ml[2 * u] = st.m * c;
-      p.state_ml[2 * u + 1] = lt;
+      p.state_ml[2 * su] = st.m * c;
+      p.state_ml[2 * su + 1] = lt;
     }
 #pragma unroll
     for (int m = 0; m < D / kSub; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p.state_acc[u * D + kSub * m + 4 * q4 + e] = st.acc[m][e] * p.v_scale;
+      for (int e = 0; e < 4; ++e)
+        p.state_acc[su * D + kSub * m + 4 * q4 + e] = st.acc[m][e] * p.v_scale;
     return;
   }
   if (whole) {
@@ -788,8 +774,8 @@ __device__ __forceinline__ void coop_piece(const DecodeParams& p, int s, int h, 
       decode_piece_mfma<D, G, Depth, Stream, Fp8>(p, s, h, a, b - a, n_s, w, x + (a - j0), jn,
                                                   plan, st[wave]);
     else
-      decode_piece<D, G, Depth, Stream, Fp8>(p, s, h, a, b - a, n_s, w, x + (a - j0), jn, plan,
-                                             p_sh, st[wave]);
+      decode_piece<D, G, Depth, Stream>(p, s, h, a, b - a, n_s, w, x + (a - j0), jn, plan, p_sh,
+                                        st[wave]);
   }
   __syncthreads();
   const int u = s * p.num_kv_heads + h;
@@ -861,8 +847,8 @@ __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& pl
       decode_piece_mfma<D, G, Depth, Stream, Fp8>(
           p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h, j, take, n_s, v, x, jn, plan);
     else
-      decode_piece<D, G, Depth, Stream, Fp8>(p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h,
-                                             j, take, n_s, v, x, jn, plan, p_sh);
+      decode_piece<D, G, Depth, Stream>(p, s, quad ? h * kWaves + (int)(threadIdx.x >> 6) : h, j,
+                                        take, n_s, v, x, jn, plan, p_sh);
     x += take;
     if (x >= x1) break;
     j = 0;
@@ -1032,9 +1018,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     constexpr bool S = decltype(stream)::value;
     const int k = quad ? 0 : wave;
     if (w < plan.ns)
-      run_worker<D, G, Depth, S, Fp8, Mfma>(p, plan, w, sh_start_s[k], sh_start_off[k], sh_start_j[k],
-                                      sh_start_x[k], sh_start_x[k + 1], p_lds[wave], nullptr,
-                                      quad);
+      run_worker<D, G, Depth, S, Fp8, Mfma>(p, plan, w, sh_start_s[k], sh_start_off[k],
+                                            sh_start_j[k], sh_start_x[k], sh_start_x[k + 1],
+                                            p_lds[wave], nullptr, quad);
     if (!dynamic) return;  // block-uniform
 
     // Dynamic chunks, each shared by the whole workgroup (one counter increment per chunk; the

@@ -83,3 +83,20 @@ def test_cascade_groups_tails_and_edges(Hq, Hkv, D, bs):
                       max_seq_len=d.max_seq_len)
     torch.cuda.synchronize()
     assert_close(upcast(host_u16(plain)), ref, "plain decode")
+
+
+def test_cascade_all_tails_empty_and_table_exactly_the_prompt():
+    """Every sequence is exactly its shared prompt and the table is exactly that wide: the tail
+    decode has no keys and no table columns left, so every row is the prompt's attention."""
+    P, bs = 64, 16
+    groups = [(0, 4), (4, 6)]
+    case = build_case(Spec(name="cascade", num_q_heads=8, num_kv_heads=2, head_dim=64,
+                           block_size=bs, seed=(444, 83), decode_lens=[P] * 6,
+                           share_groups=[(list(range(a, b)), P) for a, b in groups]))
+    d = case.decode
+    assert d.block_tables.shape[1] == P // bs
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    got = upcast(_cascade(case, kc, vc, [0, 4, 6], P))
+    ref = oracle.decode(d.query, case.key_cache, case.value_cache, d.block_tables, d.seq_lens, 2,
+                        64, bs, case.scale)
+    assert_close(got, ref, "cascade with empty tails")

@@ -104,7 +104,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over the whole batch until this much CPU time is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["decode", "copy", "mixed", "cow", "prefix"], default="decode")
+    ap.add_argument("--mode", choices=["decode", "copy", "mixed", "cow", "prefix", "configs"],
+                    default="decode")
     ap.add_argument("--mixed-steps", type=int, default=30)
     ap.add_argument("--mixed-warmup", type=int, default=60)
     ap.add_argument("--mixed-order", choices=["decode-first", "prefill-first"], default="decode-first",
@@ -163,6 +164,9 @@ def main():
         return
     if args.mode == "prefix":
         print(json.dumps(run_prefix_shared(args)), flush=True)
+        return
+    if args.mode == "configs":
+        print(json.dumps(run_configs(args)), flush=True)
         return
 
     import paged_kv_cache_444_amd as pa
@@ -692,6 +696,63 @@ def run_prefix_shared(args):
         "cascade_logical_gbs": round(logical / (best_c * 1e-6) / 1e9, 1),
         "plain_logical_gbs": round(logical / (best_p * 1e-6) / 1e9, 1),
     }
+
+
+def run_configs(args):
+    """Decode kernel time on each named decode workload (tiny; 70B shape; wide-head; prefix-shared,
+    plain decode), one pool per workload, after its new tokens are written: per-call kernel
+    time from HIP events and algorithmic GB/s.  Context for the parity workloads, not the metric."""
+    import torch
+
+    import paged_kv_cache_444_amd as pa
+    from workloads import named_case
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    res = {}
+    for cfg in (1, 2, 3, 5):
+        case = named_case(cfg)
+        Hq, Hkv, D, bs = case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+        d = case.decode
+        log(f"configs: {case.name}")
+        kc, vc = dev(case.key_cache), dev(case.value_cache)
+        if case.reshape is not None:
+            r = case.reshape
+            pa.reshape_and_cache(dev(r.key), dev(r.value), kc, vc,
+                                 torch.from_numpy(r.slot_mapping).cuda(), num_kv_heads=Hkv,
+                                 head_dim=D, block_size=bs)
+        q, bt, sl = dev(d.query), torch.from_numpy(d.block_tables).cuda(), torch.from_numpy(d.seq_lens).cuda()
+        out = torch.empty_like(q)
+        ws = torch.zeros(max(pa.decode_workspace_bytes(d.num_seqs, Hq, Hkv, D, d.max_seq_len), 1),
+                         dtype=torch.uint8, device="cuda")
+
+        def step():
+            pa.decode(q, kc, vc, bt, sl, num_kv_heads=Hkv, block_size=bs, scale=float(case.scale),
+                      max_seq_len=d.max_seq_len, out=out, workspace=ws)
+
+        for _ in range(30):
+            step()
+        torch.cuda.synchronize()
+        pa.trace_enable(True)
+        pa.trace_read("decode_partition")
+        pa.trace_read("decode_merge")
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+        n, ms = pa.trace_read("decode_partition")
+        nm, msm = pa.trace_read("decode_merge")
+        pa.trace_enable(False)
+        us = ms / n * 1e3
+        nbytes = decode_bytes(d.seq_lens, Hq, Hkv, D, bs)
+        res[case.name] = {"kernel_us": round(us, 2), "merge_us": round(msm / max(nm, 1) * 1e3, 2),
+                          "algorithmic_bytes": nbytes,
+                          "kernel_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        del kc, vc
+        torch.cuda.empty_cache()
+    return {"mode": "configs", "note": "one pool per workload (no cycling of copies)",
+            "workloads": res}
 
 
 def cpu_baseline(case, budget_s):

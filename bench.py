@@ -652,9 +652,11 @@ def run_prefix_shared(args):
     def plain():
         pa.decode(q, kc, vc, bt, sl, workspace=ws, **kw)
 
+    pl = torch.full((d.num_seqs,), 4096, dtype=torch.int32, device="cuda")
+
     def cascade():
-        pa.decode_cascade(q, kc, vc, bt, sl, gs, prefix_len=4096, max_group_size=16, workspace=cws,
-                          **kw)
+        pa.decode_cascade(q, kc, vc, bt, sl, gs, pl, max_prefix_len=4096, max_group_size=16,
+                          workspace=cws, **kw)
 
     def timed(fn):
         for _ in range(20):

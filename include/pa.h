@@ -202,13 +202,14 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const void* key_cache,
  * combined.
  *
  *   group_start    int32 [num_groups+1]: group i is sequences group_start[i] .. group_start[i+1]-1,
- *                  group_start[0] == 0, group_start[num_groups] == num_seqs, non-decreasing;
- *                  a sequence that shares nothing can be a group of one
+ *                  group_start[0] == 0, group_start[num_groups] == num_seqs, non-decreasing
+ *   prefix_lens    int32 [num_seqs]: tokens a sequence shares with its group, a multiple of
+ *                  block_size (0: nothing shared), the same for every member of a group and
+ *                  <= that sequence's seq_lens entry; members' first prefix_len / block_size table
+ *                  entries must be those of the group's first member (otherwise results are
+ *                  unspecified, never an access outside the buffers)
  *   max_group_size host-side bound of every group's size (1 <= max_group_size <= num_seqs)
- *   prefix_len     tokens shared within every group: a positive multiple of block_size,
- *                  <= max_seq_len; every member's first prefix_len / block_size table entries
- *                  must be those of its group's first member, and every seq_lens entry must be
- *                  >= prefix_len (otherwise results are unspecified)
+ *   max_prefix_len host-side bound of prefix_lens (0 <= max_prefix_len <= max_seq_len)
  *   workspace      at least pa_decode_cascade_workspace_bytes(...) bytes, 256-byte aligned,
  *                  zero-filled before its first use and reusable by later calls on one stream
  * Other arguments, limits and errors as pa_decode (bf16 pools).  Outputs are fp32-accumulated and
@@ -217,15 +218,31 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const void* key_cache,
 size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_groups,
                                          int32_t max_group_size, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim,
-                                         int32_t prefix_len);
+                                         int32_t max_prefix_len);
 pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache,
                               const void* value_cache, int64_t num_blocks,
                               const int32_t* block_tables, const int32_t* seq_lens,
-                              const int32_t* group_start, int32_t num_seqs, int32_t num_groups,
-                              int32_t max_group_size, int32_t prefix_len, int32_t num_q_heads,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                              int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              const int32_t* group_start, const int32_t* prefix_lens,
+                              int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                              int32_t max_prefix_len, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_cascade_fp8 — pa_decode_cascade over FP8 pools (pa_reshape_and_cache_fp8, same
+ * k_scale and v_scale): the result of pa_decode_fp8.  Same workspace size query.
+ */
+pa_status_t pa_decode_cascade_fp8(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, int64_t num_blocks,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens,
+                                  int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                                  int32_t max_prefix_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                                  float k_scale, float v_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of workspace pa_prefill_chunk needs for this batch shape on the current device; 0 means

@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "load_library", "reshape_and_cache", "reshape_and_cache_fp8", "copy_blocks", "decode",
-    "decode_fp8", "decode_cascade", "decode_cascade_workspace_bytes", "prefill_chunk",
+    "decode_fp8", "decode_cascade", "decode_cascade_fp8", "decode_cascade_workspace_bytes",
+    "prefill_chunk",
     "prefill_chunk_fp8",
     "mixed_step", "decode_workspace_bytes", "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
     "LIB_PATH",
@@ -51,8 +52,11 @@ _SIGNATURES = {
     "pa_decode_fp8": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                              ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _SZ, _P]),
     "pa_decode_cascade_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
-    "pa_decode_cascade": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+    "pa_decode_cascade": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                  _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _SZ, _P]),
+    "pa_decode_cascade_fp8": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                     _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
+                                     ctypes.c_float, ctypes.c_float, _P, _SZ, _P]),
     "pa_copy_blocks": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _P]),
     "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pa_decode": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -255,20 +259,15 @@ def decode_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.
 
 def decode_cascade_workspace_bytes(num_seqs: int, num_groups: int, max_group_size: int,
                                    num_q_heads: int, num_kv_heads: int, head_dim: int,
-                                   prefix_len: int) -> int:
+                                   max_prefix_len: int) -> int:
     """Workspace bytes pa_decode_cascade needs on the current device (0 for unsupported shapes)."""
     return int(load_library().pa_decode_cascade_workspace_bytes(
-        num_seqs, num_groups, max_group_size, num_q_heads, num_kv_heads, head_dim, prefix_len))
+        num_seqs, num_groups, max_group_size, num_q_heads, num_kv_heads, head_dim, max_prefix_len))
 
 
-def decode_cascade(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
-                   block_tables: torch.Tensor, seq_lens: torch.Tensor, group_start: torch.Tensor, *,
-                   prefix_len: int, max_group_size: int, num_kv_heads: int, block_size: int,
-                   scale: Optional[float] = None, max_seq_len: Optional[int] = None,
-                   out: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Decode of groups of sequences sharing their first `prefix_len` tokens' blocks (group i is
-    sequences group_start[i] .. group_start[i+1]-1): the same result as `decode`."""
+def _cascade(fp8: bool, query, key_cache, value_cache, block_tables, seq_lens, group_start,
+             prefix_lens, *, max_prefix_len, max_group_size, num_kv_heads, block_size, scale,
+             max_seq_len, out, workspace, k_scale=1.0, v_scale=1.0):
     lib = load_library()
     B, Hq, D = query.shape
     n_groups = group_start.numel() - 1
@@ -279,18 +278,53 @@ def decode_cascade(query: torch.Tensor, key_cache: torch.Tensor, value_cache: to
     if out is None:
         out = torch.empty_like(query)
     nbytes = decode_cascade_workspace_bytes(B, n_groups, max_group_size, Hq, num_kv_heads, D,
-                                            prefix_len)
+                                            max_prefix_len)
     ws, ws_bytes = _workspace(nbytes, workspace, query.device)
-    n = _num_blocks(key_cache, num_kv_heads, block_size, D)
-    _check(lib.pa_decode_cascade(_bf16(out, "out"), _bf16(query, "query"), _bf16(key_cache, "key_cache"),
-                                 _bf16(value_cache, "value_cache"), n,
-                                 _ints(block_tables, torch.int32, "block_tables"),
-                                 _ints(seq_lens, torch.int32, "seq_lens"),
-                                 _ints(group_start, torch.int32, "group_start"), B, n_groups,
-                                 max_group_size, prefix_len, Hq, num_kv_heads, D, block_size,
-                                 block_tables.shape[1], max_seq_len, float(scale), ws, ws_bytes,
-                                 _stream()))
+    pools = ((_fp8_pool(key_cache, "key_cache"), _fp8_pool(value_cache, "value_cache")) if fp8 else
+             (_bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache")))
+    n = (_num_blocks_fp8 if fp8 else _num_blocks)(key_cache, num_kv_heads, block_size, D)
+    args = [_bf16(out, "out"), _bf16(query, "query"), *pools, n,
+            _ints(block_tables, torch.int32, "block_tables"), _ints(seq_lens, torch.int32, "seq_lens"),
+            _ints(group_start, torch.int32, "group_start"),
+            _ints(prefix_lens, torch.int32, "prefix_lens"), B, n_groups, max_group_size,
+            max_prefix_len, Hq, num_kv_heads, D, block_size, block_tables.shape[1], max_seq_len,
+            float(scale)]
+    if fp8:
+        _check(lib.pa_decode_cascade_fp8(*args, float(k_scale), float(v_scale), ws, ws_bytes,
+                                         _stream()))
+    else:
+        _check(lib.pa_decode_cascade(*args, ws, ws_bytes, _stream()))
     return out
+
+
+def decode_cascade(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                   block_tables: torch.Tensor, seq_lens: torch.Tensor, group_start: torch.Tensor,
+                   prefix_lens: torch.Tensor, *, max_prefix_len: int, max_group_size: int,
+                   num_kv_heads: int, block_size: int, scale: Optional[float] = None,
+                   max_seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode of groups of sequences sharing the blocks of their first prefix_lens[s] tokens
+    (group i is sequences group_start[i] .. group_start[i+1]-1): the same result as `decode`."""
+    return _cascade(False, query, key_cache, value_cache, block_tables, seq_lens, group_start,
+                    prefix_lens, max_prefix_len=max_prefix_len, max_group_size=max_group_size,
+                    num_kv_heads=num_kv_heads, block_size=block_size, scale=scale,
+                    max_seq_len=max_seq_len, out=out, workspace=workspace)
+
+
+def decode_cascade_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                       block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                       group_start: torch.Tensor, prefix_lens: torch.Tensor, *,
+                       max_prefix_len: int, max_group_size: int, num_kv_heads: int,
+                       block_size: int, k_scale: float, v_scale: float,
+                       scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+                       out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode_cascade over uint8 pools of E4M3 codes: the same result as `decode_fp8`."""
+    return _cascade(True, query, key_cache, value_cache, block_tables, seq_lens, group_start,
+                    prefix_lens, max_prefix_len=max_prefix_len, max_group_size=max_group_size,
+                    num_kv_heads=num_kv_heads, block_size=block_size, scale=scale,
+                    max_seq_len=max_seq_len, out=out, workspace=workspace, k_scale=k_scale,
+                    v_scale=v_scale)
 
 
 def prefill_chunk(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,

@@ -69,9 +69,15 @@ constexpr int kPrefixLdsBytes = (kMaxPrefixSeqs + 1) * 4;
 constexpr int kDynSlotsPerWorker = 2;
 constexpr int kBlocksPerCU = 1;
 
+// Whole blocks of sequence s left out at the front (a shared prefix attended elsewhere).
+__device__ __forceinline__ int skip_blocks(const DecodeParams& p, int s) {
+  if (!p.skip_lens) return 0;
+  return min(max(p.skip_lens[s], 0) / p.block_size, p.max_blocks_per_seq);
+}
+
 // Tokens of sequence s this call attends: its length, clamped, less the skipped prefix.
 __device__ __forceinline__ int clamped_len(const DecodeParams& p, int s) {
-  return max(min(max(p.seq_lens[s], 0), p.len_cap) - p.kv_skip, 0);
+  return max(min(max(p.seq_lens[s], 0), p.len_cap) - skip_blocks(p, s) * p.block_size, 0);
 }
 
 // Slot of (sequence, query head) row `row` in the prefill-layout state workspace.
@@ -206,7 +212,7 @@ __device__ __forceinline__ std::conditional_t<Fp8, uint2, uint4> load_elems(cons
 
 template <int D, bool Stream>
 __device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodeParams& p,
-                                          const int* bt, int& win, int& ids,
+                                          const int* bt, int cols, int& win, int& ids,
                                           size_t head_off, size_t block_elems) {
   constexpr int R = D / kSlice;
   const int lane = threadIdx.x & 63;
@@ -215,7 +221,7 @@ __device__ __forceinline__ void load_step(StepRegs<D>& r, int i, const DecodePar
   const int b = t0 >> (bs == 32 ? 5 : 4);
   if (b - win >= 64) {  // rare: refill the block-id window
     win = b;
-    const int id = (win + lane < p.table_cols) ? bt[win + lane] : 0;
+    const int id = (win + lane < cols) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const int id = __builtin_amdgcn_readlane(ids, b - win);
@@ -390,14 +396,17 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   }
 
   const int bs = p.block_size;
-  const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  // Table entries of the sequence from its first attended block on (after a skipped prefix).
+  const int skip_b = skip_blocks(p, s);
+  const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq + skip_b;
+  const int cols = p.max_blocks_per_seq - skip_b;
   const int tok_end = min(L, (j0 + take) * kSub);
   int win = (j0 * kSub) / bs;
   int ids;
   {
     // Read without waiting for the length: entries past the sequence's blocks are padding, and
     // the steps below only ever use the sequence's own blocks.
-    const int id = (win + lane < p.table_cols) ? bt[win + lane] : 0;
+    const int id = (win + lane < cols) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const size_t tile = (size_t)bs * D;
@@ -425,39 +434,42 @@ __device__ __forceinline__ void decode_piece(const DecodeParams& p, int s, int h
   // Prefetch loads are issued unconditionally (past the last step they repeat the last step's
   // addresses, which hit in cache): a load issued on only some paths would make the compiler
   // wait for every outstanding load before each step.
+  auto ld = [&](StepRegs<D>& r, int step) __attribute__((always_inline)) {
+    load_step<D, Stream>(r, step, p, bt, cols, win, ids, head_off, block_elems);
+  };
   const int iend = j0 + take;
   const int ilast = iend - 1;
   int i = j0;
   if constexpr (Depth == 0) {  // no prefetch: fewer registers, more resident waves
     while (true) {
       StepRegs<D> ra;
-      load_step<D, Stream>(ra, i, p, bt, win, ids, head_off, block_elems);
+      ld(ra, i);
       compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else if constexpr (Depth == 1) {
     StepRegs<D> ra, rb;
-    load_step<D, Stream>(ra, i, p, bt, win, ids, head_off, block_elems);
+    ld(ra, i);
     while (true) {
-      load_step<D, Stream>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(rb, min(i + 1, ilast));
       compute_step<D, G>(ra, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D, Stream>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(ra, min(i + 1, ilast));
       compute_step<D, G>(rb, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
   } else {  // two steps in flight while one is computed
     StepRegs<D> r0, r1, r2;
-    load_step<D, Stream>(r0, i, p, bt, win, ids, head_off, block_elems);
-    load_step<D, Stream>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+    ld(r0, i);
+    ld(r1, min(i + 1, ilast));
     while (true) {
-      load_step<D, Stream>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(r2, min(i + 2, ilast));
       compute_step<D, G>(r0, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D, Stream>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(r0, min(i + 2, ilast));
       compute_step<D, G>(r1, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
-      load_step<D, Stream>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(r1, min(i + 2, ilast));
       compute_step<D, G>(r2, q, tok_end - i * kSub, c, slack_raw, p_sh, st);
       if (++i >= iend) break;
     }
@@ -548,15 +560,15 @@ __device__ __forceinline__ uint2 load8_u16(const uint16_t* ptr) {
 
 template <int D, bool Stream, bool Fp8>
 __device__ __forceinline__ void load_mstep(MStepRegs<D, Fp8>& r, int i, const DecodeParams& p,
-                                           const int* bt, int& win, int& ids, size_t head_off,
-                                           size_t block_elems) {
+                                           const int* bt, int cols, int& win, int& ids,
+                                           size_t head_off, size_t block_elems) {
   const int lane = threadIdx.x & 63;
   const int bs = p.block_size;
   const int t0 = i * kSub;
   const int b = t0 >> (bs == 32 ? 5 : 4);
   if (b - win >= 64) {  // rare: refill the block-id window
     win = b;
-    const int id = (win + lane < p.table_cols) ? bt[win + lane] : 0;
+    const int id = (win + lane < cols) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const int id = __builtin_amdgcn_readlane(ids, b - win);
@@ -661,12 +673,15 @@ __device__ __forceinline__ void decode_piece_mfma(const DecodeParams& p, int s, 
   }
 
   const int bs = p.block_size;
-  const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  // Table entries of the sequence from its first attended block on (after a skipped prefix).
+  const int skip_b = skip_blocks(p, s);
+  const int* bt = p.block_tables + (size_t)s * p.max_blocks_per_seq + skip_b;
+  const int cols = p.max_blocks_per_seq - skip_b;
   const int tok_end = min(L, (j0 + take) * kSub);
   int win = (j0 * kSub) / bs;
   int ids;
   {
-    const int id = (win + lane < p.table_cols) ? bt[win + lane] : 0;
+    const int id = (win + lane < cols) ? bt[win + lane] : 0;
     ids = min(max(id, 0), (int)(p.num_blocks - 1));
   }
   const size_t tile = (size_t)bs * D;
@@ -684,32 +699,35 @@ __device__ __forceinline__ void decode_piece_mfma(const DecodeParams& p, int s, 
   for (int m = 0; m < D / kSub; ++m) st.acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Prefetch loads are issued unconditionally (past the last step they repeat its addresses).
+  auto ld = [&](MStepRegs<D, Fp8>& r, int step) __attribute__((always_inline)) {
+    load_mstep<D, Stream, Fp8>(r, step, p, bt, cols, win, ids, head_off, block_elems);
+  };
   const int iend = j0 + take;
   const int ilast = iend - 1;
   int i = j0;
   if constexpr (Depth <= 1) {
     MStepRegs<D, Fp8> ra, rb;
-    load_mstep<D, Stream, Fp8>(ra, i, p, bt, win, ids, head_off, block_elems);
+    ld(ra, i);
     while (true) {
-      load_mstep<D, Stream, Fp8>(rb, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(rb, min(i + 1, ilast));
       compute_mstep<D, Fp8>(ra, qb, tok_end - i * kSub, c, slack_raw, st);
       if (++i >= iend) break;
-      load_mstep<D, Stream, Fp8>(ra, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(ra, min(i + 1, ilast));
       compute_mstep<D, Fp8>(rb, qb, tok_end - i * kSub, c, slack_raw, st);
       if (++i >= iend) break;
     }
   } else {
     MStepRegs<D, Fp8> r0, r1, r2;
-    load_mstep<D, Stream, Fp8>(r0, i, p, bt, win, ids, head_off, block_elems);
-    load_mstep<D, Stream, Fp8>(r1, min(i + 1, ilast), p, bt, win, ids, head_off, block_elems);
+    ld(r0, i);
+    ld(r1, min(i + 1, ilast));
     while (true) {
-      load_mstep<D, Stream, Fp8>(r2, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(r2, min(i + 2, ilast));
       compute_mstep<D, Fp8>(r0, qb, tok_end - i * kSub, c, slack_raw, st);
       if (++i >= iend) break;
-      load_mstep<D, Stream, Fp8>(r0, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(r0, min(i + 2, ilast));
       compute_mstep<D, Fp8>(r1, qb, tok_end - i * kSub, c, slack_raw, st);
       if (++i >= iend) break;
-      load_mstep<D, Stream, Fp8>(r1, min(i + 2, ilast), p, bt, win, ids, head_off, block_elems);
+      ld(r1, min(i + 2, ilast));
       compute_mstep<D, Fp8>(r2, qb, tok_end - i * kSub, c, slack_raw, st);
       if (++i >= iend) break;
     }
@@ -903,8 +921,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // batch re-reads blocks, so its K/V loads stay ordinary; any other batch streams them.
   int shares = 0;
   const size_t row = (size_t)p.max_blocks_per_seq;
-  for (int s = threadIdx.x; s + 1 < B && p.table_cols > 0; s += kThreads)
-    shares |= p.block_tables[(size_t)s * row] == p.block_tables[(size_t)(s + 1) * row];
+  for (int s = threadIdx.x; s + 1 < B; s += kThreads) {
+    const int a = skip_blocks(p, s), b = skip_blocks(p, s + 1);  // first attended entries
+    if (a < (int)row && b < (int)row)
+      shares |= p.block_tables[(size_t)s * row + a] == p.block_tables[(size_t)(s + 1) * row + b];
+  }
   shares = __any(shares);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {

@@ -290,9 +290,9 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                         int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
                         bool fp8, float k_scale, float v_scale, void* workspace,
-                        size_t workspace_bytes, void* stream, int kv_skip = 0,
-                        float* state_ml = nullptr, float* state_acc = nullptr,
-                        int state_stride = 0, int state_split = 0) {
+                        size_t workspace_bytes, void* stream,
+                        const int32_t* skip_lens = nullptr, float* state_ml = nullptr,
+                        float* state_acc = nullptr, int state_stride = 0, int state_split = 0) {
   if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (fp8 && !std::isfinite(scale * k_scale))
@@ -324,10 +324,8 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
   p.query = static_cast<const uint16_t*>(query);
   p.kpool = static_cast<const uint16_t*>(key_cache);
   p.vpool = static_cast<const uint16_t*>(value_cache);
-  // A skipped prefix of kv_skip tokens (whole blocks) starts every row that many entries in.
-  p.kv_skip = kv_skip;
-  p.block_tables = block_tables + kv_skip / block_size;
-  p.table_cols = max_blocks_per_seq - kv_skip / block_size;
+  p.block_tables = block_tables;
+  p.skip_lens = skip_lens;  // per-sequence prefix left out (cascade), or none
   p.state_ml = state_ml;
   p.state_acc = state_acc;
   p.state_stride = state_stride;
@@ -424,49 +422,58 @@ extern "C" {
 size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_groups,
                                          int32_t max_group_size, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim,
-                                         int32_t prefix_len) {
-  if (num_seqs <= 0 || num_groups <= 0 || max_group_size <= 0 || prefix_len <= 0 ||
+                                         int32_t max_prefix_len) {
+  if (num_seqs <= 0 || num_groups <= 0 || max_group_size <= 0 || max_prefix_len < 0 ||
       num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
     return 0;
   const int g = num_q_heads / num_kv_heads;
   if (!supported_head_dim(head_dim) || !supported_group(g, head_dim)) return 0;
   return cascade_layout(num_seqs, num_groups, max_group_size, num_q_heads, num_kv_heads, head_dim,
-                        prefix_len).bytes;
+                        max_prefix_len).bytes;
 }
 
-pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache,
-                              const void* value_cache, int64_t num_blocks,
-                              const int32_t* block_tables, const int32_t* seq_lens,
-                              const int32_t* group_start, int32_t num_seqs, int32_t num_groups,
-                              int32_t max_group_size, int32_t prefix_len, int32_t num_q_heads,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                              int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status_t cascade_impl(void* out, const void* query, const void* key_cache,
+                         const void* value_cache, int64_t num_blocks, const int32_t* block_tables,
+                         const int32_t* seq_lens, const int32_t* group_start,
+                         const int32_t* prefix_lens, int32_t num_seqs, int32_t num_groups,
+                         int32_t max_group_size, int32_t max_prefix_len, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks_per_seq, int32_t max_seq_len, float scale, bool fp8,
+                         float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   if (num_seqs < 0 || num_groups < 0 || max_group_size < 0)
     return fail(PA_ERR_INVALID_ARG, "negative size (num_seqs %d, num_groups %d, max_group_size %d)",
                 num_seqs, num_groups, max_group_size);
   pa_status_t st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
                                          max_blocks_per_seq, max_seq_len, scale);
   if (st != PA_OK) return st;
+  if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
+    return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if (fp8 && !std::isfinite(scale * k_scale))
+    return fail(PA_ERR_INVALID_ARG, "scale * k_scale overflows");
   if (num_blocks <= 0 || num_blocks > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "num_blocks %lld out of range", (long long)num_blocks);
-  if (prefix_len <= 0 || prefix_len % block_size || prefix_len > max_seq_len)
-    return fail(PA_ERR_INVALID_ARG,
-                "prefix_len %d must be a positive multiple of block_size %d and <= max_seq_len %d",
-                prefix_len, block_size, max_seq_len);
+  if (max_prefix_len < 0 || max_prefix_len > max_seq_len)
+    return fail(PA_ERR_INVALID_ARG, "max_prefix_len %d must be in [0, max_seq_len %d]",
+                max_prefix_len, max_seq_len);
   if (num_seqs == 0) return ok();
   if (num_groups == 0 || max_group_size == 0 || max_group_size > num_seqs)
     return fail(PA_ERR_INVALID_ARG, "num_groups %d / max_group_size %d do not cover %d sequences",
                 num_groups, max_group_size, num_seqs);
-  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !group_start)
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !seq_lens || !group_start ||
+      !prefix_lens)
     return fail(PA_ERR_NULL_POINTER, "null pointer argument");
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
       !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4) ||
-      !aligned(group_start, 4))
-    return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for bf16 arrays)");
+      !aligned(group_start, 4) || !aligned(prefix_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for the bf16 arrays)");
   if (out == query) return fail(PA_ERR_INVALID_ARG, "out must not alias query");
   const CascadeLayout c = cascade_layout(num_seqs, num_groups, max_group_size, num_q_heads,
-                                         num_kv_heads, head_dim, prefix_len);
+                                         num_kv_heads, head_dim, max_prefix_len);
   if (c.bytes == 0) return fail(PA_ERR_HIP, "cannot query the device for the launch shapes");
   if (!workspace || workspace_bytes < c.bytes)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
@@ -478,8 +485,8 @@ pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cach
   const int S = c.split.splits;
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  // 1. The shared prompt, once per group: the group's decode queries are one non-causal chunk
-  //    over the first prefix_len tokens, read through the table row of the group's first member.
+  // 1. Each group's shared prompt, once: the group's decode queries are one non-causal chunk over
+  //    its first prefix_lens[first member] tokens, read through its first member's table row.
   pa::PrefillParams a{};
   a.out = static_cast<uint16_t*>(out);
   a.query = static_cast<const uint16_t*>(query);
@@ -487,7 +494,7 @@ pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cach
   a.vpool = static_cast<const uint16_t*>(value_cache);
   a.block_tables = block_tables;
   a.query_start_loc = group_start;
-  a.seq_lens = seq_lens;
+  a.seq_lens = prefix_lens;
   a.ws_ml = ml;
   a.ws_acc = acc;
   a.num_blocks = num_blocks;
@@ -499,29 +506,66 @@ pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cach
   a.head_dim = head_dim;
   a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
-  a.max_seq_len = prefix_len;
+  a.max_seq_len = max_prefix_len;
   a.splits = S;
-  a.split_keys = S > 1 ? c.split.split_keys : prefix_len;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.split_keys = S > 1 ? c.split.split_keys : std::max(max_prefix_len, 1);
+  a.scale_log2 = (fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
   a.noncausal = 1;
-  a.table_from_qsl = 1;
-  a.fixed_len = prefix_len;
+  a.from_first_row = 1;
   a.ws_splits = S + 1;
   a.defer_merge = 1;
-  a.v_scale = 1.f;
+  a.kv_fp8 = fp8;
+  a.v_scale = fp8 ? v_scale : 1.f;
   if (S > 1 && a.split_keys % 32)
     return fail(PA_ERR_HIP, "internal: prompt split of %d keys", a.split_keys);
   hipError_t e = pa::launch_prefill(a, hs);
   if (e != hipSuccess) return hip_status(e, "decode_cascade (prompt)");
-  // 2. Each sequence's own tokens past the prompt, as decode with the prompt's blocks skipped;
+  // 2. Each sequence's own tokens past its prompt, as decode with the prompt's blocks skipped;
   //    the per-row state goes to the last split.
   st = decode_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                   max_seq_len, scale, false, 1.f, 1.f, ws + c.dec_off, workspace_bytes - c.dec_off,
-                   stream, prefix_len, ml, acc, S + 1, S);
+                   max_seq_len, scale, fp8, k_scale, v_scale, ws + c.dec_off,
+                   workspace_bytes - c.dec_off, stream, prefix_lens, ml, acc, S + 1, S);
   if (st != PA_OK) return st;
   // 3. Combine the prompt splits with the tail split of every row.
   return hip_status(pa::launch_prefill_merge(a, hs), "decode_cascade (merge)");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode_cascade(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, int64_t num_blocks,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* group_start, const int32_t* prefix_lens,
+                              int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                              int32_t max_prefix_len, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return cascade_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
+                      group_start, prefix_lens, num_seqs, num_groups, max_group_size,
+                      max_prefix_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                      max_blocks_per_seq, max_seq_len, scale, false, 1.f, 1.f, workspace,
+                      workspace_bytes, stream);
+}
+
+pa_status_t pa_decode_cascade_fp8(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, int64_t num_blocks,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens,
+                                  int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                                  int32_t max_prefix_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                                  float k_scale, float v_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return cascade_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
+                      group_start, prefix_lens, num_seqs, num_groups, max_group_size,
+                      max_prefix_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                      max_blocks_per_seq, max_seq_len, scale, true, k_scale, v_scale, workspace,
+                      workspace_bytes, stream);
 }
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
@@ -605,7 +649,7 @@ pa_status_t prefill_impl(void* out, const void* query, const void* key_cache,
   p.splits = need > 0 ? sp.splits : 1;
   p.split_keys = need > 0 ? sp.split_keys : max_seq_len;
   p.ws_splits = p.splits;
-  p.fixed_len = -1;  // lengths from seq_lens; causal; merged here
+  // lengths from seq_lens, causal, merged here
   // FP8: the K scale joins the softmax scale and the V scale multiplies the outputs.
   p.scale_log2 = (fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
   p.kv_fp8 = fp8;

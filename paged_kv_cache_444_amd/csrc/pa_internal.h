@@ -43,13 +43,13 @@ struct DecodeParams {
   // every output is multiplied by v_scale; for bf16 pools v_scale is 1.
   int kv_fp8;
   float v_scale;
-  // Shared-prefix (cascade) use.  kv_skip: leading tokens of every sequence left out (a multiple
-  // of block_size; block_tables then points kv_skip / block_size entries into each row and
-  // table_cols is the entries left per row).  state_ml non-null: each (sequence, query head) row's
-  // final (m in the log2 domain, l) and unnormalised acc go to split state_split of the prefill
-  // workspace layout (state_ml[2u], state_ml[2u+1], state_acc[u*D..], u = row*state_stride +
-  // state_split) instead of the output.
-  int kv_skip, table_cols;
+  // Shared-prefix (cascade) use.  skip_lens non-null: int32 [num_seqs], leading tokens of each
+  // sequence left out (whole blocks: rounded down to a multiple of block_size), so the sequence
+  // is attended from table entry skip / block_size on.  state_ml non-null: each (sequence, query
+  // head) row's final (m in the log2 domain, l) and unnormalised acc go to split state_split of
+  // the prefill workspace layout (state_ml[2u], state_ml[2u+1], state_acc[u*D..],
+  // u = row*state_stride + state_split) instead of the output.
+  const int32_t* skip_lens;
   float* state_ml;
   float* state_acc;
   int state_stride, state_split;
@@ -96,12 +96,12 @@ struct PrefillParams {
   int max_blocks_per_seq, max_seq_len;
   int splits, split_keys;  // context split: `splits` key ranges of split_keys keys (multiple of 32)
   float scale_log2;
-  // Shared-prefix (cascade) use.  noncausal: every row sees all L keys.  table_from_qsl: sequence
-  // i's block-table row is query_start_loc[i] (its first query row's sequence).  fixed_len >= 0:
-  // every sequence's L.  ws_splits: split count of the workspace layout (>= splits; split j of
-  // row u is slot u * ws_splits + j).  defer_merge: always write split states, never the output;
-  // the caller merges later.
-  int noncausal, table_from_qsl, fixed_len, ws_splits, defer_merge;
+  // Shared-prefix (cascade) use.  noncausal: every row sees all L keys.  from_first_row: sequence
+  // i's block-table row and length are those of row query_start_loc[i] (its first query row's
+  // sequence): block_tables and seq_lens are then indexed by query row.  ws_splits: split count
+  // of the workspace layout (>= splits; split j of row u is slot u * ws_splits + j).
+  // defer_merge: always write split states, never the output; the caller merges later.
+  int noncausal, from_first_row, ws_splits, defer_merge;
   // FP8 pools (E4M3 codes, same element order, one byte each); outputs and split states are
   // multiplied by v_scale (1 for bf16 pools).
   int kv_fp8;

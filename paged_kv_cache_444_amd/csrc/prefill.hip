@@ -233,8 +233,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   const int q_len = p.query_start_loc[s + 1] - qs;
   const int q0 = blockIdx.x * TQ;
   if (q_len <= 0 || q0 >= q_len) return;  // block-uniform
-  const int L = p.fixed_len >= 0 ? min(p.fixed_len, p.max_seq_len)
-                                  : min(max(p.seq_lens[s], 0), p.max_seq_len);
+  // With from_first_row the table row and length are those of the first query row, clamped into
+  // the table (whose rows are then the total_q query rows) so a malformed query_start_loc cannot
+  // leave it.
+  const int trow = p.from_first_row ? min(max(qs, 0), p.total_q - 1) : s;
+  const int L = min(max(p.seq_lens[trow], 0), p.max_seq_len);
   // Non-causal rows see every key: ctx = L makes each row's last visible key L - 1.
   const int ctx = p.noncausal ? L : max(L - q_len, 0);
   const int tq = min(TQ, q_len - q0);
@@ -290,9 +293,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // With table_from_qsl the row is the first query row's sequence, clamped into the table (whose
-  // rows are the total_q query rows) so a malformed query_start_loc cannot leave it.
-  const int trow = p.table_from_qsl ? min(max(qs, 0), p.total_q - 1) : s;
   const int* bt = p.block_tables + (size_t)trow * p.max_blocks_per_seq;
   const int t_first = kb / kKeyTile;
   const int t_end = (ke + kKeyTile - 1) / kKeyTile;  // empty range: t_end <= t_first

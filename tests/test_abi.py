@@ -76,15 +76,15 @@ def test_host_side_validation(lib):
     assert lib.pa_decode_fp8(z, z, z, z, 10, z, z, 1, 8, 2, 96, 16, 4, 64, 0.1, 1.0, 1.0, z, 0, z) == 3
     assert lib.pa_reshape_and_cache_fp8(z, z, 256, z, z, z, 1, 2, 128, 16, 10, -1.0, 1.0, z) == 2
     assert lib.pa_reshape_and_cache_fp8(z, z, 256, z, z, z, 0, 2, 128, 16, 10, 1.0, 1.0, z) == 0
-    # cascade: prefix_len not a multiple of the block size / beyond max_seq_len / zero
-    assert lib.pa_decode_cascade(z, z, z, z, 10, z, z, z, 4, 1, 4, 20, 8, 2, 64, 16, 4, 64, 0.1, z, 0,
-                                 z) == 2
-    assert lib.pa_decode_cascade(z, z, z, z, 10, z, z, z, 4, 1, 4, 80, 8, 2, 64, 16, 8, 64, 0.1, z, 0,
-                                 z) == 2
-    assert lib.pa_decode_cascade(z, z, z, z, 10, z, z, z, 4, 1, 4, 0, 8, 2, 64, 16, 4, 64, 0.1, z, 0,
-                                 z) == 2
-    assert lib.pa_decode_cascade(z, z, z, z, 10, z, z, z, 4, 1, 4, 32, 8, 2, 64, 16, 4, 64, 0.1, z, 0,
-                                 z) == 1  # nulls
+    # cascade: max_prefix_len beyond max_seq_len / negative; null pointers; FP8 scale
+    assert lib.pa_decode_cascade(z, z, z, z, 10, z, z, z, z, 4, 1, 4, 80, 8, 2, 64, 16, 8, 64, 0.1,
+                                 z, 0, z) == 2
+    assert lib.pa_decode_cascade(z, z, z, z, 10, z, z, z, z, 4, 1, 4, -16, 8, 2, 64, 16, 4, 64, 0.1,
+                                 z, 0, z) == 2
+    assert lib.pa_decode_cascade(z, z, z, z, 10, z, z, z, z, 4, 1, 4, 32, 8, 2, 64, 16, 4, 64, 0.1,
+                                 z, 0, z) == 1
+    assert lib.pa_decode_cascade_fp8(z, z, z, z, 10, z, z, z, z, 4, 1, 4, 32, 8, 2, 64, 16, 4, 64,
+                                     0.1, 0.0, 1.0, z, 0, z) == 2
     assert lib.pa_decode_cascade_workspace_bytes(4, 1, 4, 8, 2, 96, 32) == 0
     assert lib.pa_prefill_chunk_fp8(z, z, z, z, 10, z, z, z, 1, 4, 4, 8, 2, 64, 16, 4, 64, 0.1, 0.0,
                                     1.0, z, 0, z) == 2  # k_scale

@@ -22,15 +22,26 @@ def say(msg):
     sys.stdout.flush()
 
 
-def _cascade(case, kc, vc, group_start, prefix_len, seq_lens=None):
+def _prefix_lens(group_start, prefix):
+    """Per-sequence shared lengths: `prefix` is one length for every group or one per group."""
+    gs = np.asarray(group_start)
+    per_group = np.broadcast_to(np.asarray(prefix), (len(gs) - 1,))
+    return np.repeat(per_group, np.diff(gs)).astype(np.int32)
+
+
+def _cascade(case, kc, vc, group_start, prefix, fp8_scales=None):
     d = case.decode
-    sl = d.seq_lens if seq_lens is None else seq_lens
     gs = np.asarray(group_start, dtype=np.int32)
-    out = pa.decode_cascade(dev_u16(d.query), kc, vc, dev_i32(d.block_tables), dev_i32(sl),
-                            dev_i32(gs), prefix_len=prefix_len,
-                            max_group_size=int(np.diff(gs).max()), num_kv_heads=case.num_kv_heads,
-                            block_size=case.block_size, scale=float(case.scale),
-                            max_seq_len=int(np.max(sl)))
+    pl = _prefix_lens(gs, prefix)
+    kw = dict(max_prefix_len=int(pl.max()), max_group_size=int(np.diff(gs).max()),
+              num_kv_heads=case.num_kv_heads, block_size=case.block_size, scale=float(case.scale),
+              max_seq_len=int(d.seq_lens.max()))
+    args = (dev_u16(d.query), kc, vc, dev_i32(d.block_tables), dev_i32(d.seq_lens), dev_i32(gs),
+            dev_i32(pl))
+    if fp8_scales is None:
+        out = pa.decode_cascade(*args, **kw)
+    else:
+        out = pa.decode_cascade_fp8(*args, k_scale=fp8_scales[0], v_scale=fp8_scales[1], **kw)
     torch.cuda.synchronize()
     return host_u16(out)
 
@@ -100,3 +111,38 @@ def test_cascade_all_tails_empty_and_table_exactly_the_prompt():
     ref = oracle.decode(d.query, case.key_cache, case.value_cache, d.block_tables, d.seq_lens, 2,
                         64, bs, case.scale)
     assert_close(got, ref, "cascade with empty tails")
+
+
+def test_cascade_prompts_of_different_lengths_and_unshared_sequences():
+    """Groups with prompts of 2, 0 (nothing shared), 5 and 1 blocks in one call."""
+    bs = 16
+    groups = [(0, 3, 2), (3, 5, 0), (5, 9, 5), (9, 10, 1)]  # (first, end, shared blocks)
+    lens = [40, 33, 70, 20, 9, 81, 90, 100, 85, 30]
+    case = build_case(Spec(name="cascade", num_q_heads=8, num_kv_heads=2, head_dim=64,
+                           block_size=bs, seed=(444, 84), decode_lens=lens,
+                           share_groups=[(list(range(a, b)), n * bs) for a, b, n in groups
+                                         if n and b - a > 1]))
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    gs = [0] + [b for _, b, _ in groups]
+    got = upcast(_cascade(case, kc, vc, gs, [n * bs for _, _, n in groups]))
+    d = case.decode
+    ref = oracle.decode(d.query, case.key_cache, case.value_cache, d.block_tables, d.seq_lens, 2,
+                        64, bs, case.scale)
+    assert_close(got, ref, "cascade with mixed prompt lengths")
+
+
+def test_cascade_fp8_prefix_shared_rollouts():
+    """The prefix-shared rollouts over an FP8 cache quantised by the oracle."""
+    from helpers import dev_u8, oracle_quantize_pool
+
+    case = cached_named_case(5)
+    d = case.decode
+    ks, vs = 6.0 / 448.0, 5.5 / 448.0
+    okc, ovc = cached_oracle_pools(5)
+    kc8, vc8 = oracle_quantize_pool(okc, ks), oracle_quantize_pool(ovc, vs)
+    gs = np.arange(0, 129, 16)
+    got = _cascade(case, dev_u8(kc8), dev_u8(vc8), gs, 4096, fp8_scales=(ks, vs))
+    seqs = [0, 17, 90, 127]
+    ref = oracle.decode_fp8(d.query, kc8, vc8, d.block_tables, d.seq_lens, case.num_kv_heads,
+                            case.head_dim, case.block_size, case.scale, ks, vs, seqs=seqs)
+    assert_close(upcast(got)[seqs], ref[seqs], "FP8 cascade decode cfg5")

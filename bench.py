@@ -244,6 +244,7 @@ def main():
     if not args.no_fp8:
         fp8 = run_fp8_decode(args, case, pools, q, bt, sl, out, ws, ms_per_step, main_ms)
     n_pools = len(pools)
+    ceiling = stream_read_ceiling()
     mixed = None
     if not args.no_mixed:
         del pools, kc0, vc0
@@ -295,6 +296,9 @@ def main():
             "ms_per_step_with_events": round((t3 - t2) * 1e3 / args.steps, 5),
         },
         "warm_single_pool_us_per_step": None if warm_us is None else round(warm_us, 2),
+        "stream_read_ceiling": dict(ceiling,
+                                    decode_kernel_frac=round(main_gbs / ceiling["gbs"], 4),
+                                    decode_call_frac=round(gbs / ceiling["gbs"], 4)),
         "fp8_decode": fp8,
         "mixed_step": mixed,
         "cow_step": cow,
@@ -302,6 +306,32 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def stream_read_ceiling(gib=4, reps=20):
+    """The measured HBM read ceiling: the library's plain streaming-read kernel (every byte of a
+    `gib` GiB buffer once, 16-byte non-temporal loads) timed with events on its stream."""
+    import torch
+
+    import paged_kv_cache_444_amd as pa
+
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = pa.stream_read(buf)
+    for _ in range(5):
+        pa.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    pa.trace_enable(True)
+    pa.trace_read("stream_read")
+    for _ in range(reps):
+        pa.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    n, ms = pa.trace_read("stream_read")
+    pa.trace_enable(False)
+    del buf, sink
+    torch.cuda.empty_cache()
+    us = ms / n * 1e3
+    return {"kernel": "stream_read_kernel", "bytes": gib << 30, "us": round(us, 1),
+            "gbs": round((gib << 30) / (us * 1e-6) / 1e9, 1)}
 
 
 def fp8_decode_bytes(seq_lens, Hq, Hkv, D, bs):

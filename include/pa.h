@@ -306,11 +306,22 @@ pa_status_t pa_prefill_chunk_fp8(void* out, const void* query, const void* key_c
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Measurement: a plain streaming read, the HBM read ceiling the decode kernel is compared
+ * against.  pa_stream_read reads `bytes` of `src` (a multiple of 16, 16-byte aligned) once, in
+ * order, with 16-byte non-temporal loads, and writes one XOR word per workgroup to `sink`
+ * (at least pa_stream_read_sink_words() words; 0 means the device could not be queried).
+ * Errors as elsewhere; PA_ERR_WORKSPACE for a short sink.  Kernel name for tracing: "stream_read".
+ */
+int32_t pa_stream_read_sink_words(void);
+pa_status_t pa_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                           void* stream);
+
+/*
  * Kernel timing (tracing).  While enabled, every kernel the library launches is bracketed by a
  * pair of HIP events recorded on its stream.  pa_trace_read synchronises on the recorded events,
  * returns the number of launches and their summed duration (milliseconds) for one kernel name, and
  * forgets those records.  Kernel names: "reshape_and_cache", "copy_blocks", "decode_partition",
- * "decode_merge", "prefill_chunk", "prefill_merge".  Events are host-side driver objects; no
+ * "decode_merge", "prefill_chunk", "prefill_merge", "stream_read".  Events are host-side driver objects; no
  * device memory is used.
  */
 pa_status_t pa_trace_enable(int32_t enable);

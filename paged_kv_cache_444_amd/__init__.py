@@ -18,10 +18,9 @@ import torch
 __all__ = [
     "load_library", "reshape_and_cache", "reshape_and_cache_fp8", "copy_blocks", "decode",
     "decode_fp8", "decode_cascade", "decode_cascade_fp8", "decode_cascade_workspace_bytes",
-    "prefill_chunk",
-    "prefill_chunk_fp8",
-    "mixed_step", "decode_workspace_bytes", "prefill_workspace_bytes", "trace_enable", "trace_read", "PagedAttentionError", "pool_shape",
-    "LIB_PATH",
+    "prefill_chunk", "prefill_chunk_fp8", "mixed_step", "decode_workspace_bytes",
+    "prefill_workspace_bytes", "stream_read", "trace_enable", "trace_read", "PagedAttentionError",
+    "pool_shape", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -67,6 +66,8 @@ _SIGNATURES = {
     "pa_prefill_chunk_fp8": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                     _I32, _I32, _I32, _I32, ctypes.c_float, ctypes.c_float,
                                     ctypes.c_float, _P, _SZ, _P]),
+    "pa_stream_read_sink_words": (_I32, []),
+    "pa_stream_read": (_I32, [_P, _SZ, _P, _SZ, _P]),
     "pa_trace_enable": (_I32, [_I32]),
     "pa_trace_read": (_I32, [ctypes.c_char_p, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double)]),
 }
@@ -412,6 +413,19 @@ def prefill_chunk_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache:
                                     max_seq_len, float(scale), float(k_scale), float(v_scale), ws,
                                     ws_bytes, _stream()))
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Read every byte of `buf` once (the streaming-read ceiling kernel); returns the sink."""
+    lib = load_library()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    words = int(lib.pa_stream_read_sink_words())
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=buf.device)
+    _check(lib.pa_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                              sink.numel(), _stream()))
+    return sink
 
 
 def trace_enable(on: bool = True) -> None:

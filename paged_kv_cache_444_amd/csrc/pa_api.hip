@@ -4,6 +4,7 @@
 #include "../../include/pa.h"
 #include "cascade.h"
 #include "copy_blocks.h"
+#include "stream_read.h"
 #include "pa_internal.h"
 
 #include <algorithm>
@@ -257,6 +258,22 @@ pa_status_t pa_copy_blocks(void* key_cache, void* value_cache, int64_t num_block
   p.block_vec16 = (int64_t)num_kv_heads * block_size * head_dim / 8;
   p.num_pairs = num_pairs;
   return hip_status(pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)), "copy_blocks");
+}
+
+int32_t pa_stream_read_sink_words(void) { return pa::stream_read_grid(); }
+
+pa_status_t pa_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                           void* stream) {
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(PA_ERR_NULL_POINTER, "null pointer argument");
+  if (bytes % 16 || !aligned(src, 16) || !aligned(sink, 4))
+    return fail(PA_ERR_INVALID_ARG, "bytes must be a multiple of 16 and src 16-byte aligned");
+  const int grid = pa::stream_read_grid();
+  if (grid <= 0) return fail(PA_ERR_HIP, "cannot query the device");
+  if (sink_words < (size_t)grid)
+    return fail(PA_ERR_WORKSPACE, "sink of %zu words given, %d needed", sink_words, grid);
+  return hip_status(pa::launch_stream_read(src, bytes, sink, grid, static_cast<hipStream_t>(stream)),
+                    "stream_read");
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

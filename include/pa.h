@@ -11,7 +11,8 @@
  *
  * Conventions for every entry point
  *   - All arrays are device pointers owned by the caller; the library allocates no device memory,
- *     keeps no device state between calls, and never synchronises the stream.
+ *     keeps no device state between calls, and never synchronises the stream (pa_mixed_step
+ *     keeps two host-side events per thread and device, see there).
  *   - bf16 tensors are raw 16-bit bfloat16 bit patterns, contiguous, 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call enqueues its kernels on
  *     that stream and returns immediately.
@@ -304,6 +305,64 @@ pa_status_t pa_prefill_chunk_fp8(void* out, const void* query, const void* key_c
                                  int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                  int32_t max_seq_len, float scale, float k_scale, float v_scale,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_mixed_step — one chunked-prefill batch step: a prefill-chunk call and a decode call run side
+ * by side, the decode on `side_stream`, so decode's HBM-bound work overlaps the matrix-core-bound
+ * chunk.
+ *
+ * Source: a serving step batches the slices of a long prompt with the decode tokens of the other
+ * requests ("Serving engine internals" lesson, chunked-prefill section: the batch is one GPU
+ * call).  Write every new token's K/V first (pa_reshape_and_cache on `stream`).
+ *
+ *   prefill, decode  the arguments of pa_prefill_chunk / pa_decode (or their FP8 forms when
+ *                    kv_fp8 is nonzero, with k_scale and v_scale); the two outputs and the two
+ *                    workspaces must be distinct
+ *   stream           the caller's stream: both halves start after the work already on it, and
+ *                    later work on it waits for both
+ *   side_stream      a second stream of the same device at default priority; NULL or `stream`
+ *                    runs the two calls one after the other on `stream`
+ * Both halves are validated before either is launched; errors as the two calls.  Results are
+ * those of the two calls made one after the other, bit for bit.  The library keeps one pair of
+ * events per thread and device for the fork and the join (created on first use).
+ */
+typedef struct pa_prefill_args {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  const int32_t* query_start_loc;
+  const int32_t* seq_lens;
+  int32_t num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size;
+  int32_t max_blocks_per_seq, max_seq_len;
+  float scale;
+  int32_t kv_fp8;
+  float k_scale, v_scale;
+  void* workspace;
+  size_t workspace_bytes;
+} pa_prefill_args;
+
+typedef struct pa_decode_args {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
+  int32_t max_seq_len;
+  float scale;
+  int32_t kv_fp8;
+  float k_scale, v_scale;
+  void* workspace;
+  size_t workspace_bytes;
+} pa_decode_args;
+
+pa_status_t pa_mixed_step(const pa_prefill_args* prefill, const pa_decode_args* decode,
+                          void* stream, void* side_stream);
 
 /*
  * Measurement: a plain streaming read, the HBM read ceiling the decode kernel is compared

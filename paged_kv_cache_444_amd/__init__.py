@@ -42,6 +42,27 @@ _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 
+class _PrefillArgs(ctypes.Structure):
+    """pa_prefill_args (include/pa.h), field for field."""
+    _fields_ = [("out", _P), ("query", _P), ("key_cache", _P), ("value_cache", _P),
+                ("num_blocks", _I64), ("block_tables", _P), ("query_start_loc", _P),
+                ("seq_lens", _P), ("num_seqs", _I32), ("total_q", _I32), ("max_q_len", _I32),
+                ("num_q_heads", _I32), ("num_kv_heads", _I32), ("head_dim", _I32),
+                ("block_size", _I32), ("max_blocks_per_seq", _I32), ("max_seq_len", _I32),
+                ("scale", ctypes.c_float), ("kv_fp8", _I32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float), ("workspace", _P), ("workspace_bytes", _SZ)]
+
+
+class _DecodeArgs(ctypes.Structure):
+    """pa_decode_args (include/pa.h), field for field."""
+    _fields_ = [("out", _P), ("query", _P), ("key_cache", _P), ("value_cache", _P),
+                ("num_blocks", _I64), ("block_tables", _P), ("seq_lens", _P), ("num_seqs", _I32),
+                ("num_q_heads", _I32), ("num_kv_heads", _I32), ("head_dim", _I32),
+                ("block_size", _I32), ("max_blocks_per_seq", _I32), ("max_seq_len", _I32),
+                ("scale", ctypes.c_float), ("kv_fp8", _I32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float), ("workspace", _P), ("workspace_bytes", _SZ)]
+
+
 _SIGNATURES = {
     "pa_version": (_I32, []),
     "pa_last_error": (ctypes.c_char_p, []),
@@ -68,6 +89,7 @@ _SIGNATURES = {
                                     ctypes.c_float, _P, _SZ, _P]),
     "pa_stream_read_sink_words": (_I32, []),
     "pa_stream_read": (_I32, [_P, _SZ, _P, _SZ, _P]),
+    "pa_mixed_step": (_I32, [ctypes.POINTER(_PrefillArgs), ctypes.POINTER(_DecodeArgs), _P, _P]),
     "pa_trace_enable": (_I32, [_I32]),
     "pa_trace_read": (_I32, [ctypes.c_char_p, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double)]),
 }
@@ -357,32 +379,90 @@ def prefill_chunk(query: torch.Tensor, key_cache: torch.Tensor, value_cache: tor
 _side_streams = {}
 
 
-def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None, fp8: bool = False):
-    """One chunked-prefill batch step: the prefill chunk and the decode of the other sequences run
-    side by side on two streams, so decode's HBM-bound work overlaps the matrix-core-bound chunk.
+def _owned_workspace(nbytes: int, workspace: Optional[torch.Tensor], device):
+    """(tensor, pointer, bytes) of a workspace; a fresh one is zero-filled.  The caller keeps the
+    tensor: two workspaces used by concurrent kernels must not share a cached block."""
+    if nbytes == 0:
+        return None, 0, 0
+    if workspace is None:
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
-    `prefill` and `decode_call` hold the keyword arguments of `prefill_chunk` and `decode`.  Both
+
+def _pools(key_cache, value_cache, fp8):
+    if fp8:
+        return _fp8_pool(key_cache, "key_cache"), _fp8_pool(value_cache, "value_cache")
+    return _bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache")
+
+
+def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None, fp8: bool = False):
+    """One chunked-prefill batch step (pa_mixed_step): the prefill chunk and the decode of the
+    other sequences run side by side on two streams, so decode's HBM-bound work overlaps the
+    matrix-core-bound chunk.
+
+    `prefill` and `decode_call` hold the keyword arguments of `prefill_chunk` and `decode` (with
+    `fp8`: of `prefill_chunk_fp8` and `decode_fp8`, the uint8 pools and k_scale / v_scale).  Both
     halves start after the work already queued on the current stream (write every new token's
-    K/V with reshape_and_cache first), and the current stream waits for both before later work.
-    Decode is launched first, on `side_stream` (default: one stream per device, kept for reuse),
-    so its workgroups are resident before the prefill chunk's fill the remaining room.  Returns
-    (prefill output, decode output); the results are those of the two calls made one after the
-    other.  With `fp8` the halves are prefill_chunk_fp8 and decode_fp8 (the dicts then carry the
-    uint8 pools and k_scale / v_scale).
+    K/V with reshape_and_cache first), and the current stream waits for both.  The decode runs on
+    `side_stream` (default: one stream per device, kept for reuse).  Returns (prefill output,
+    decode output), bit for bit those of the two calls made one after the other.
     """
+    lib = load_library()
     main = torch.cuda.current_stream()
     if side_stream is None:
-        dev = main.device
-        side_stream = _side_streams.get(dev)
+        side_stream = _side_streams.get(main.device)
         if side_stream is None:
-            side_stream = _side_streams[dev] = torch.cuda.Stream(device=dev)
-    side_stream.wait_stream(main)
-    with torch.cuda.stream(side_stream):
-        dout = (decode_fp8 if fp8 else decode)(**decode_call)
-    pout = (prefill_chunk_fp8 if fp8 else prefill_chunk)(**prefill)
-    main.wait_stream(side_stream)
-    # The decode output (and a caller's tensors) are used on the current stream from here on.
-    dout.record_stream(main)
+            side_stream = _side_streams[main.device] = torch.cuda.Stream(device=main.device)
+    p, d = dict(prefill), dict(decode_call)
+    # prefill half
+    pq = p["query"]
+    total_q, Hq, D = pq.shape
+    n_p = p["seq_lens"].numel()
+    pout = p.get("out")
+    if pout is None:
+        pout = torch.empty_like(pq)
+    pws_t, pws, pws_bytes = _owned_workspace(
+        prefill_workspace_bytes(n_p, total_q, p["max_q_len"], Hq, p["num_kv_heads"], D,
+                                p["max_seq_len"]), p.get("workspace"), pq.device)
+    nb = (_num_blocks_fp8 if fp8 else _num_blocks)(p["key_cache"], p["num_kv_heads"],
+                                                   p["block_size"], D)
+    pk, pv = _pools(p["key_cache"], p["value_cache"], fp8)
+    pa_args = _PrefillArgs(
+        _bf16(pout, "out"), _bf16(pq, "query"), pk, pv, nb,
+        _ints(p["block_tables"], torch.int32, "block_tables"),
+        _ints(p["query_start_loc"], torch.int32, "query_start_loc"),
+        _ints(p["seq_lens"], torch.int32, "seq_lens"), n_p, total_q, p["max_q_len"], Hq,
+        p["num_kv_heads"], D, p["block_size"], p["block_tables"].shape[1], p["max_seq_len"],
+        float(p.get("scale") or 1.0 / math.sqrt(D)), int(fp8), float(p.get("k_scale", 1.0)),
+        float(p.get("v_scale", 1.0)), pws, pws_bytes)
+    # decode half
+    dq = d["query"]
+    B, dHq, dD = dq.shape
+    max_len = d.get("max_seq_len")
+    if max_len is None:
+        max_len = int(d["seq_lens"].max().item()) if B else 0
+    dout = d.get("out")
+    if dout is None:
+        dout = torch.empty_like(dq)
+    dws_t, dws, dws_bytes = _owned_workspace(
+        decode_workspace_bytes(B, dHq, d["num_kv_heads"], dD, max_len), d.get("workspace"),
+        dq.device)
+    dnb = (_num_blocks_fp8 if fp8 else _num_blocks)(d["key_cache"], d["num_kv_heads"],
+                                                    d["block_size"], dD)
+    dk, dv = _pools(d["key_cache"], d["value_cache"], fp8)
+    de_args = _DecodeArgs(
+        _bf16(dout, "out"), _bf16(dq, "query"), dk, dv, dnb,
+        _ints(d["block_tables"], torch.int32, "block_tables"),
+        _ints(d["seq_lens"], torch.int32, "seq_lens"), B, dHq, d["num_kv_heads"], dD,
+        d["block_size"], d["block_tables"].shape[1], max_len,
+        float(d.get("scale") or 1.0 / math.sqrt(dD)), int(fp8), float(d.get("k_scale", 1.0)),
+        float(d.get("v_scale", 1.0)), dws, dws_bytes)
+    _check(lib.pa_mixed_step(ctypes.byref(pa_args), ctypes.byref(de_args), _stream(),
+                             side_stream.cuda_stream))
+    # Everything above was allocated on the current stream, which waits for the side stream
+    # before any later work, so once the call is enqueued the workspaces may go back to the
+    # cache: no later allocation can reach them before both halves are done.
+    del pws_t, dws_t
     return pout, dout
 
 

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -309,7 +310,8 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
                         bool fp8, float k_scale, float v_scale, void* workspace,
                         size_t workspace_bytes, void* stream,
                         const int32_t* skip_lens = nullptr, float* state_ml = nullptr,
-                        float* state_acc = nullptr, int state_stride = 0, int state_split = 0) {
+                        float* state_acc = nullptr, int state_stride = 0, int state_split = 0,
+                        bool validate_only = false) {
   if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (fp8 && !std::isfinite(scale * k_scale))
@@ -372,6 +374,7 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
   p.counter = reinterpret_cast<unsigned*>(base + wl.counter_off);
   p.unit_info = reinterpret_cast<int2*>(base + wl.info_off);
   p.partials = reinterpret_cast<float*>(base + wl.partials_off);
+  if (validate_only) return ok();
   return hip_status(pa::launch_decode(p, static_cast<hipStream_t>(stream)), "decode");
 }
 
@@ -611,7 +614,8 @@ pa_status_t prefill_impl(void* out, const void* query, const void* key_cache,
                          int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                          int32_t max_seq_len, float scale, bool fp8, float k_scale,
-                         float v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                         float v_scale, void* workspace, size_t workspace_bytes, void* stream,
+                         bool validate_only = false) {
   if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (fp8 && !std::isfinite(scale * k_scale))
@@ -677,6 +681,7 @@ pa_status_t prefill_impl(void* out, const void* query, const void* key_cache,
     p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         align_up(rows * 2 * sizeof(float), 256));
   }
+  if (validate_only) return ok();
   return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill_chunk");
 }
 
@@ -710,6 +715,82 @@ pa_status_t pa_prefill_chunk_fp8(void* out, const void* query, const void* key_c
                       query_start_loc, seq_lens, num_seqs, total_q, max_q_len, num_q_heads,
                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_seq_len, scale,
                       true, k_scale, v_scale, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Mixed step: decode beside the prefill chunk on a second stream.
+
+}  // extern "C"
+
+namespace {
+
+pa_status_t prefill_call(const pa_prefill_args& a, void* stream, bool validate_only) {
+  return prefill_impl(a.out, a.query, a.key_cache, a.value_cache, a.num_blocks, a.block_tables,
+                      a.query_start_loc, a.seq_lens, a.num_seqs, a.total_q, a.max_q_len,
+                      a.num_q_heads, a.num_kv_heads, a.head_dim, a.block_size,
+                      a.max_blocks_per_seq, a.max_seq_len, a.scale, a.kv_fp8 != 0, a.k_scale,
+                      a.v_scale, a.workspace, a.workspace_bytes, stream, validate_only);
+}
+
+pa_status_t decode_call(const pa_decode_args& a, void* stream, bool validate_only) {
+  return decode_impl(a.out, a.query, a.key_cache, a.value_cache, a.num_blocks, a.block_tables,
+                     a.seq_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim,
+                     a.block_size, a.max_blocks_per_seq, a.max_seq_len, a.scale, a.kv_fp8 != 0,
+                     a.k_scale, a.v_scale, a.workspace, a.workspace_bytes, stream, nullptr,
+                     nullptr, nullptr, 0, 0, validate_only);
+}
+
+// Fork and join events of the calling thread on the current device (created on first use, kept
+// until the process ends).  They keep the default release on record: the other stream's kernels
+// consume what was written before the event (workspaces, inputs copied in), and without that
+// release those writes need not be visible to another queue's kernels.
+hipError_t fork_join_events(hipEvent_t* fork, hipEvent_t* join) {
+  thread_local std::map<int, std::pair<hipEvent_t, hipEvent_t>> per_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  auto& ev = per_device[dev];
+  if (!ev.first) {
+    const unsigned f = hipEventDisableTiming;
+    if ((e = hipEventCreateWithFlags(&ev.first, f)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ev.second, f)) != hipSuccess) return e;
+  }
+  *fork = ev.first;
+  *join = ev.second;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_mixed_step(const pa_prefill_args* prefill, const pa_decode_args* decode,
+                          void* stream, void* side_stream) {
+  if (!prefill || !decode) return fail(PA_ERR_NULL_POINTER, "null argument struct");
+  if (decode->out == prefill->out)
+    return fail(PA_ERR_INVALID_ARG, "the two halves must write different outputs");
+  // Both halves are validated before either is launched.
+  pa_status_t st = prefill_call(*prefill, stream, true);
+  if (st != PA_OK) return st;
+  if ((st = decode_call(*decode, side_stream, true)) != PA_OK) return st;
+  if (!side_stream || side_stream == stream) {  // one stream: the two calls in order
+    if ((st = decode_call(*decode, stream, false)) != PA_OK) return st;
+    return prefill_call(*prefill, stream, false);
+  }
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipError_t e = fork_join_events(&fork, &join);
+  if (e != hipSuccess) return hip_status(e, "mixed_step (events)");
+  hipStream_t hs = static_cast<hipStream_t>(stream), side = static_cast<hipStream_t>(side_stream);
+  if ((e = hipEventRecord(fork, hs)) != hipSuccess ||
+      (e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess)
+    return hip_status(e, "mixed_step (fork)");
+  // Decode first, so its persistent workgroups are resident before the chunk's fill the rest.
+  if ((st = decode_call(*decode, side_stream, false)) != PA_OK) return st;
+  if ((st = prefill_call(*prefill, stream, false)) != PA_OK) return st;
+  if ((e = hipEventRecord(join, side)) != hipSuccess ||
+      (e = hipStreamWaitEvent(hs, join, 0)) != hipSuccess)
+    return hip_status(e, "mixed_step (join)");
+  return ok();
 }
 
 }  // extern "C"

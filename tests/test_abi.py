@@ -91,3 +91,36 @@ def test_host_side_validation(lib):
     assert lib.pa_stream_read(z, 0, z, 0, z) == 0       # nothing to read
     assert lib.pa_stream_read(z, 32, z, 0, z) == 1      # nulls
     assert lib.pa_trace_read(b"decode_partition", None, None) == 1
+
+
+def test_argument_structs_match_the_header(tmp_path):
+    """pa_prefill_args / pa_decode_args: the binding's ctypes mirrors have the header's field
+    offsets and sizes (the header compiled by the host C compiler)."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "pa.h"', "int main(void) {"]
+    for cname, cls in (("pa_prefill_args", pa._PrefillArgs), ("pa_decode_args", pa._DecodeArgs)):
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "abi.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "abi"
+    subprocess.run([cc, "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    want = {}
+    for cname, cls in (("pa_prefill_args", pa._PrefillArgs), ("pa_decode_args", pa._DecodeArgs)):
+        want[f"{cname} size"] = ctypes.sizeof(cls)
+        for f, _ in cls._fields_:
+            want[f"{cname} {f}"] = getattr(cls, f).offset
+    got = {l.rsplit(" ", 1)[0]: int(l.rsplit(" ", 1)[1]) for l in out if l}
+    assert got == want
+
+
+def test_binding_exports_every_listed_name():
+    assert [n for n in pa.__all__ if not hasattr(pa, n)] == []

@@ -96,3 +96,43 @@ def test_overlapped_mixed_step_fp8_equals_serial_and_oracle():
     ref_p = oracle.prefill_chunk_fp8(p.query, kc8, vc8, p.block_tables, p.query_start_loc,
                                      p.seq_lens, Hkv, D, bs, case.scale, ks, vs, rows=rows)
     assert_close(upcast(serial_p)[rows], ref_p, "FP8 prefill in the mixed step")
+
+
+def _small_mixed():
+    from workloads import Spec, build_case
+
+    case = build_case(Spec(name="mixed", num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                           seed=(444, 85), decode_lens=[17, 200, 1, 64], prefill=[(100, 40)],
+                           prefill_new_tokens=True))
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    r = case.reshape
+    pa.reshape_and_cache(dev_u16(r.key), dev_u16(r.value), kc, vc, dev_i64(r.slot_mapping),
+                         num_kv_heads=2, head_dim=64, block_size=16)
+    p, d = case.prefill, case.decode
+    pre = dict(query=dev_u16(p.query), key_cache=kc, value_cache=vc,
+               block_tables=dev_i32(p.block_tables), query_start_loc=dev_i32(p.query_start_loc),
+               seq_lens=dev_i32(p.seq_lens), num_kv_heads=2, block_size=16, max_q_len=p.max_q_len,
+               max_seq_len=p.max_seq_len, scale=float(case.scale))
+    dec = dict(query=dev_u16(d.query), key_cache=kc, value_cache=vc,
+               block_tables=dev_i32(d.block_tables), seq_lens=dev_i32(d.seq_lens),
+               num_kv_heads=2, block_size=16, scale=float(case.scale), max_seq_len=d.max_seq_len)
+    return pre, dec
+
+
+def test_mixed_step_on_one_stream_equals_serial():
+    pre, dec = _small_mixed()
+    serial_p, serial_d = host_u16(pa.prefill_chunk(**pre)), host_u16(pa.decode(**dec))
+    pout, dout = pa.mixed_step(pre, dec, side_stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(pout), serial_p) and np.array_equal(host_u16(dout), serial_d)
+
+
+def test_mixed_step_validates_both_halves_before_launching():
+    pre, dec = _small_mixed()
+    sentinel = torch.full_like(dec["query"], 7.0)
+    dec["out"] = sentinel
+    pre["max_q_len"] = pre["max_seq_len"] + 1  # invalid: rejected on the host
+    with pytest.raises(pa.PagedAttentionError):
+        pa.mixed_step(pre, dec)
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all()), "the decode half ran although the prefill half was invalid"

@@ -555,3 +555,67 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         with monkeypatch.context() as m:
             m.setattr(pa, name, fake)
             assert not _pins_pass(), f"planted mistake {fake.__name__} went unnoticed"
+
+
+# ---------------------------------------------------------------- scalar brute force
+
+def _bf16_scalar(bits):
+    import struct
+    return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+
+def _scalar_kv(pool, b, h, o, d, Hkv, D, bs, kind):
+    """One cached element, read through the documented block layout (not the oracle's views)."""
+    tile = (b * Hkv + h) * bs * D
+    if kind == "k":
+        off = (o // 16) * 16 * D + (d // 32) * 512 + (o % 16) * 32 + d % 32
+    else:
+        off = (o // 16) * 16 * D + d * 16 + o % 16
+    return _bf16_scalar(pool.reshape(-1)[tile + off])
+
+
+def _scalar_attention(q_row, table, L, last_key, kc, vc, kvh, Hkv, D, bs, scale):
+    """softmax(scale * q.k) . v over keys 0..last_key, with plain loops and math.exp."""
+    scores = []
+    for p in range(last_key + 1):
+        b, o = int(table[p // bs]), p % bs
+        scores.append(scale * sum(q_row[d] * _scalar_kv(kc, b, kvh, o, d, Hkv, D, bs, "k")
+                                  for d in range(D)))
+    m = max(scores)
+    w = [math.exp(s - m) for s in scores]
+    tot = sum(w)
+    out = []
+    for d in range(D):
+        acc = 0.0
+        for p in range(last_key + 1):
+            b, o = int(table[p // bs]), p % bs
+            acc += w[p] * _scalar_kv(vc, b, kvh, o, d, Hkv, D, bs, "v")
+        out.append(acc / tot)
+    return out
+
+
+def test_oracle_matches_scalar_loops_on_tiny_cases():
+    # decode: four sequences over two blocks sizes' worth of positions, GQA 2
+    case = small_case(31, lens=(1, 7, 17, 40), Hq=4, Hkv=2, D=64, bs=16)
+    d = case.decode
+    ref = oracle_decode(case)
+    scale = float(case.scale)
+    for s in range(4):
+        L = int(d.seq_lens[s])
+        for h in range(4):
+            q_row = [_bf16_scalar(x) for x in d.query[s, h]]
+            got = _scalar_attention(q_row, d.block_tables[s], L, L - 1, case.key_cache,
+                                    case.value_cache, h // 2, 2, 64, 16, scale)
+            assert np.allclose(got, ref[s, h], rtol=1e-12, atol=1e-12)
+    # prefill chunk: 5 rows after 20 cached tokens, 32-token blocks, causal by loop bounds
+    case = build_case(Spec(name="p", num_q_heads=2, num_kv_heads=1, head_dim=32, block_size=32,
+                           seed=(32,), prefill=[(20, 5)]))
+    p = case.prefill
+    ref = pa.prefill_chunk(p.query, case.key_cache, case.value_cache, p.block_tables,
+                           p.query_start_loc, p.seq_lens, 1, 32, 32, case.scale)
+    for t in range(5):
+        for h in range(2):
+            q_row = [_bf16_scalar(x) for x in p.query[t, h]]
+            got = _scalar_attention(q_row, p.block_tables[0], 25, 20 + t, case.key_cache,
+                                    case.value_cache, 0, 1, 32, 32, float(case.scale))
+            assert np.allclose(got, ref[t, h], rtol=1e-12, atol=1e-12)

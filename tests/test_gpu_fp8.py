@@ -173,3 +173,47 @@ def test_prefill_fp8_shapes_and_ragged_chunks(Hq, Hkv, D, bs):
     ref = oracle.prefill_chunk_fp8(p.query, kc8, vc8, p.block_tables, p.query_start_loc,
                                    p.seq_lens, Hkv, D, bs, case.scale, 0.02, 0.03)
     assert_close(got, ref, f"FP8 prefill {Hq}/{Hkv}/{D}/{bs}")
+
+
+def test_fp8_nan_in_unused_slots_never_read():
+    """NaN codes (0x7F) in every slot past each sequence's length, in its last block and in all
+    unreferenced blocks, must not change decode or prefill outputs (bitwise)."""
+    Hkv, D, bs = 2, 64, 16
+    case = build_case(Spec(name="fp8nan", num_q_heads=8, num_kv_heads=Hkv, head_dim=D,
+                           block_size=bs, seed=(444, 76), decode_lens=[1, 15, 17, 40, 95],
+                           prefill=[(30, 7), (0, 20)]))
+    kc8 = oracle_quantize_pool(case.key_cache, 0.02)
+    vc8 = oracle_quantize_pool(case.value_cache, 0.03)
+    used = {}
+    d, p = case.decode, case.prefill
+    for tables, lens in ((d.block_tables, d.seq_lens), (p.block_tables, p.seq_lens)):
+        for row, L in zip(tables, lens):
+            for pos in range(int(L)):
+                used.setdefault(int(row[pos // bs]), set()).add(pos % bs)
+    kn, vn = kc8.copy(), vc8.copy()
+    for b in range(kc8.shape[0]):
+        for o in range(bs):
+            if o in used.get(b, ()):
+                continue
+            for h in range(Hkv):
+                kv = kn[b].reshape(Hkv, bs // 16, D // 32, 16, 32)
+                vv = vn[b].reshape(Hkv, bs // 16, D, 16)
+                kv[h, o // 16, :, o % 16, :] = 0x7F
+                vv[h, o // 16, :, o % 16] = 0x7F
+
+    def run(k, v):
+        dec = pa.decode_fp8(dev_u16(d.query), dev_u8(k), dev_u8(v), dev_i32(d.block_tables),
+                            dev_i32(d.seq_lens), num_kv_heads=Hkv, block_size=bs, k_scale=0.02,
+                            v_scale=0.03, scale=float(case.scale), max_seq_len=d.max_seq_len)
+        pre = pa.prefill_chunk_fp8(dev_u16(p.query), dev_u8(k), dev_u8(v), dev_i32(p.block_tables),
+                                   dev_i32(p.query_start_loc), dev_i32(p.seq_lens),
+                                   num_kv_heads=Hkv, block_size=bs, max_q_len=p.max_q_len,
+                                   max_seq_len=p.max_seq_len, k_scale=0.02, v_scale=0.03,
+                                   scale=float(case.scale))
+        torch.cuda.synchronize()
+        return host_u16(dec), host_u16(pre)
+
+    a_dec, a_pre = run(kc8, vc8)
+    b_dec, b_pre = run(kn, vn)
+    assert np.array_equal(a_dec, b_dec) and np.array_equal(a_pre, b_pre)
+    assert not np.isnan(upcast(b_dec)).any() and not np.isnan(upcast(b_pre)).any()

@@ -317,7 +317,8 @@ pa_status_t pa_prefill_chunk_fp8(void* out, const void* query, const void* key_c
  *
  *   prefill, decode  the arguments of pa_prefill_chunk / pa_decode (or their FP8 forms when
  *                    kv_fp8 is nonzero, with k_scale and v_scale); the two outputs and the two
- *                    workspaces must be distinct
+ *                    workspaces must be distinct.  A half with no sequences launches nothing
+ *                    and may pass null pointers, as the single calls allow
  *   stream           the caller's stream: both halves start after the work already on it, and
  *                    later work on it waits for both
  *   side_stream      a second stream of the same device at default priority; NULL or `stream`

@@ -767,7 +767,8 @@ extern "C" {
 pa_status_t pa_mixed_step(const pa_prefill_args* prefill, const pa_decode_args* decode,
                           void* stream, void* side_stream) {
   if (!prefill || !decode) return fail(PA_ERR_NULL_POINTER, "null argument struct");
-  if (decode->out == prefill->out)
+  // An empty half may pass null pointers; two real outputs must differ.
+  if (decode->out && decode->out == prefill->out)
     return fail(PA_ERR_INVALID_ARG, "the two halves must write different outputs");
   // Both halves are validated before either is launched.
   pa_status_t st = prefill_call(*prefill, stream, true);

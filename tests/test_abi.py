@@ -124,3 +124,32 @@ def test_argument_structs_match_the_header(tmp_path):
 
 def test_binding_exports_every_listed_name():
     assert [n for n in pa.__all__ if not hasattr(pa, n)] == []
+
+
+def test_mixed_step_with_empty_halves(lib):
+    """Empty halves (no sequences) may pass null pointers: with both empty the call succeeds on
+    one stream without launching anything; a bad shape in either half is still rejected, and two
+    real halves may not share an output."""
+    def prefill_args(num_seqs=0, head_dim=128, out=None):
+        return pa._PrefillArgs(out=out, num_blocks=16, num_seqs=num_seqs, total_q=num_seqs,
+                               max_q_len=num_seqs, num_q_heads=8, num_kv_heads=2,
+                               head_dim=head_dim, block_size=16, max_blocks_per_seq=4,
+                               max_seq_len=64, scale=0.125, k_scale=1.0, v_scale=1.0)
+
+    def decode_args(num_seqs=0, head_dim=128, out=None):
+        return pa._DecodeArgs(out=out, num_blocks=16, num_seqs=num_seqs, num_q_heads=8,
+                              num_kv_heads=2, head_dim=head_dim, block_size=16,
+                              max_blocks_per_seq=4, max_seq_len=64, scale=0.125, k_scale=1.0,
+                              v_scale=1.0)
+
+    def call(pf, dc):
+        return lib.pa_mixed_step(ctypes.byref(pf), ctypes.byref(dc), None, None)
+
+    assert call(prefill_args(), decode_args()) == 0, lib.pa_last_error()
+    assert call(prefill_args(head_dim=96), decode_args()) == 3  # unsupported head_dim
+    assert call(prefill_args(), decode_args(head_dim=96)) == 3
+    assert call(prefill_args(num_seqs=-1), decode_args()) == 2
+    # two real halves writing one buffer: rejected before either is looked at further
+    buf = ctypes.c_void_p(0x1000)
+    assert call(prefill_args(num_seqs=1, out=buf), decode_args(num_seqs=1, out=buf)) == 2
+    assert b"different outputs" in lib.pa_last_error()

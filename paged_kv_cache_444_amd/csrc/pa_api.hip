@@ -786,12 +786,14 @@ pa_status_t pa_mixed_step(const pa_prefill_args* prefill, const pa_decode_args* 
       (e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess)
     return hip_status(e, "mixed_step (fork)");
   // Decode first, so its persistent workgroups are resident before the chunk's fill the rest.
-  if ((st = decode_call(*decode, side_stream, false)) != PA_OK) return st;
-  if ((st = prefill_call(*prefill, stream, false)) != PA_OK) return st;
+  // Once the fork is recorded the join is always made, so later work on `stream` waits for
+  // whatever was launched on the side stream even when a launch fails.
+  st = decode_call(*decode, side_stream, false);
+  if (st == PA_OK) st = prefill_call(*prefill, stream, false);
   if ((e = hipEventRecord(join, side)) != hipSuccess ||
       (e = hipStreamWaitEvent(hs, join, 0)) != hipSuccess)
-    return hip_status(e, "mixed_step (join)");
-  return ok();
+    return st != PA_OK ? st : hip_status(e, "mixed_step (join)");
+  return st;
 }
 
 }  // extern "C"

@@ -146,3 +146,49 @@ def test_cascade_fp8_prefix_shared_rollouts():
     ref = oracle.decode_fp8(d.query, kc8, vc8, d.block_tables, d.seq_lens, case.num_kv_heads,
                             case.head_dim, case.block_size, case.scale, ks, vs, seqs=seqs)
     assert_close(upcast(got)[seqs], ref[seqs], "FP8 cascade decode cfg5")
+
+
+def _draw_cascade(seed):
+    """A supported shape, 1-5 groups of 1-12 sequences, each group's prompt 0-40 whole blocks
+    (shared when the group has several members), private tails of 0-400 tokens."""
+    rng = np.random.default_rng((444, 85, seed))
+    D = int(rng.choice([64, 128, 256]))
+    G = int(rng.choice([g for g in (1, 2, 4, 8, 16) if g * D <= 1024]))
+    Hkv = int(rng.choice([1, 2, 4, 8] if G <= 4 else [1, 2, 4]))
+    bs = int(rng.choice([16, 32]))
+    sizes = [int(rng.integers(1, 13)) for _ in range(int(rng.integers(1, 6)))]
+    prompts = [int(rng.integers(0, 41)) * bs for _ in sizes]
+    lens, shares, gs = [], [], [0]
+    for n, P in zip(sizes, prompts):
+        first = len(lens)
+        lens += [P + (0 if rng.random() < 0.2 else int(rng.integers(0, 401))) for _ in range(n)]
+        lens[-1] = max(lens[-1], 1)
+        if n > 1 and P > 0:
+            shares.append((list(range(first, first + n)), P))
+        gs.append(len(lens))
+    case = build_case(Spec(name=f"cascade_random{seed}", num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                           head_dim=D, block_size=bs, seed=(444, 86, seed), decode_lens=lens,
+                           share_groups=shares))
+    return case, gs, prompts
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cascade_random_groups(seed):
+    """Seeded random group layouts, bf16 and FP8 caches, against the oracle's plain decode."""
+    from helpers import dev_u8, oracle_quantize_pool
+
+    case, gs, prompts = _draw_cascade(seed)
+    d = case.decode
+    Hkv, D, bs = case.num_kv_heads, case.head_dim, case.block_size
+    say(f"cascade random {seed}: Hq={case.num_q_heads} Hkv={Hkv} D={D} bs={bs} groups={gs} "
+        f"prompts={prompts}")
+    got = upcast(_cascade(case, dev_u16(case.key_cache), dev_u16(case.value_cache), gs, prompts))
+    ref = oracle.decode(d.query, case.key_cache, case.value_cache, d.block_tables, d.seq_lens, Hkv,
+                        D, bs, case.scale)
+    assert_close(got, ref, f"cascade decode, random case {seed}")
+    ks, vs = 6.0 / 448.0, 5.5 / 448.0
+    kc8, vc8 = oracle_quantize_pool(case.key_cache, ks), oracle_quantize_pool(case.value_cache, vs)
+    got8 = upcast(_cascade(case, dev_u8(kc8), dev_u8(vc8), gs, prompts, fp8_scales=(ks, vs)))
+    ref8 = oracle.decode_fp8(d.query, kc8, vc8, d.block_tables, d.seq_lens, Hkv, D, bs, case.scale,
+                             ks, vs)
+    assert_close(got8, ref8, f"FP8 cascade decode, random case {seed}")

@@ -286,7 +286,7 @@ def main():
             "decode_prefetch": int(os.environ.get("PA_DECODE_PREFETCH", "1")),
             "decode_static_q10": int(os.environ.get("PA_DECODE_STATIC_Q10", "1024")),
             "decode_chunk_steps": int(os.environ.get("PA_DECODE_CHUNK", "4")),
-            "decode_step": "matrix cores" if os.environ.get("PA_DECODE_MFMA") == "1" else "vector",
+            "decode_step": "vector" if os.environ.get("PA_DECODE_MFMA") == "0" else "matrix cores",
         },
         "roofline": {
             "bound": "hbm", "kernel": "decode_kernel", "achieved": round(main_gbs, 1),

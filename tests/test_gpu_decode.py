@@ -19,6 +19,9 @@ from workloads import Spec, build_case
 
 pytestmark = pytest.mark.gpu
 
+# bf16 decode steps: "0" the vector step, "1" the matrix-core step (the default).
+STEPS = ["0", "1"]
+
 
 def say(msg):
     print(msg, flush=True)
@@ -144,25 +147,29 @@ def test_decode_many_short_sequences_and_wide_batch():
     assert_close(got, oracle_decode(case, case.key_cache, case.value_cache), "700 short sequences")
 
 
+@pytest.mark.parametrize("step", STEPS)
 @pytest.mark.parametrize("workers", [4, 12, 64])
-def test_decode_few_workers_long_ranges(workers, monkeypatch):
+def test_decode_few_workers_long_ranges(workers, step, monkeypatch):
     """Few worker waves: each wave streams hundreds of steps, crossing the 64-block id window and
     several unit boundaries; results must not depend on the worker count beyond rounding."""
     case = build_case(Spec(name="few", num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
                            seed=(25,), decode_lens=[3000, 1, 2049, 4100, 17, 1500]))
     kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
     monkeypatch.setenv("PA_DECODE_WORKERS", str(workers))
+    monkeypatch.setenv("PA_DECODE_MFMA", step)
     got = upcast(gpu_decode(case, kc, vc))
     assert_close(got, oracle_decode(case, case.key_cache, case.value_cache), f"{workers} workers")
 
 
+@pytest.mark.parametrize("step", STEPS)
 @pytest.mark.parametrize("static_q10,chunk", [(1024, 4), (768, 4), (512, 1), (640, 16)])
-def test_decode_static_and_dynamic_splits(static_q10, chunk, monkeypatch):
+def test_decode_static_and_dynamic_splits(static_q10, chunk, step, monkeypatch):
     """The share of statically split steps and the dynamic chunk size change only how work is
     handed out: every split must match the oracle, and one workspace is reused across calls."""
     case = cached_named_case(2)
     monkeypatch.setenv("PA_DECODE_STATIC_Q10", str(static_q10))
     monkeypatch.setenv("PA_DECODE_CHUNK", str(chunk))
+    monkeypatch.setenv("PA_DECODE_MFMA", step)
     d = case.decode
     kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
     q, bt, sl = dev_u16(d.query), dev_i32(d.block_tables), dev_i32(d.seq_lens)
@@ -184,7 +191,8 @@ def test_decode_static_and_dynamic_splits(static_q10, chunk, monkeypatch):
 @pytest.mark.parametrize("Hq,Hkv,D,bs", [(16, 1, 64, 16), (8, 2, 128, 32), (8, 2, 256, 16),
                                           (4, 4, 128, 16)])
 @pytest.mark.parametrize("chunk", [1, 3, 16])
-def test_decode_shared_chunks_shapes(Hq, Hkv, D, bs, chunk, monkeypatch):
+@pytest.mark.parametrize("step", STEPS)
+def test_decode_shared_chunks_shapes(Hq, Hkv, D, bs, chunk, step, monkeypatch):
     """Dynamic chunks are shared by a workgroup's waves (some idle when a piece has fewer steps
     than waves) and combined in LDS: every head shape must match the oracle, deterministically."""
     case = build_case(Spec(name="shared", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
@@ -194,6 +202,7 @@ def test_decode_shared_chunks_shapes(Hq, Hkv, D, bs, chunk, monkeypatch):
     monkeypatch.setenv("PA_DECODE_WORKERS", "8")
     monkeypatch.setenv("PA_DECODE_STATIC_Q10", "600")
     monkeypatch.setenv("PA_DECODE_CHUNK", str(chunk))
+    monkeypatch.setenv("PA_DECODE_MFMA", step)
     a = gpu_decode(case, kc, vc)
     assert np.array_equal(a, gpu_decode(case, kc, vc))
     assert_close(upcast(a), oracle_decode(case, case.key_cache, case.value_cache),
@@ -203,7 +212,8 @@ def test_decode_shared_chunks_shapes(Hq, Hkv, D, bs, chunk, monkeypatch):
 @pytest.mark.parametrize("Hq,Hkv,D,bs,workers", [(32, 8, 128, 16, None), (16, 4, 256, 32, "8"),
                                                  (32, 8, 64, 16, "12"), (8, 2, 128, 16, None),
                                                  (16, 4, 128, 32, "4")])
-def test_decode_head_quads(Hq, Hkv, D, bs, workers, monkeypatch):
+@pytest.mark.parametrize("step", STEPS)
+def test_decode_head_quads(Hq, Hkv, D, bs, workers, step, monkeypatch):
     """Workgroup workers over units of four KV heads (a wave per head, the four reading the same
     block together) change only how steps are handed out: every shape must match the oracle,
     deterministically, with the merge kernel combining units split between workgroups."""
@@ -212,6 +222,7 @@ def test_decode_head_quads(Hq, Hkv, D, bs, workers, monkeypatch):
                            decode_lens=[1, 17, 300, 1000, 2049, 5, 640, 0, 3000]))
     kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
     monkeypatch.setenv("PA_DECODE_QUAD", "1")
+    monkeypatch.setenv("PA_DECODE_MFMA", step)
     if workers:
         monkeypatch.setenv("PA_DECODE_WORKERS", workers)
     a = gpu_decode(case, kc, vc)

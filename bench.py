@@ -148,7 +148,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(this build runs on a single GPU: run with --gpus 1)", file=sys.stderr)
+              f"(the library's path runs on a single GPU: run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

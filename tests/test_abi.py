@@ -153,3 +153,16 @@ def test_mixed_step_with_empty_halves(lib):
     buf = ctypes.c_void_p(0x1000)
     assert call(prefill_args(num_seqs=1, out=buf), decode_args(num_seqs=1, out=buf)) == 2
     assert b"different outputs" in lib.pa_last_error()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says so, before any GPU
+    or library work."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""

@@ -60,6 +60,31 @@ int32_t pa_version(void);
 const char* pa_last_error(void);
 
 /*
+ * Launch tunables, for sweeps and tests: they change how work is spread over the GPU, never what
+ * is computed beyond fp32 rounding order.  Each starts from its default, or from the environment
+ * variable of the same name if that holds an in-range integer; the environment is read once, at
+ * the first call that needs a tunable.  Values are process-wide (all threads and devices); a call
+ * uses the values current when it is made.
+ *   PA_DECODE_PREFETCH      0-2, default 1: K/V steps in flight per wave on the vector step
+ *   PA_DECODE_PREFETCH_FP8  1-2, default 1: the same for FP8 pools
+ *   PA_DECODE_MFMA          0-1, default 1: bf16 decode steps on the matrix cores (0: vector ALUs)
+ *   PA_DECODE_QUAD          0-1, default 1: workgroup workers over units of four KV heads
+ *   PA_DECODE_PIECE_COST    0-64, default 6: steps' worth of cost per unit a decode worker starts
+ *   PA_DECODE_WORKERS       default 0 (one workgroup of four waves per CU): total decode worker
+ *                           waves, rounded down to a multiple of 4 and capped at what can be
+ *                           resident; values below 4 mean the default
+ *   PA_DECODE_STATIC_Q10    512-1024, default 1024: share (in 1/1024) of decode steps split
+ *                           statically; the rest is handed out in dynamic chunks
+ *   PA_DECODE_CHUNK         1-256, default 4: smallest dynamic chunk, in steps
+ *   PA_PREFILL_SPLITS       0-16, default 0 (automatic): forced context split of a prefill chunk
+ * The decode workspace size depends on PA_DECODE_WORKERS: query it after setting that.
+ * pa_set_tunable returns PA_ERR_INVALID_ARG for an unknown name or an out-of-range value (the
+ * value is then unchanged); pa_get_tunable writes the current value to *value.
+ */
+pa_status_t pa_set_tunable(const char* name, int32_t value);
+pa_status_t pa_get_tunable(const char* name, int32_t* value);
+
+/*
  * pa_reshape_and_cache — write the K/V rows of new tokens into their cache slots.
  *
  * Source: blocks fill as tokens arrive and a sequence that outgrows its blocks gets one more
@@ -316,9 +341,10 @@ pa_status_t pa_prefill_chunk_fp8(void* out, const void* query, const void* key_c
  * call).  Write every new token's K/V first (pa_reshape_and_cache on `stream`).
  *
  *   prefill, decode  the arguments of pa_prefill_chunk / pa_decode (or their FP8 forms when
- *                    kv_fp8 is nonzero, with k_scale and v_scale); the two outputs and the two
- *                    workspaces must be distinct.  A half with no sequences launches nothing
- *                    and may pass null pointers, as the single calls allow
+ *                    kv_fp8 is nonzero, with k_scale and v_scale).  The two outputs and the
+ *                    workspace bytes each half uses (its *_workspace_bytes query) must not
+ *                    overlap one another: PA_ERR_INVALID_ARG otherwise.  A half with no sequences
+ *                    launches nothing and may pass null pointers, as the single calls allow
  *   stream           the caller's stream: both halves start after the work already on it, and
  *                    later work on it waits for both
  *   side_stream      a second stream of the same device at default priority; NULL or `stream`

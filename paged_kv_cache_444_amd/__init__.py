@@ -20,7 +20,7 @@ __all__ = [
     "decode_fp8", "decode_cascade", "decode_cascade_fp8", "decode_cascade_workspace_bytes",
     "prefill_chunk", "prefill_chunk_fp8", "mixed_step", "decode_workspace_bytes",
     "prefill_workspace_bytes", "stream_read", "trace_enable", "trace_read", "PagedAttentionError",
-    "pool_shape", "LIB_PATH",
+    "pool_shape", "LIB_PATH", "set_tunable", "get_tunable", "tunables", "TUNABLES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -91,6 +91,8 @@ _SIGNATURES = {
     "pa_stream_read": (_I32, [_P, _SZ, _P, _SZ, _P]),
     "pa_mixed_step": (_I32, [ctypes.POINTER(_PrefillArgs), ctypes.POINTER(_DecodeArgs), _P, _P]),
     "pa_trace_enable": (_I32, [_I32]),
+    "pa_set_tunable": (_I32, [ctypes.c_char_p, _I32]),
+    "pa_get_tunable": (_I32, [ctypes.c_char_p, ctypes.POINTER(_I32)]),
     "pa_trace_read": (_I32, [ctypes.c_char_p, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double)]),
 }
 
@@ -141,10 +143,53 @@ def pool_shape(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: in
     return (num_blocks, num_kv_heads * block_size * head_dim)
 
 
-def _num_blocks(pool: torch.Tensor, num_kv_heads: int, block_size: int, head_dim: int) -> int:
-    """Whole blocks the pool holds for this shape (the library validates the shape itself)."""
-    per = max(num_kv_heads * block_size * head_dim, 1)
-    return max(pool.numel() // per, 1)
+def _num_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, num_kv_heads: int,
+                block_size: int, head_dim: int) -> int:
+    """Whole blocks both pools hold for this shape (the smaller of the two, so neither is read or
+    written past its end).  Element counts are the same for bf16 and FP8 pools."""
+    per = num_kv_heads * block_size * head_dim
+    if per <= 0:
+        raise ValueError("num_kv_heads, block_size and head_dim must be positive")
+    n = min(key_cache.numel(), value_cache.numel()) // per
+    if n < 1:
+        raise ValueError(f"the pools must hold at least one block of {per} elements "
+                         f"(key_cache {key_cache.numel()}, value_cache {value_cache.numel()})")
+    return n
+
+
+def _rows(t: torch.Tensor, n: int, name: str, *, dim0: Optional[int] = None) -> None:
+    """Raise ValueError unless `t` has n elements (dim0 None) or n rows (dim0 = expected ndim)."""
+    if dim0 is None:
+        if t.numel() != n:
+            raise ValueError(f"{name} must hold {n} entries (got {t.numel()})")
+    elif t.dim() != dim0 or t.shape[0] != n:
+        raise ValueError(f"{name} must be {dim0}-D with {n} rows (got shape {tuple(t.shape)})")
+
+
+def _out_like(out: Optional[torch.Tensor], query: torch.Tensor) -> torch.Tensor:
+    if out is None:
+        return torch.empty_like(query)
+    if out.shape != query.shape or out.element_size() != 2:
+        raise ValueError(f"out must be a 16-bit tensor of the query's shape {tuple(query.shape)} "
+                         f"(got {tuple(out.shape)}, {out.dtype})")
+    return out
+
+
+def _decode_shapes(query, block_tables, seq_lens) -> None:
+    if query.dim() != 3:
+        raise ValueError("query must be [num_seqs][num_q_heads][head_dim]")
+    B = query.shape[0]
+    _rows(seq_lens, B, "seq_lens")
+    _rows(block_tables, B, "block_tables", dim0=2)
+
+
+def _prefill_shapes(query, block_tables, query_start_loc, seq_lens) -> int:
+    if query.dim() != 3:
+        raise ValueError("query must be [total_q][num_q_heads][head_dim]")
+    n = seq_lens.numel()
+    _rows(query_start_loc, n + 1, "query_start_loc")
+    _rows(block_tables, n, "block_tables", dim0=2)
+    return n
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
@@ -155,7 +200,7 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
     T = slot_mapping.numel()
     if key.shape != value.shape or key.numel() != T * num_kv_heads * head_dim:
         raise ValueError("key/value must be [T][num_kv_heads][head_dim]")
-    n = _num_blocks(key_cache, num_kv_heads, block_size, head_dim)
+    n = _num_blocks(key_cache, value_cache, num_kv_heads, block_size, head_dim)
     _check(lib.pa_reshape_and_cache(_bf16(key, "key"), _bf16(value, "value"), num_kv_heads * head_dim,
                                     _bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache"),
                                     _ints(slot_mapping, torch.int64, "slot_mapping"), T, num_kv_heads,
@@ -168,11 +213,6 @@ def _fp8_pool(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
-def _num_blocks_fp8(pool: torch.Tensor, num_kv_heads: int, block_size: int, head_dim: int) -> int:
-    per = max(num_kv_heads * block_size * head_dim, 1)
-    return max(pool.numel() // per, 1)
-
-
 def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
                           value_cache: torch.Tensor, slot_mapping: torch.Tensor, *, num_kv_heads: int,
                           head_dim: int, block_size: int, k_scale: float, v_scale: float) -> None:
@@ -181,7 +221,7 @@ def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: tor
     T = slot_mapping.numel()
     if key.shape != value.shape or key.numel() != T * num_kv_heads * head_dim:
         raise ValueError("key/value must be [T][num_kv_heads][head_dim]")
-    n = _num_blocks_fp8(key_cache, num_kv_heads, block_size, head_dim)
+    n = _num_blocks(key_cache, value_cache, num_kv_heads, block_size, head_dim)
     _check(lib.pa_reshape_and_cache_fp8(_bf16(key, "key"), _bf16(value, "value"),
                                         num_kv_heads * head_dim, _fp8_pool(key_cache, "key_cache"),
                                         _fp8_pool(value_cache, "value_cache"),
@@ -196,7 +236,7 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_mappin
     lib = load_library()
     if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [n][2]")
-    n = _num_blocks(key_cache, num_kv_heads, block_size, head_dim)
+    n = _num_blocks(key_cache, value_cache, num_kv_heads, block_size, head_dim)
     _check(lib.pa_copy_blocks(_bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache"), n,
                               _ints(block_mapping, torch.int64, "block_mapping"),
                               block_mapping.shape[0], num_kv_heads, head_dim, block_size, _stream()))
@@ -236,16 +276,16 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     `max_seq_len` must bound seq_lens; if omitted it is read back from the device (a sync).
     """
     lib = load_library()
+    _decode_shapes(query, block_tables, seq_lens)
     B, Hq, D = query.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if B else 0
-    if out is None:
-        out = torch.empty_like(query)
+    out = _out_like(out, query)
+    n = _num_blocks(key_cache, value_cache, num_kv_heads, block_size, D)
     ws, ws_bytes = _workspace(decode_workspace_bytes(B, Hq, num_kv_heads, D, max_seq_len), workspace,
                               query.device)
-    n = _num_blocks(key_cache, num_kv_heads, block_size, D)
     _check(lib.pa_decode(_bf16(out, "out"), _bf16(query, "query"), _bf16(key_cache, "key_cache"),
                          _bf16(value_cache, "value_cache"), n,
                          _ints(block_tables, torch.int32, "block_tables"),
@@ -261,16 +301,16 @@ def decode_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.
                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged decode over uint8 pools of E4M3 codes (written by reshape_and_cache_fp8)."""
     lib = load_library()
+    _decode_shapes(query, block_tables, seq_lens)
     B, Hq, D = query.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if B else 0
-    if out is None:
-        out = torch.empty_like(query)
+    out = _out_like(out, query)
+    n = _num_blocks(key_cache, value_cache, num_kv_heads, block_size, D)
     ws, ws_bytes = _workspace(decode_workspace_bytes(B, Hq, num_kv_heads, D, max_seq_len), workspace,
                               query.device)
-    n = _num_blocks_fp8(key_cache, num_kv_heads, block_size, D)
     _check(lib.pa_decode_fp8(_bf16(out, "out"), _bf16(query, "query"),
                              _fp8_pool(key_cache, "key_cache"), _fp8_pool(value_cache, "value_cache"),
                              n, _ints(block_tables, torch.int32, "block_tables"),
@@ -292,20 +332,23 @@ def _cascade(fp8: bool, query, key_cache, value_cache, block_tables, seq_lens, g
              prefix_lens, *, max_prefix_len, max_group_size, num_kv_heads, block_size, scale,
              max_seq_len, out, workspace, k_scale=1.0, v_scale=1.0):
     lib = load_library()
+    _decode_shapes(query, block_tables, seq_lens)
     B, Hq, D = query.shape
     n_groups = group_start.numel() - 1
+    if n_groups < 1 and B > 0:
+        raise ValueError("group_start must hold num_groups + 1 >= 2 entries")
+    _rows(prefix_lens, B, "prefix_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if B else 0
-    if out is None:
-        out = torch.empty_like(query)
+    out = _out_like(out, query)
     nbytes = decode_cascade_workspace_bytes(B, n_groups, max_group_size, Hq, num_kv_heads, D,
                                             max_prefix_len)
     ws, ws_bytes = _workspace(nbytes, workspace, query.device)
     pools = ((_fp8_pool(key_cache, "key_cache"), _fp8_pool(value_cache, "value_cache")) if fp8 else
              (_bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache")))
-    n = (_num_blocks_fp8 if fp8 else _num_blocks)(key_cache, num_kv_heads, block_size, D)
+    n = _num_blocks(key_cache, value_cache, num_kv_heads, block_size, D)
     args = [_bf16(out, "out"), _bf16(query, "query"), *pools, n,
             _ints(block_tables, torch.int32, "block_tables"), _ints(seq_lens, torch.int32, "seq_lens"),
             _ints(group_start, torch.int32, "group_start"),
@@ -357,15 +400,14 @@ def prefill_chunk(query: torch.Tensor, key_cache: torch.Tensor, value_cache: tor
                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal chunked-prefill attention: query [total_q][Hq][D] -> out [total_q][Hq][D] bf16."""
     lib = load_library()
+    n = _prefill_shapes(query, block_tables, query_start_loc, seq_lens)
     total_q, Hq, D = query.shape
-    n = seq_lens.numel()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(query)
+    out = _out_like(out, query)
+    nb = _num_blocks(key_cache, value_cache, num_kv_heads, block_size, D)
     ws, ws_bytes = _workspace(prefill_workspace_bytes(n, total_q, max_q_len, Hq, num_kv_heads, D,
                                                       max_seq_len), workspace, query.device)
-    nb = _num_blocks(key_cache, num_kv_heads, block_size, D)
     _check(lib.pa_prefill_chunk(_bf16(out, "out"), _bf16(query, "query"), _bf16(key_cache, "key_cache"),
                                 _bf16(value_cache, "value_cache"), nb,
                                 _ints(block_tables, torch.int32, "block_tables"),
@@ -416,16 +458,13 @@ def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None, fp8: bool 
     p, d = dict(prefill), dict(decode_call)
     # prefill half
     pq = p["query"]
+    n_p = _prefill_shapes(pq, p["block_tables"], p["query_start_loc"], p["seq_lens"])
     total_q, Hq, D = pq.shape
-    n_p = p["seq_lens"].numel()
-    pout = p.get("out")
-    if pout is None:
-        pout = torch.empty_like(pq)
+    pout = _out_like(p.get("out"), pq)
     pws_t, pws, pws_bytes = _owned_workspace(
         prefill_workspace_bytes(n_p, total_q, p["max_q_len"], Hq, p["num_kv_heads"], D,
                                 p["max_seq_len"]), p.get("workspace"), pq.device)
-    nb = (_num_blocks_fp8 if fp8 else _num_blocks)(p["key_cache"], p["num_kv_heads"],
-                                                   p["block_size"], D)
+    nb = _num_blocks(p["key_cache"], p["value_cache"], p["num_kv_heads"], p["block_size"], D)
     pk, pv = _pools(p["key_cache"], p["value_cache"], fp8)
     pa_args = _PrefillArgs(
         _bf16(pout, "out"), _bf16(pq, "query"), pk, pv, nb,
@@ -437,18 +476,16 @@ def mixed_step(prefill: dict, decode_call: dict, *, side_stream=None, fp8: bool 
         float(p.get("v_scale", 1.0)), pws, pws_bytes)
     # decode half
     dq = d["query"]
+    _decode_shapes(dq, d["block_tables"], d["seq_lens"])
     B, dHq, dD = dq.shape
     max_len = d.get("max_seq_len")
     if max_len is None:
         max_len = int(d["seq_lens"].max().item()) if B else 0
-    dout = d.get("out")
-    if dout is None:
-        dout = torch.empty_like(dq)
+    dout = _out_like(d.get("out"), dq)
     dws_t, dws, dws_bytes = _owned_workspace(
         decode_workspace_bytes(B, dHq, d["num_kv_heads"], dD, max_len), d.get("workspace"),
         dq.device)
-    dnb = (_num_blocks_fp8 if fp8 else _num_blocks)(d["key_cache"], d["num_kv_heads"],
-                                                    d["block_size"], dD)
+    dnb = _num_blocks(d["key_cache"], d["value_cache"], d["num_kv_heads"], d["block_size"], dD)
     dk, dv = _pools(d["key_cache"], d["value_cache"], fp8)
     de_args = _DecodeArgs(
         _bf16(dout, "out"), _bf16(dq, "query"), dk, dv, dnb,
@@ -474,15 +511,14 @@ def prefill_chunk_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache:
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Chunked-prefill attention over uint8 pools of E4M3 codes (reshape_and_cache_fp8)."""
     lib = load_library()
+    n = _prefill_shapes(query, block_tables, query_start_loc, seq_lens)
     total_q, Hq, D = query.shape
-    n = seq_lens.numel()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(query)
+    out = _out_like(out, query)
+    nb = _num_blocks(key_cache, value_cache, num_kv_heads, block_size, D)
     ws, ws_bytes = _workspace(prefill_workspace_bytes(n, total_q, max_q_len, Hq, num_kv_heads, D,
                                                       max_seq_len), workspace, query.device)
-    nb = _num_blocks_fp8(key_cache, num_kv_heads, block_size, D)
     _check(lib.pa_prefill_chunk_fp8(_bf16(out, "out"), _bf16(query, "query"),
                                     _fp8_pool(key_cache, "key_cache"),
                                     _fp8_pool(value_cache, "value_cache"), nb,
@@ -518,3 +554,44 @@ def trace_read(kernel_name: str):
     ms = ctypes.c_double()
     _check(load_library().pa_trace_read(kernel_name.encode(), ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+# Launch tunables of the library (include/pa.h): they change how work is spread over the GPU,
+# never what is computed beyond fp32 rounding order.
+TUNABLES = ("PA_DECODE_PREFETCH", "PA_DECODE_PREFETCH_FP8", "PA_DECODE_MFMA", "PA_DECODE_QUAD",
+            "PA_DECODE_PIECE_COST", "PA_DECODE_WORKERS", "PA_DECODE_STATIC_Q10", "PA_DECODE_CHUNK",
+            "PA_PREFILL_SPLITS")
+
+
+def set_tunable(name: str, value: int) -> None:
+    """Set a launch tunable (PagedAttentionError for an unknown name or out-of-range value)."""
+    _check(load_library().pa_set_tunable(name.encode(), int(value)))
+
+
+def get_tunable(name: str) -> int:
+    v = _I32()
+    _check(load_library().pa_get_tunable(name.encode(), ctypes.byref(v)))
+    return v.value
+
+
+class tunables:
+    """Context manager: set launch tunables for a block, then restore their previous values.
+
+        with pa.tunables(PA_DECODE_WORKERS=8, PA_DECODE_MFMA=0):
+            pa.decode(...)
+    """
+
+    def __init__(self, **values: int):
+        self._values = values
+        self._saved = {}
+
+    def __enter__(self):
+        for k, v in self._values.items():
+            self._saved[k] = get_tunable(k)
+            set_tunable(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self._saved.items():
+            set_tunable(k, v)
+        return False

@@ -48,7 +48,6 @@
 
 #include <algorithm>
 #include <type_traits>
-#include <cstdlib>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -1160,34 +1159,33 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   }
 }
 
-// Prefetch depth of the decode kernel: PA_DECODE_PREFETCH=0, 1 or 2 (default 1).
-int prefetch_depth() {
-  const char* e = std::getenv("PA_DECODE_PREFETCH");
-  const int v = e ? std::atoi(e) : 1;
-  return (v == 0 || v == 2) ? v : 1;
-}
+// Which decode_kernel instantiation a call launches.  FP8 pools always run on the matrix-core
+// step, with prefetch depth 1 or 2.  bf16 pools run on the matrix-core step by default:
+// offloading the products frees the vector issue slots the bf16 step spends most of its time
+// in, which at the 70B shape makes the kernel about 2 % faster; the vector step (prefetch depth
+// 0, 1 or 2) stays selectable.
+enum class Variant { kFp8Depth1, kFp8Depth2, kBf16Mfma, kVecDepth0, kVecDepth1, kVecDepth2 };
 
-// Prefetch depth of the FP8 decode kernel: PA_DECODE_PREFETCH_FP8=1 or 2 (default 1).
-int prefetch_depth_fp8() {
-  const char* e = std::getenv("PA_DECODE_PREFETCH_FP8");
-  const int v = e ? std::atoi(e) : 1;
-  return v == 2 ? 2 : 1;
-}
-
-// bf16 pools on the matrix-core step (the default; PA_DECODE_MFMA=0 selects the vector step).
-// Offloading the products frees the vector issue slots the bf16 step spends most of its time
-// in, which at the 70B shape makes the kernel about 2 % faster.
-bool bf16_on_matrix_cores() {
-  const char* e = std::getenv("PA_DECODE_MFMA");
-  return !(e && *e && std::atoi(e) == 0);
+Variant variant(bool fp8) {
+  if (fp8) return tunable(kTuneDecodePrefetchFp8) == 2 ? Variant::kFp8Depth2 : Variant::kFp8Depth1;
+  if (tunable(kTuneDecodeMfma)) return Variant::kBf16Mfma;
+  switch (tunable(kTuneDecodePrefetch)) {
+    case 0: return Variant::kVecDepth0;
+    case 2: return Variant::kVecDepth2;
+    default: return Variant::kVecDepth1;
+  }
 }
 
 template <int D, int G>
-const void* kernel_ptr() {
-  switch (prefetch_depth()) {
-    case 0: return reinterpret_cast<const void*>(&decode_kernel<D, G, 0, false>);
-    case 1: return reinterpret_cast<const void*>(&decode_kernel<D, G, 1, false>);
-    default: return reinterpret_cast<const void*>(&decode_kernel<D, G, 2, false>);
+const void* kernel_of(Variant v) {
+  switch (v) {
+    case Variant::kFp8Depth1: return reinterpret_cast<const void*>(&decode_kernel<D, G, 1, true>);
+    case Variant::kFp8Depth2: return reinterpret_cast<const void*>(&decode_kernel<D, G, 2, true>);
+    case Variant::kBf16Mfma:
+      return reinterpret_cast<const void*>(&decode_kernel<D, G, 1, false, true>);
+    case Variant::kVecDepth0: return reinterpret_cast<const void*>(&decode_kernel<D, G, 0, false>);
+    case Variant::kVecDepth2: return reinterpret_cast<const void*>(&decode_kernel<D, G, 2, false>);
+    default: return reinterpret_cast<const void*>(&decode_kernel<D, G, 1, false>);
   }
 }
 
@@ -1197,26 +1195,25 @@ hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
     TraceScope t("decode_partition", stream);
     const dim3 grid(p.num_workers / kWaves), block(kThreads);
     const size_t lds = p.dyn_cap > 0 ? (size_t)(p.num_seqs + 1) * 4 : 0;
-    if (p.kv_fp8) {
-      // FP8 steps carry half the bytes: prefetch depth 1 or 2.
-      if (prefetch_depth_fp8() == 2)
-        hipLaunchKernelGGL((decode_kernel<D, G, 2, true>), grid, block, lds, stream, p);
-      else
+    switch (variant(p.kv_fp8 != 0)) {
+      case Variant::kFp8Depth1:
         hipLaunchKernelGGL((decode_kernel<D, G, 1, true>), grid, block, lds, stream, p);
-    } else if (bf16_on_matrix_cores()) {
-      hipLaunchKernelGGL((decode_kernel<D, G, 1, false, true>), grid, block, lds, stream, p);
-    } else {
-      switch (prefetch_depth()) {
-        case 0:
-          hipLaunchKernelGGL((decode_kernel<D, G, 0, false>), grid, block, lds, stream, p);
-          break;
-        case 1:
-          hipLaunchKernelGGL((decode_kernel<D, G, 1, false>), grid, block, lds, stream, p);
-          break;
-        default:
-          hipLaunchKernelGGL((decode_kernel<D, G, 2, false>), grid, block, lds, stream, p);
-          break;
-      }
+        break;
+      case Variant::kFp8Depth2:
+        hipLaunchKernelGGL((decode_kernel<D, G, 2, true>), grid, block, lds, stream, p);
+        break;
+      case Variant::kBf16Mfma:
+        hipLaunchKernelGGL((decode_kernel<D, G, 1, false, true>), grid, block, lds, stream, p);
+        break;
+      case Variant::kVecDepth0:
+        hipLaunchKernelGGL((decode_kernel<D, G, 0, false>), grid, block, lds, stream, p);
+        break;
+      case Variant::kVecDepth2:
+        hipLaunchKernelGGL((decode_kernel<D, G, 2, false>), grid, block, lds, stream, p);
+        break;
+      default:
+        hipLaunchKernelGGL((decode_kernel<D, G, 1, false>), grid, block, lds, stream, p);
+        break;
     }
   }
   hipError_t e = hipGetLastError();
@@ -1263,16 +1260,17 @@ Ret dispatch(int D, int G, Ret fallback, F&& f) {
 
 }  // namespace
 
-int decode_workers(int head_dim, int group) {
+int decode_workers(int head_dim, int group, bool fp8) {
   static std::mutex mu;
-  // (device, variant) -> (default workgroups, resident workgroups)
+  // (device, shape, launched variant) -> (default workgroups, resident workgroups)
   static std::map<std::pair<int, int>, std::pair<int, int>> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const Variant v = variant(fp8);
   std::pair<int, int> blocks{0, 0};
   {
     std::lock_guard<std::mutex> lk(mu);
-    const auto key = std::make_pair(dev, (head_dim * 64 + group) * 4 + prefetch_depth());
+    const auto key = std::make_pair(dev, (head_dim * 64 + group) * 8 + (int)v);
     auto it = cache.find(key);
     if (it != cache.end()) {
       blocks = it->second;
@@ -1280,8 +1278,9 @@ int decode_workers(int head_dim, int group) {
       int cus = 0, per_cu = 0;
       if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
+      // Residency of the instantiation this call launches.
       const void* fn = dispatch(head_dim, group, (const void*)nullptr,
-                                []<int D, int G>() { return kernel_ptr<D, G>(); });
+                                [v]<int D, int G>() { return kernel_of<D, G>(v); });
       if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads,
                                                               kPrefixLdsBytes) != hipSuccess)
         return 0;
@@ -1293,28 +1292,31 @@ int decode_workers(int head_dim, int group) {
       cache[key] = blocks;
     }
   }
-  // Tuning and test override, read on every call: the total number of worker waves, at most
-  // what can be resident.
-  if (const char* e = std::getenv("PA_DECODE_WORKERS"); e && *e) {
-    const int v = std::atoi(e);
-    if (v >= kWaves) return std::min(v / kWaves, blocks.second) * kWaves;
-  }
+  // Tuning and test override: the total number of worker waves, at most what can be resident.
+  if (const int w = tunable(kTuneDecodeWorkers); w >= kWaves)
+    return std::min(w / kWaves, blocks.second) * kWaves;
   return blocks.first * kWaves;
 }
 
-DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group) {
+DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group, bool fp8) {
   DecodeWorkspace ws{};
-  ws.workers = decode_workers(head_dim, group);
-  if (ws.workers <= 0 || num_seqs <= 0) return ws;
+  ws.workers = decode_workers(head_dim, group, fp8);
+  // The size covers the worker count of either pool type, so one query serves both.
+  const int most = std::max(decode_workers(head_dim, group, !fp8), ws.workers);
+  if (ws.workers <= 0 || most <= 0 || num_seqs <= 0) {
+    ws.workers = 0;
+    return ws;
+  }
   // Dynamic chunks need the per-sequence prefix in LDS: batches up to kMaxPrefixSeqs.
   ws.dyn_cap = num_seqs <= kMaxPrefixSeqs ? kDynSlotsPerWorker * ws.workers : 0;
+  const int most_dyn = num_seqs <= kMaxPrefixSeqs ? kDynSlotsPerWorker * most : 0;
   const size_t units = (size_t)num_seqs * num_kv_heads;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   ws.counter_off = 0;
   ws.info_off = 256;
   ws.partials_off = ws.info_off + up(units * sizeof(int2));
   ws.bytes = ws.partials_off +
-             ((size_t)ws.workers + ws.dyn_cap + units) * group * (2 + head_dim) * sizeof(float);
+             ((size_t)most + most_dyn + units) * group * (2 + head_dim) * sizeof(float);
   return ws;
 }
 

@@ -128,9 +128,74 @@ TraceScope::~TraceScope() {
 
 }  // namespace pa
 
+namespace {
+
+// Launch tunables: name, default, allowed range.  The environment is read once, when the table is
+// first used; pa_set_tunable changes a value afterwards.
+struct TunableDef {
+  const char* name;
+  int dflt, lo, hi;
+};
+constexpr TunableDef kTunableDefs[pa::kNumTunables] = {
+    {"PA_DECODE_PREFETCH", 1, 0, 2},    {"PA_DECODE_PREFETCH_FP8", 1, 1, 2},
+    {"PA_DECODE_MFMA", 1, 0, 1},        {"PA_DECODE_QUAD", 1, 0, 1},
+    {"PA_DECODE_PIECE_COST", 6, 0, 64}, {"PA_DECODE_WORKERS", 0, 0, 1 << 20},
+    {"PA_DECODE_STATIC_Q10", 1024, 512, 1024}, {"PA_DECODE_CHUNK", 4, 1, 256},
+    {"PA_PREFILL_SPLITS", 0, 0, 16},
+};
+
+std::atomic<int>* tunable_values() {
+  static std::atomic<int> values[pa::kNumTunables];
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (int i = 0; i < pa::kNumTunables; ++i) {
+      const TunableDef& d = kTunableDefs[i];
+      int v = d.dflt;
+      if (const char* e = std::getenv(d.name); e && *e) {
+        char* end = nullptr;
+        const long x = std::strtol(e, &end, 10);
+        if (end && *end == '\0' && x >= d.lo && x <= d.hi) v = (int)x;
+      }
+      values[i].store(v);
+    }
+  });
+  return values;
+}
+
+int tunable_index(const char* name) {
+  for (int i = 0; i < pa::kNumTunables; ++i)
+    if (std::strcmp(kTunableDefs[i].name, name) == 0) return i;
+  return -1;
+}
+
+}  // namespace
+
+namespace pa {
+int tunable(Tunable t) { return tunable_values()[t].load(std::memory_order_relaxed); }
+}  // namespace pa
+
 extern "C" {
 
-int32_t pa_version(void) { return 100; }
+pa_status_t pa_set_tunable(const char* name, int32_t value) {
+  if (!name) return fail(PA_ERR_NULL_POINTER, "null tunable name");
+  const int i = tunable_index(name);
+  if (i < 0) return fail(PA_ERR_INVALID_ARG, "unknown tunable %s", name);
+  const TunableDef& d = kTunableDefs[i];
+  if (value < d.lo || value > d.hi)
+    return fail(PA_ERR_INVALID_ARG, "%s must be in [%d, %d] (got %d)", name, d.lo, d.hi, value);
+  tunable_values()[i].store(value);
+  return ok();
+}
+
+pa_status_t pa_get_tunable(const char* name, int32_t* value) {
+  if (!name || !value) return fail(PA_ERR_NULL_POINTER, "null argument");
+  const int i = tunable_index(name);
+  if (i < 0) return fail(PA_ERR_INVALID_ARG, "unknown tunable %s", name);
+  *value = tunable_values()[i].load();
+  return ok();
+}
+
+int32_t pa_version(void) { return 200; }
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
@@ -284,19 +349,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
     return 0;
   const int g = num_q_heads / num_kv_heads;
   if (!supported_head_dim(head_dim) || !supported_group(g, head_dim)) return 0;
-  return pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g).bytes;
+  return pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g, false).bytes;
 }
-
-namespace {
-// Decode tunables, read on every call (for sweeps): share of the steps split statically and the
-// smallest dynamic chunk.
-int env_int(const char* name, int dflt, int lo, int hi) {
-  const char* e = std::getenv(name);
-  if (!e || !*e) return dflt;
-  const int v = std::atoi(e);
-  return (v >= lo && v <= hi) ? v : dflt;
-}
-}  // namespace
 
 }  // extern "C"
 
@@ -330,7 +384,7 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
     return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for bf16 arrays)");
   if (out == query) return fail(PA_ERR_INVALID_ARG, "out must not alias query");
   const int g = num_q_heads / num_kv_heads;
-  const pa::DecodeWorkspace wl = pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g);
+  const pa::DecodeWorkspace wl = pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g, fp8);
   if (wl.workers <= 0)
     return fail(PA_ERR_HIP, "cannot query the device for the decode launch shape");
   if (!workspace || workspace_bytes < wl.bytes)
@@ -359,12 +413,12 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.num_workers = wl.workers;
   p.dyn_cap = wl.dyn_cap;
-  p.chunk_steps = env_int("PA_DECODE_CHUNK", 4, 1, 256);
-  p.static_frac_q10 = env_int("PA_DECODE_STATIC_Q10", 1024, 512, 1024);
+  p.chunk_steps = pa::tunable(pa::kTuneDecodeChunk);
+  p.static_frac_q10 = pa::tunable(pa::kTuneDecodeStaticQ10);
   // Head quads (four KV heads per workgroup worker) need a multiple of four KV heads.
   p.quad = p.static_frac_q10 == 1024 && num_kv_heads % 4 == 0 &&
-           env_int("PA_DECODE_QUAD", 1, 0, 1);
-  p.piece_cost = env_int("PA_DECODE_PIECE_COST", 6, 0, 64);
+           pa::tunable(pa::kTuneDecodeQuad) != 0;
+  p.piece_cost = pa::tunable(pa::kTuneDecodePieceCost);
   p.len_cap = max_seq_len;
   // FP8: the K scale joins the softmax scale and the V scale multiplies the outputs.
   p.scale_log2 = (fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
@@ -430,7 +484,7 @@ CascadeLayout cascade_layout(int num_seqs, int num_groups, int max_group_size, i
   c.ml_bytes = align_up(slots * 2 * sizeof(float), 256);
   c.acc_off = c.ml_bytes;
   c.dec_off = align_up(c.acc_off + slots * head_dim * sizeof(float), 256);
-  const size_t dec = pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g).bytes;
+  const size_t dec = pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g, false).bytes;
   c.bytes = dec ? c.dec_off + dec : 0;
   return c;
 }
@@ -740,6 +794,18 @@ pa_status_t decode_call(const pa_decode_args& a, void* stream, bool validate_onl
                      nullptr, nullptr, 0, 0, validate_only);
 }
 
+// A byte range one half of a mixed step writes.
+struct Span {
+  const char* what;
+  const void* ptr;
+  size_t bytes;
+  bool overlaps(const Span& o) const {
+    if (!ptr || !o.ptr || !bytes || !o.bytes) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(ptr), b = reinterpret_cast<uintptr_t>(o.ptr);
+    return a < b + o.bytes && b < a + bytes;
+  }
+};
+
 // Fork and join events of the calling thread on the current device (created on first use, kept
 // until the process ends).  They keep the default release on record: the other stream's kernels
 // consume what was written before the event (workspaces, inputs copied in), and without that
@@ -767,12 +833,35 @@ extern "C" {
 pa_status_t pa_mixed_step(const pa_prefill_args* prefill, const pa_decode_args* decode,
                           void* stream, void* side_stream) {
   if (!prefill || !decode) return fail(PA_ERR_NULL_POINTER, "null argument struct");
-  // An empty half may pass null pointers; two real outputs must differ.
-  if (decode->out && decode->out == prefill->out)
-    return fail(PA_ERR_INVALID_ARG, "the two halves must write different outputs");
   // Both halves are validated before either is launched.
   pa_status_t st = prefill_call(*prefill, stream, true);
   if (st != PA_OK) return st;
+  // The halves run at the same time: nothing one writes may overlap what the other writes.  The
+  // byte ranges are the outputs and the workspace bytes each call uses (an empty half writes
+  // nothing).
+  const pa_prefill_args& pf = *prefill;
+  const pa_decode_args& dc = *decode;
+  std::vector<Span> spans;
+  if (pf.num_seqs > 0 && pf.total_q > 0) {
+    spans.push_back({"the prefill output", pf.out,
+                     (size_t)pf.total_q * pf.num_q_heads * pf.head_dim * 2});
+    spans.push_back({"the prefill workspace", pf.workspace,
+                     pa_prefill_workspace_bytes(pf.num_seqs, pf.total_q, pf.max_q_len,
+                                                pf.num_q_heads, pf.num_kv_heads, pf.head_dim,
+                                                pf.max_seq_len)});
+  }
+  if (dc.num_seqs > 0 && dc.num_q_heads > 0 && dc.num_kv_heads > 0 && dc.head_dim > 0) {
+    spans.push_back({"the decode output", dc.out,
+                     (size_t)dc.num_seqs * dc.num_q_heads * dc.head_dim * 2});
+    spans.push_back({"the decode workspace", dc.workspace,
+                     pa::decode_workspace(dc.num_seqs, dc.num_kv_heads, dc.head_dim,
+                                          dc.num_q_heads / dc.num_kv_heads, dc.kv_fp8 != 0)
+                         .bytes});
+  }
+  for (size_t i = 0; i < spans.size(); ++i)
+    for (size_t j = i + 1; j < spans.size(); ++j)
+      if (spans[i].overlaps(spans[j]))
+        return fail(PA_ERR_INVALID_ARG, "%s overlaps %s", spans[i].what, spans[j].what);
   if ((st = decode_call(*decode, side_stream, true)) != PA_OK) return st;
   if (!side_stream || side_stream == stream) {  // one stream: the two calls in order
     if ((st = decode_call(*decode, stream, false)) != PA_OK) return st;

@@ -7,6 +7,23 @@
 
 namespace pa {
 
+// Launch tunables (for sweeps and tests).  Each starts from its default, or from the environment
+// variable of the same name if that holds an in-range value; the environment is read once, on
+// first use.  pa_set_tunable / pa_get_tunable change and read them afterwards.
+enum Tunable {
+  kTuneDecodePrefetch,     // PA_DECODE_PREFETCH: K/V steps in flight per wave, vector step (0-2)
+  kTuneDecodePrefetchFp8,  // PA_DECODE_PREFETCH_FP8: the same for FP8 pools (1-2)
+  kTuneDecodeMfma,         // PA_DECODE_MFMA: bf16 steps on the matrix cores (1) or vector ALUs (0)
+  kTuneDecodeQuad,         // PA_DECODE_QUAD: workgroup workers over units of four KV heads (0-1)
+  kTuneDecodePieceCost,    // PA_DECODE_PIECE_COST: steps charged per unit a worker starts (0-64)
+  kTuneDecodeWorkers,      // PA_DECODE_WORKERS: worker waves (0: one workgroup per CU)
+  kTuneDecodeStaticQ10,    // PA_DECODE_STATIC_Q10: share of steps split statically (512-1024)
+  kTuneDecodeChunk,        // PA_DECODE_CHUNK: smallest dynamic chunk, in steps (1-256)
+  kTunePrefillSplits,      // PA_PREFILL_SPLITS: forced context split of a prefill (0: automatic)
+  kNumTunables
+};
+int tunable(Tunable t);
+
 // Decode work is cut into "steps" of 16 tokens of one (sequence, KV head) pair.  The pairs
 // ("units", numbered s*num_kv_heads + h) are laid end to end and every worker wave takes an equal
 // contiguous range of the concatenated steps, so the load is balanced whatever the length mix.
@@ -55,14 +72,15 @@ struct DecodeParams {
   int state_stride, state_split;
 };
 
-// Waves the decode kernel is launched with for this shape on the current device.
-int decode_workers(int head_dim, int group);
+// Waves the decode kernel is launched with for this shape and pool type on the current device.
+int decode_workers(int head_dim, int group, bool fp8);
 // Workspace layout of pa_decode: the chunk counter, then unit_info, then the partial slots.
+// `bytes` covers both pool types (one size query serves pa_decode and pa_decode_fp8).
 struct DecodeWorkspace {
   size_t counter_off, info_off, partials_off, bytes;
   int workers, dyn_cap;
 };
-DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group);
+DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group, bool fp8);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 struct ReshapeParams {

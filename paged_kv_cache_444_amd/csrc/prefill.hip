@@ -35,7 +35,6 @@
 #include "pa_internal.h"
 
 #include <algorithm>
-#include <cstdlib>
 #include <map>
 #include <mutex>
 #include <type_traits>
@@ -626,7 +625,7 @@ PrefillSplit split_for(int num_seqs, int max_q_len, int num_kv_heads, int group,
   // second resident round, and every extra range adds merge traffic.
   const long long slots = (long long)(one_per_cu ? 1 : resident_per_cu(head_dim, group)) * cu_count();
   long long want = (slots + base - 1) / base;
-  if (const char* e = std::getenv("PA_PREFILL_SPLITS"); e && *e) want = std::atoi(e);
+  if (const int forced = tunable(kTunePrefillSplits); forced > 0) want = forced;
   want = std::min<long long>(std::max<long long>(want, 1), 16);
   want = std::min<long long>(want, std::max(1, max_seq_len / 256));
   want = std::max(want, need);

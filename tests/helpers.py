@@ -100,3 +100,49 @@ def dev_u8(a: np.ndarray) -> torch.Tensor:
 
 def host_u8(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
+
+
+# Per-tensor FP8 scales for the N(0,1) workloads: the largest of ~10^8 normal draws (about 6)
+# maps near the E4M3 maximum 448.
+FP8_K_SCALE = 6.0 / 448.0
+FP8_V_SCALE = 5.5 / 448.0
+
+
+@functools.lru_cache(maxsize=2)
+def cached_fp8_pools(cfg_id: int):
+    """E4M3 pools of a named workload: its bf16 pools after the step's reshape (the oracle's),
+    quantised whole by the oracle's quantiser with FP8_K_SCALE / FP8_V_SCALE."""
+    okc, ovc = cached_oracle_pools(cfg_id)
+    return oracle_quantize_pool(okc, FP8_K_SCALE), oracle_quantize_pool(ovc, FP8_V_SCALE)
+
+
+@functools.lru_cache(maxsize=16)
+def full_decode_oracle(cfg_id: int, fp8: bool = False) -> np.ndarray:
+    """Oracle decode of every sequence of a named workload ([B][Hq][D] float64), over the pools
+    after the step's reshape (bf16, or their E4M3 codes), computed on several host processes."""
+    import oracle_pool
+
+    case = cached_named_case(cfg_id)
+    d = case.decode
+    kc, vc = cached_fp8_pools(cfg_id) if fp8 else cached_oracle_pools(cfg_id)
+    extra = dict(k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE) if fp8 else {}
+    return oracle_pool.decode_seqs("decode_fp8" if fp8 else "decode", d.query, kc, vc,
+                                   d.block_tables, d.seq_lens, case.num_kv_heads, case.head_dim,
+                                   case.block_size, case.scale, **extra)
+
+
+@functools.lru_cache(maxsize=2)
+def full_prefill_oracle(cfg_id: int, fp8: bool = False) -> np.ndarray:
+    """Oracle output of every query row of a named workload's prefill chunk ([total_q][Hq][D]
+    float64), over the pools after the chunk's reshape (bf16, or their E4M3 codes), computed on
+    several host processes."""
+    import oracle_pool
+
+    case = cached_named_case(cfg_id)
+    p = case.prefill
+    kc, vc = cached_fp8_pools(cfg_id) if fp8 else cached_oracle_pools(cfg_id)
+    extra = dict(k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE) if fp8 else {}
+    return oracle_pool.prefill_rows("prefill_chunk_fp8" if fp8 else "prefill_chunk", p.query, kc,
+                                    vc, p.block_tables, p.query_start_loc, p.seq_lens,
+                                    case.num_kv_heads, case.head_dim, case.block_size, case.scale,
+                                    **extra)

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_error_text(lib):
-    assert lib.pa_version() >= 100
+    assert lib.pa_version() >= 200
     assert isinstance(lib.pa_last_error(), bytes)
 
 
@@ -128,8 +128,7 @@ def test_binding_exports_every_listed_name():
 
 def test_mixed_step_with_empty_halves(lib):
     """Empty halves (no sequences) may pass null pointers: with both empty the call succeeds on
-    one stream without launching anything; a bad shape in either half is still rejected, and two
-    real halves may not share an output."""
+    one stream without launching anything; a bad shape in either half is still rejected."""
     def prefill_args(num_seqs=0, head_dim=128, out=None):
         return pa._PrefillArgs(out=out, num_blocks=16, num_seqs=num_seqs, total_q=num_seqs,
                                max_q_len=num_seqs, num_q_heads=8, num_kv_heads=2,
@@ -149,10 +148,87 @@ def test_mixed_step_with_empty_halves(lib):
     assert call(prefill_args(head_dim=96), decode_args()) == 3  # unsupported head_dim
     assert call(prefill_args(), decode_args(head_dim=96)) == 3
     assert call(prefill_args(num_seqs=-1), decode_args()) == 2
-    # two real halves writing one buffer: rejected before either is looked at further
-    buf = ctypes.c_void_p(0x1000)
-    assert call(prefill_args(num_seqs=1, out=buf), decode_args(num_seqs=1, out=buf)) == 2
-    assert b"different outputs" in lib.pa_last_error()
+
+
+def test_mixed_step_rejects_overlapping_outputs_and_workspaces(lib):
+    """The two halves of a mixed step run at the same time, so no byte one writes may be written
+    by the other: outputs and used workspace ranges must be disjoint (checked on the host before
+    any launch; the pointers here are never dereferenced)."""
+    Hq, Hkv, D = 64, 8, 128
+    L, q = 40000, 512  # longer than one workgroup's table slice: always split, on any device
+
+    def prefill_args(out, ws, ws_bytes):
+        return pa._PrefillArgs(out=out, query=0x100000, key_cache=0x200000, value_cache=0x300000,
+                               num_blocks=4096, block_tables=0x400000, query_start_loc=0x410000,
+                               seq_lens=0x420000, num_seqs=1, total_q=q, max_q_len=q,
+                               num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=16,
+                               max_blocks_per_seq=L // 16, max_seq_len=L, scale=0.088,
+                               k_scale=1.0, v_scale=1.0, workspace=ws, workspace_bytes=ws_bytes)
+
+    def decode_args(out):
+        return pa._DecodeArgs(out=out, query=0x500000, key_cache=0x200000, value_cache=0x300000,
+                              num_blocks=4096, block_tables=0x600000, seq_lens=0x610000,
+                              num_seqs=4, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                              block_size=16, max_blocks_per_seq=64, max_seq_len=1024, scale=0.088,
+                              k_scale=1.0, v_scale=1.0)
+
+    need = lib.pa_prefill_workspace_bytes(1, q, q, Hq, Hkv, D, L)
+    assert need > 0  # the long context is split, so the prefill half uses its workspace
+    pout, ws = 0x10000000, 0x20000000
+    out_bytes = q * Hq * D * 2
+
+    def call(pf, dc):
+        return lib.pa_mixed_step(ctypes.byref(pf), ctypes.byref(dc), None, None)
+
+    # the decode output starts inside the prefill output
+    assert call(prefill_args(pout, ws, need), decode_args(pout + out_bytes - 256)) == 2
+    assert b"prefill output overlaps the decode output" in lib.pa_last_error()
+    # the decode output lies inside the prefill workspace
+    assert call(prefill_args(pout, ws, need), decode_args(ws + need // 2)) == 2
+    assert b"prefill workspace overlaps the decode output" in lib.pa_last_error()
+    # the prefill workspace runs into its own output
+    assert call(prefill_args(ws + 256, ws, need), decode_args(0x30000000)) == 2
+
+
+def test_tunable_setter(lib):
+    """Launch tunables: read through pa_get_tunable, changed by pa_set_tunable within their range,
+    rejected (and left unchanged) outside it or under an unknown name."""
+    v = ctypes.c_int32()
+    assert lib.pa_get_tunable(b"PA_DECODE_PIECE_COST", ctypes.byref(v)) == 0
+    before = v.value
+    assert lib.pa_set_tunable(b"PA_DECODE_PIECE_COST", 9) == 0
+    assert lib.pa_get_tunable(b"PA_DECODE_PIECE_COST", ctypes.byref(v)) == 0 and v.value == 9
+    assert lib.pa_set_tunable(b"PA_DECODE_PIECE_COST", 65) == 2      # out of range
+    assert b"PA_DECODE_PIECE_COST" in lib.pa_last_error()
+    assert lib.pa_get_tunable(b"PA_DECODE_PIECE_COST", ctypes.byref(v)) == 0 and v.value == 9
+    assert lib.pa_set_tunable(b"PA_NO_SUCH_THING", 1) == 2
+    assert lib.pa_get_tunable(b"PA_NO_SUCH_THING", ctypes.byref(v)) == 2
+    assert lib.pa_set_tunable(None, 1) == 1
+    assert lib.pa_set_tunable(b"PA_DECODE_PIECE_COST", before) == 0
+    # every name the binding lists is known to the library, and the context manager restores
+    for name in pa.TUNABLES:
+        assert lib.pa_get_tunable(name.encode(), ctypes.byref(v)) == 0, name
+    with pa.tunables(PA_PREFILL_SPLITS=3, PA_DECODE_MFMA=0):
+        assert pa.get_tunable("PA_PREFILL_SPLITS") == 3 and pa.get_tunable("PA_DECODE_MFMA") == 0
+    assert pa.get_tunable("PA_PREFILL_SPLITS") == 0 and pa.get_tunable("PA_DECODE_MFMA") == 1
+
+
+def test_tunables_read_from_the_environment_once():
+    """A fresh process picks its tunables from the environment when the library first needs
+    them; later changes of the environment do not matter."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import os, paged_kv_cache_444_amd as pa\n"
+            "a = pa.get_tunable('PA_DECODE_CHUNK'), pa.get_tunable('PA_DECODE_QUAD')\n"
+            "os.environ['PA_DECODE_CHUNK'] = '7'\n"
+            "print(a, pa.get_tunable('PA_DECODE_CHUNK'))\n")
+    env = dict(os.environ, PA_DECODE_CHUNK="16", PA_DECODE_QUAD="9")  # 9: out of range, ignored
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "(16, 1) 16"
 
 
 def test_bench_refuses_more_than_one_gpu():

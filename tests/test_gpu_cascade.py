@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import paged_kv_cache_444_amd as pa
-from helpers import (assert_close, cached_named_case, cached_oracle_pools, dev_i32, dev_i64,
-                     dev_u16, host_u16, upcast)
+from helpers import (FP8_K_SCALE, FP8_V_SCALE, assert_close, cached_fp8_pools, cached_named_case,
+                     dev_i32, dev_i64, dev_u16, dev_u8, full_decode_oracle, host_u16, upcast)
 from oracle import paged_attention as oracle
 from workloads import Spec, build_case
 
@@ -60,11 +60,8 @@ def test_cascade_parity_prefix_shared_rollouts():
     gs = np.arange(0, 129, 16)
     got = _cascade(case, kc, vc, gs, 4096)
     assert np.array_equal(got, _cascade(case, kc, vc, gs, 4096)), "not reproducible"
-    okc, ovc = cached_oracle_pools(5)
-    seqs = sorted({0, 15, 16, 127} | set(np.random.default_rng(80).choice(128, 12, replace=False).tolist()))
-    ref = oracle.decode(d.query, okc, ovc, d.block_tables, d.seq_lens, case.num_kv_heads,
-                        case.head_dim, case.block_size, case.scale, seqs=seqs)
-    assert_close(upcast(got)[seqs], ref[seqs], "cascade decode cfg5")
+    # every sequence of the batch against the oracle's plain decode
+    assert_close(upcast(got), full_decode_oracle(5), "cascade decode cfg5")
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,bs", [(8, 2, 64, 16), (16, 1, 64, 32), (64, 8, 128, 16),
@@ -133,19 +130,13 @@ def test_cascade_prompts_of_different_lengths_and_unshared_sequences():
 
 def test_cascade_fp8_prefix_shared_rollouts():
     """The prefix-shared rollouts over an FP8 cache quantised by the oracle."""
-    from helpers import dev_u8, oracle_quantize_pool
-
     case = cached_named_case(5)
-    d = case.decode
-    ks, vs = 6.0 / 448.0, 5.5 / 448.0
-    okc, ovc = cached_oracle_pools(5)
-    kc8, vc8 = oracle_quantize_pool(okc, ks), oracle_quantize_pool(ovc, vs)
+    ks, vs = FP8_K_SCALE, FP8_V_SCALE
+    kc8, vc8 = cached_fp8_pools(5)
     gs = np.arange(0, 129, 16)
     got = _cascade(case, dev_u8(kc8), dev_u8(vc8), gs, 4096, fp8_scales=(ks, vs))
-    seqs = [0, 17, 90, 127]
-    ref = oracle.decode_fp8(d.query, kc8, vc8, d.block_tables, d.seq_lens, case.num_kv_heads,
-                            case.head_dim, case.block_size, case.scale, ks, vs, seqs=seqs)
-    assert_close(upcast(got)[seqs], ref[seqs], "FP8 cascade decode cfg5")
+    # every sequence of the batch against the oracle's plain FP8 decode
+    assert_close(upcast(got), full_decode_oracle(5, fp8=True), "FP8 cascade decode cfg5")
 
 
 def _draw_cascade(seed):
@@ -175,7 +166,7 @@ def _draw_cascade(seed):
 @pytest.mark.parametrize("seed", range(8))
 def test_cascade_random_groups(seed):
     """Seeded random group layouts, bf16 and FP8 caches, against the oracle's plain decode."""
-    from helpers import dev_u8, oracle_quantize_pool
+    from helpers import oracle_quantize_pool
 
     case, gs, prompts = _draw_cascade(seed)
     d = case.decode

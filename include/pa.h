@@ -11,8 +11,9 @@
  *
  * Conventions for every entry point
  *   - All arrays are device pointers owned by the caller; the library allocates no device memory,
- *     keeps no device state between calls, and never synchronises the stream (pa_mixed_step
- *     keeps two host-side events per thread and device, see there).
+ *     keeps no device state between calls (except pa_decode_no_alloc's fixed scratch array, see
+ *     there), and never synchronises the stream (pa_mixed_step keeps two host-side events per
+ *     thread and device, see there).
  *   - bf16 tensors are raw 16-bit bfloat16 bit patterns, contiguous, 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call enqueues its kernels on
  *     that stream and returns immediately.
@@ -215,6 +216,31 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const void* key_cache,
                           int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len,
                           float scale, float k_scale, float v_scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_no_alloc — pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It takes no workspace
+ * and allocates nothing; its scratch (the unit table and partial softmax states of sequences
+ * split over several waves) is a fixed array of PA_DECODE_NO_ALLOC_SCRATCH_BYTES inside the
+ * library, one per device, held from the device's first call until the process ends.
+ *
+ *   arguments      as pa_decode (bf16 pools), without the workspace
+ * Limit: the batch's scratch (about (num_seqs*num_kv_heads + 4 * CUs) * G * (head_dim + 2) * 4
+ * bytes: 8.5 MB for 128 sequences of 8 KV heads, G 8, head_dim 128 on 256 CUs) must fit the
+ * array; a larger batch returns PA_ERR_WORKSPACE before anything is launched (use pa_decode).
+ * The whole batch is split statically (dynamic chunks are not used), which is also pa_decode's
+ * default, so results equal pa_decode's bit for bit under the default tunables.
+ * Every call on a device uses that device's one array, and nothing in it has to start at a set
+ * value: calls that overlap in time on one device (different streams, or threads) race on it and
+ * give unspecified results; calls ordered on one stream are safe.  Other errors as pa_decode.
+ */
+#define PA_DECODE_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+pa_status_t pa_decode_no_alloc(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, int64_t num_blocks,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                               int32_t max_seq_len, float scale, void* stream);
 
 /*
  * Cascade decode for sequences that share a prompt (copy-on-write rollouts).

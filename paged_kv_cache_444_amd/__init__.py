@@ -21,6 +21,7 @@ __all__ = [
     "prefill_chunk", "prefill_chunk_fp8", "mixed_step", "decode_workspace_bytes",
     "prefill_workspace_bytes", "stream_read", "trace_enable", "trace_read", "PagedAttentionError",
     "pool_shape", "LIB_PATH", "set_tunable", "get_tunable", "tunables", "TUNABLES",
+    "decode_no_alloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -79,6 +80,8 @@ _SIGNATURES = {
                                      ctypes.c_float, ctypes.c_float, _P, _SZ, _P]),
     "pa_copy_blocks": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _P]),
     "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_decode_no_alloc": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                  _I32, ctypes.c_float, _P]),
     "pa_decode": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                          ctypes.c_float, _P, _SZ, _P]),
     "pa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
@@ -291,6 +294,29 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
                          _ints(block_tables, torch.int32, "block_tables"),
                          _ints(seq_lens, torch.int32, "seq_lens"), B, Hq, num_kv_heads, D, block_size,
                          block_tables.shape[1], max_seq_len, float(scale), ws, ws_bytes, _stream()))
+    return out
+
+
+def decode_no_alloc(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                    block_tables: torch.Tensor, seq_lens: torch.Tensor, *, num_kv_heads: int,
+                    block_size: int, max_seq_len: int, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """`decode` without a workspace (pa_decode_no_alloc): the library's fixed per-device scratch
+    array is used, so the call allocates nothing when `out` is given.  Calls that overlap in time
+    on one device race on that array; batches too large for it raise PA_ERR_WORKSPACE."""
+    lib = load_library()
+    _decode_shapes(query, block_tables, seq_lens)
+    B, Hq, D = query.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = _out_like(out, query)
+    n = _num_blocks(key_cache, value_cache, num_kv_heads, block_size, D)
+    _check(lib.pa_decode_no_alloc(_bf16(out, "out"), _bf16(query, "query"),
+                                  _bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache"),
+                                  n, _ints(block_tables, torch.int32, "block_tables"),
+                                  _ints(seq_lens, torch.int32, "seq_lens"), B, Hq, num_kv_heads, D,
+                                  block_size, block_tables.shape[1], max_seq_len, float(scale),
+                                  _stream()))
     return out
 
 

@@ -954,7 +954,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   if (plan.T == 0) return;  // block-uniform
   const long long workers = quad ? (long long)gridDim.x : (long long)p.num_workers;
   plan.ns = min(workers, (plan.T + kMinStepsPerWave - 1) / kMinStepsPerWave);
-  const bool dynamic = !quad && p.dyn_cap > 0 && plan.ns == p.num_workers;
+  // Dynamic chunks only when a share of the steps is left to them: with the whole batch split
+  // statically the plan (piece cost included) does not depend on the workspace's chunk slots.
+  const bool dynamic =
+      !quad && p.dyn_cap > 0 && p.static_frac_q10 < 1024 && plan.ns == p.num_workers;
   if (dynamic) {
     plan.S = max(plan.ns, plan.T * p.static_frac_q10 / 1024);
     const long long rest = plan.T - plan.S;
@@ -1194,7 +1197,8 @@ hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
   {
     TraceScope t("decode_partition", stream);
     const dim3 grid(p.num_workers / kWaves), block(kThreads);
-    const size_t lds = p.dyn_cap > 0 ? (size_t)(p.num_seqs + 1) * 4 : 0;
+    const size_t lds =
+        (p.dyn_cap > 0 && p.static_frac_q10 < 1024) ? (size_t)(p.num_seqs + 1) * 4 : 0;
     switch (variant(p.kv_fp8 != 0)) {
       case Variant::kFp8Depth1:
         hipLaunchKernelGGL((decode_kernel<D, G, 1, true>), grid, block, lds, stream, p);
@@ -1298,18 +1302,22 @@ int decode_workers(int head_dim, int group, bool fp8) {
   return blocks.first * kWaves;
 }
 
-DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group, bool fp8) {
+DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group, bool fp8,
+                                 bool chunk_slots) {
   DecodeWorkspace ws{};
   ws.workers = decode_workers(head_dim, group, fp8);
-  // The size covers the worker count of either pool type, so one query serves both.
-  const int most = std::max(decode_workers(head_dim, group, !fp8), ws.workers);
+  // With chunk slots the size covers the worker count of either pool type, so one query serves
+  // both; without them it is exactly this launch's static layout.
+  const int most =
+      chunk_slots ? std::max(decode_workers(head_dim, group, !fp8), ws.workers) : ws.workers;
   if (ws.workers <= 0 || most <= 0 || num_seqs <= 0) {
     ws.workers = 0;
     return ws;
   }
   // Dynamic chunks need the per-sequence prefix in LDS: batches up to kMaxPrefixSeqs.
-  ws.dyn_cap = num_seqs <= kMaxPrefixSeqs ? kDynSlotsPerWorker * ws.workers : 0;
-  const int most_dyn = num_seqs <= kMaxPrefixSeqs ? kDynSlotsPerWorker * most : 0;
+  const bool dyn = chunk_slots && num_seqs <= kMaxPrefixSeqs;
+  ws.dyn_cap = dyn ? kDynSlotsPerWorker * ws.workers : 0;
+  const int most_dyn = dyn ? kDynSlotsPerWorker * most : 0;
   const size_t units = (size_t)num_seqs * num_kv_heads;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   ws.counter_off = 0;

@@ -365,7 +365,7 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
                         size_t workspace_bytes, void* stream,
                         const int32_t* skip_lens = nullptr, float* state_ml = nullptr,
                         float* state_acc = nullptr, int state_stride = 0, int state_split = 0,
-                        bool validate_only = false) {
+                        bool validate_only = false, bool static_layout = false) {
   if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (fp8 && !std::isfinite(scale * k_scale))
@@ -384,9 +384,16 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
     return fail(PA_ERR_INVALID_ARG, "misaligned pointer (need 16 bytes for bf16 arrays)");
   if (out == query) return fail(PA_ERR_INVALID_ARG, "out must not alias query");
   const int g = num_q_heads / num_kv_heads;
-  const pa::DecodeWorkspace wl = pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g, fp8);
+  // static_layout: no dynamic-chunk slots (the whole batch is split statically).
+  const pa::DecodeWorkspace wl =
+      pa::decode_workspace(num_seqs, num_kv_heads, head_dim, g, fp8, !static_layout);
   if (wl.workers <= 0)
     return fail(PA_ERR_HIP, "cannot query the device for the decode launch shape");
+  if (static_layout && workspace_bytes < wl.bytes)
+    return fail(PA_ERR_WORKSPACE,
+                "this batch needs %zu bytes of decode scratch, more than the %zu the library "
+                "holds for pa_decode_no_alloc (use pa_decode with a workspace)",
+                wl.bytes, workspace_bytes);
   if (!workspace || workspace_bytes < wl.bytes)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 wl.bytes);
@@ -414,7 +421,7 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
   p.num_workers = wl.workers;
   p.dyn_cap = wl.dyn_cap;
   p.chunk_steps = pa::tunable(pa::kTuneDecodeChunk);
-  p.static_frac_q10 = pa::tunable(pa::kTuneDecodeStaticQ10);
+  p.static_frac_q10 = static_layout ? 1024 : pa::tunable(pa::kTuneDecodeStaticQ10);
   // Head quads (four KV heads per workgroup worker) need a multiple of four KV heads.
   p.quad = p.static_frac_q10 == 1024 && num_kv_heads % 4 == 0 &&
            pa::tunable(pa::kTuneDecodeQuad) != 0;
@@ -459,6 +466,69 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const void* key_cache,
                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      max_blocks_per_seq, max_seq_len, scale, true, k_scale, v_scale, workspace,
                      workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// pa_decode_no_alloc: pa_decode whose scratch (unit table, partial states, chunk counter) is a
+// fixed device array of the library instead of a caller workspace.  Each device holds its own
+// copy of the array for as long as the process runs; host code reaches a device's copy only
+// through the address hipGetSymbolAddress returns for it with that device current (the array's
+// name on the host is a stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up on the first call that device
+// makes and kept.
+pa_status_t scratch_on_current_device(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "decode_no_alloc (device)");
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "decode_no_alloc (scratch address)");
+    if (!p) return fail(PA_ERR_HIP, "decode_no_alloc: no scratch address on device %d", dev);
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode_no_alloc(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, int64_t num_blocks,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                               int32_t max_seq_len, float scale, void* stream) {
+  // Host-side checks first (the scratch stands in as a 256-byte aligned placeholder of its full
+  // size), so a rejected call touches no device state.
+  const size_t cap = PA_DECODE_NO_ALLOC_SCRATCH_BYTES;
+  void* ws = reinterpret_cast<void*>(uintptr_t{256});
+  pa_status_t st = decode_impl(out, query, key_cache, value_cache, num_blocks, block_tables,
+                               seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                               block_size, max_blocks_per_seq, max_seq_len, scale, false, 1.f, 1.f,
+                               ws, cap, stream, nullptr, nullptr, nullptr, 0, 0,
+                               /*validate_only=*/true, /*static_layout=*/true);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if ((st = scratch_on_current_device(&ws)) != PA_OK) return st;
+  // Nothing in the scratch has to start at zero: with the static split every unit's table entry
+  // and every partial slot is written before it is read, and the chunk counter is unused.
+  return decode_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, max_seq_len, scale, false, 1.f, 1.f, ws, cap, stream,
+                     nullptr, nullptr, nullptr, 0, 0, /*validate_only=*/false,
+                     /*static_layout=*/true);
 }
 
 }  // extern "C"

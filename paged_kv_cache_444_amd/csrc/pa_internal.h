@@ -75,12 +75,15 @@ struct DecodeParams {
 // Waves the decode kernel is launched with for this shape and pool type on the current device.
 int decode_workers(int head_dim, int group, bool fp8);
 // Workspace layout of pa_decode: the chunk counter, then unit_info, then the partial slots.
-// `bytes` covers both pool types (one size query serves pa_decode and pa_decode_fp8).
+// With chunk_slots, `bytes` also holds the dynamic chunks' slots and covers both pool types (one
+// size query serves pa_decode and pa_decode_fp8); without, it is the static split's layout of
+// this launch only (no dynamic chunks: dyn_cap = 0).
 struct DecodeWorkspace {
   size_t counter_off, info_off, partials_off, bytes;
   int workers, dyn_cap;
 };
-DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group, bool fp8);
+DecodeWorkspace decode_workspace(int num_seqs, int num_kv_heads, int head_dim, int group, bool fp8,
+                                 bool chunk_slots = true);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 struct ReshapeParams {

@@ -88,6 +88,11 @@ def test_host_side_validation(lib):
     assert lib.pa_decode_cascade_workspace_bytes(4, 1, 4, 8, 2, 96, 32) == 0
     assert lib.pa_prefill_chunk_fp8(z, z, z, z, 10, z, z, z, 1, 4, 4, 8, 2, 64, 16, 4, 64, 0.1, 0.0,
                                     1.0, z, 0, z) == 2  # k_scale
+    # the no-allocation decode: pa_decode's host checks, no workspace
+    assert lib.pa_decode_no_alloc(z, z, z, z, 1000, z, z, 1, 6, 4, 128, 16, 4, 64, 0.1, z) == 2
+    assert lib.pa_decode_no_alloc(z, z, z, z, 1000, z, z, 1, 8, 2, 96, 16, 4, 64, 0.1, z) == 3
+    assert lib.pa_decode_no_alloc(z, z, z, z, 1000, z, z, 1, 8, 2, 128, 16, 4, 64, 0.1, z) == 1
+    assert lib.pa_decode_no_alloc(z, z, z, z, 1000, z, z, 0, 8, 2, 128, 16, 4, 64, 0.1, z) == 0
     assert lib.pa_stream_read(z, 0, z, 0, z) == 0       # nothing to read
     assert lib.pa_stream_read(z, 32, z, 0, z) == 1      # nulls
     assert lib.pa_trace_read(b"decode_partition", None, None) == 1

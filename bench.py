@@ -13,8 +13,14 @@ previous step filled.  Prints one JSON line.
                duration over the same K steps run again with HIP events recorded around every
                kernel launch (the events' marker packets add a few us per step, so this second
                pass is not the one `value` is taken from), against the 8 TB/s HBM peak
-  cpu_baseline the fp64 CPU oracle on a bounded sample of the same batch (a correctness tool,
-               not an optimised CPU kernel)
+  call_us      per-call durations (events around each call on its stream): p10 / p50 / p90
+  cpu_baseline the fp64 CPU oracle on the same batch, spread over the host's cores (a correctness
+               tool, not an optimised CPU kernel), with every other workload under `per_config`
+  paged_waste  share of allocated block slots the workloads leave empty (last blocks only), next
+               to a contiguous 8,192-token reservation per sequence
+
+  tp8_share    one GPU's share of the same batch at tensor parallelism 8 over KV heads (8 query
+               heads on 1 KV head): call time, kernel roofline
 
   mixed_step   the chunked-prefill mixed step of the same model shape (one 512-token chunk over
                31,744 cached tokens, batched with 127 decode sequences): per-kernel times and the
@@ -101,9 +107,13 @@ def parse():
                     help="distinct KV pool copies cycled through by consecutive steps")
     ap.add_argument("--warm-steps", type=int, default=50,
                     help="extra steps on one pool (cache-warm), reported for context")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="repeat the oracle over the whole batch until this much CPU time is spent")
+    ap.add_argument("--cpu-runs", type=int, default=3,
+                    help="timed runs of the CPU oracle per workload (the median is reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dist-steps", type=int, default=100,
+                    help="calls timed one by one for the p10/p50/p90 of the call duration")
+    ap.add_argument("--no-tp-share", action="store_true",
+                    help="skip the tensor-parallel share (8 query heads on 1 KV head)")
     ap.add_argument("--mode", choices=["decode", "copy", "mixed", "cow", "prefix", "configs"],
                     default="decode")
     ap.add_argument("--mixed-steps", type=int, default=30)
@@ -150,6 +160,13 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the library's path runs on a single GPU: run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if not args.no_cpu_baseline and args.mode == "decode":
+        # The CPU baseline's worker processes fork from a server started before this process
+        # touches the GPU.
+        from oracle import pool
+
+        pool.start()
 
     import torch
 
@@ -223,6 +240,16 @@ def main():
     pa.trace_enable(False)
     log(f"timed {args.steps} steps with per-launch events")
 
+    # Per-call distribution: events around each call on its stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.dist_steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+
     warm_us = None
     if args.warm_steps > 0:
         for _ in range(5):
@@ -244,10 +271,19 @@ def main():
     if not args.no_fp8:
         fp8 = run_fp8_decode(args, case, pools, q, bt, sl, out, ws, ms_per_step, main_ms)
     n_pools = len(pools)
+    # The measured read ceiling comes after the decode timing: run first, its 25 passes over
+    # 4 GiB left the decode 1.5 % slower (alternating fresh processes on one box).
     ceiling = stream_read_ceiling()
+    log(f"stream-read ceiling {ceiling['gbs']} GB/s")
+    tp = None
+    if not args.no_tp_share:
+        del pools, kc0, vc0
+        pools = None
+        torch.cuda.empty_cache()
+        tp = run_tp_share(args)
     mixed = None
     if not args.no_mixed:
-        del pools, kc0, vc0
+        pools = kc0 = vc0 = None
         torch.cuda.empty_cache()
         mixed = run_mixed(args)
     cow = None
@@ -259,8 +295,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample")
-        cpu = cpu_baseline(case, args.cpu_seconds)
+        log("timing the CPU oracle on every workload")
+        cpu = cpu_baseline(args)
 
     rec = {
         "metric": METRIC,
@@ -295,10 +331,17 @@ def main():
             "merge_launch_us": round(ms_merge / max(n_merge, 1) * 1e3, 2),
             "ms_per_step_with_events": round((t3 - t2) * 1e3 / args.steps, 5),
         },
+        "call_us": {"p10": round(float(np.percentile(call_us, 10)), 2),
+                    "p50": round(float(np.percentile(call_us, 50)), 2),
+                    "p90": round(float(np.percentile(call_us, 90)), 2),
+                    "mean": round(float(call_us.mean()), 2), "calls": int(call_us.size),
+                    "how": "events recorded around each call on its stream, pools cycled"},
         "warm_single_pool_us_per_step": None if warm_us is None else round(warm_us, 2),
         "stream_read_ceiling": dict(ceiling,
                                     decode_kernel_frac=round(main_gbs / ceiling["gbs"], 4),
                                     decode_call_frac=round(gbs / ceiling["gbs"], 4)),
+        "tp8_share": tp,
+        "paged_waste": paged_waste_report(),
         "fp8_decode": fp8,
         "mixed_step": mixed,
         "cow_step": cow,
@@ -787,31 +830,180 @@ def run_configs(args):
             "workloads": res}
 
 
-def cpu_baseline(case, budget_s):
-    """Time the fp64 oracle over the whole batch (all sequences and heads), repeated until about
-    `budget_s` seconds have passed (at most 8 runs); report the median run.  np.einsum without
-    optimize runs single-threaded, so one core does the work."""
-    from oracle import paged_attention as oracle
+def paged_waste_report():
+    """Share of the allocated block slots that the workloads' sequences leave empty.  Blocks are
+    taken as tokens arrive, so only each sequence's last block is partly empty; shared prompt
+    blocks are counted once.  Next to it, the share of a contiguous reservation of 8,192 tokens
+    per sequence that goes unused (the pages' fragmentation comparison)."""
+    from workloads import NAMED_CASES
 
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
+    out = {}
+    for cfg, make in NAMED_CASES.items():
+        spec = make()
+        bs = spec.block_size
+        lens = [int(x) for x in (spec.decode_lens or [])]
+        lens += [int(c) + int(q) for c, q in (spec.prefill or [])]
+        used = sum(lens)
+        slots = sum(-(-L // bs) * bs for L in lens)
+        for members, shared in (spec.share_groups or []):
+            # every member after the first reuses the group's shared blocks
+            used -= (len(members) - 1) * shared
+            slots -= (len(members) - 1) * shared
+        out[spec.name] = {"paged_waste_pct": round(100.0 * (1.0 - used / slots), 3),
+                          "contiguous_8192_waste_pct":
+                              round(100.0 * (1.0 - sum(lens) / (8192.0 * len(lens))), 1)
+                              if max(lens) <= 8192 else None,
+                          "tokens": used, "slots": slots, "block_size": bs}
+    return out
+
+
+def run_tp_share(args, tp=8, copies=8):
+    """One GPU's share of the 70B-shaped batch-128 decode at tensor parallelism `tp` over KV
+    heads: the same lengths, 64/tp query heads on 8/tp KV heads.  `copies` pool copies are cycled
+    (1/tp of the bytes per call: more copies keep the last-level cache cold)."""
+    import torch
+
+    import paged_kv_cache_444_amd as pa
+    from workloads import tp_share_case
+
+    log(f"generating the TP={tp} share of the 70B-shaped decode")
+    case = tp_share_case(tp)
     d = case.decode
-    runs = []
-    while len(runs) < 8 and sum(runs) < budget_s:
-        t0 = time.perf_counter()
-        oracle.decode(d.query, case.key_cache, case.value_cache, d.block_tables, d.seq_lens,
-                      case.num_kv_heads, case.head_dim, case.block_size, case.scale)
-        runs.append(time.perf_counter() - t0)
-    dt = float(np.median(runs))
-    nbytes = decode_bytes(d.seq_lens, case.num_q_heads, case.num_kv_heads, case.head_dim,
-                          case.block_size)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "host_cores_available": cores, "seconds_per_call": round(dt, 3), "runs": len(runs),
-            "seqs_per_s": round(d.num_seqs / dt, 2),
-            "sample": f"the whole batch ({d.num_seqs} sequences, {case.num_q_heads} query heads), "
-                      f"median of {len(runs)} runs; fp64 NumPy gather + einsum, single-threaded"}
+    Hq, Hkv, D, bs = case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    kc, vc = dev(case.key_cache), dev(case.value_cache)
+    pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(copies - 1)]
+    q, out = dev(d.query), None
+    bt, sl = torch.from_numpy(d.block_tables).cuda(), torch.from_numpy(d.seq_lens).cuda()
+    out = torch.empty_like(q)
+    ws = torch.zeros(pa.decode_workspace_bytes(d.num_seqs, Hq, Hkv, D, d.max_seq_len),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        k, v = pools[i % len(pools)]
+        pa.decode(q, k, v, bt, sl, num_kv_heads=Hkv, block_size=bs, scale=float(case.scale),
+                  max_seq_len=d.max_seq_len, out=out, workspace=ws)
+
+    for i in range(max(args.warmup, 20)):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    pa.trace_enable(True)
+    pa.trace_read("decode_partition")
+    pa.trace_read("decode_merge")
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    n_main, ms_main = pa.trace_read("decode_partition")
+    n_merge, ms_merge = pa.trace_read("decode_merge")
+    pa.trace_enable(False)
+    kms = ms_main / max(n_main, 1)
+    nbytes = decode_bytes(d.seq_lens, Hq, Hkv, D, bs)
+    gbs, kgbs = nbytes / (ms * 1e-3) / 1e9, nbytes / (kms * 1e-3) / 1e9
+    log(f"TP={tp} share: {ms * 1e3:.1f} us per call, kernel {kms * 1e3:.1f} us")
+    del pools, kc, vc
+    torch.cuda.empty_cache()
+    return {"workload": case.name, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "algorithmic_bytes": nbytes, "pool_copies_cycled": copies,
+            "us_per_call": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "seqs_per_s": round(d.num_seqs / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(kgbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(kgbs / HBM_PEAK_GBS, 4), "launch_us": round(kms * 1e3, 2),
+                         "merge_launch_us": round(ms_merge / max(n_merge, 1) * 1e3, 2)}}
+
+
+def cpu_baseline(args):
+    """The fp64 oracle (gather + attention, NumPy) on every workload, spread over the host's
+    cores: each worker process runs the unchanged oracle on a share of the sequences (or of the
+    chunk's query rows).  Input generation, the oracle's reshape of the step's new tokens and
+    writing the pools for the workers are outside the timed region.  Median of --cpu-runs runs
+    (one if a run exceeds 60 s)."""
+    from oracle import paged_attention as oracle
+    from oracle import pool
+    from workloads import named_case
+
+    pool.warm_up()
+    cores = pool.workers()
+
+    def timed(fn):
+        runs = []
+        while len(runs) < max(args.cpu_runs, 1):
+            t0 = time.perf_counter()
+            fn()
+            runs.append(time.perf_counter() - t0)
+            if runs[-1] > 60:
+                break
+        return float(np.median(runs)), len(runs)
+
+    per = {}
+    for cfg in (1, 2, 3, 4, 5):
+        case = named_case(cfg)
+        kc, vc = case.key_cache, case.value_cache
+        if case.reshape is not None:
+            r = case.reshape
+            kc, vc = oracle.reshape_and_cache(kc, vc, r.key, r.value, r.slot_mapping,
+                                              case.num_kv_heads, case.head_dim, case.block_size)
+        d = case.decode
+        sc = dict(num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                  block_size=case.block_size, scale=case.scale)
+        st = pool.Staged(dict(query=d.query, key_cache=kc, value_cache=vc,
+                              block_tables=d.block_tables, seq_lens=d.seq_lens))
+        try:
+            sec, n = timed(lambda: st.run("decode", sc, "seqs", range(d.num_seqs)))
+        finally:
+            st.remove()
+        nbytes = decode_bytes(d.seq_lens, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                              case.block_size)
+        per[case.name] = {"seconds": round(sec, 4), "runs": n, "gbs": round(nbytes / sec / 1e9, 4),
+                          "seqs_per_s": round(d.num_seqs / sec, 2),
+                          "sample": f"decode of all {d.num_seqs} sequences"}
+        if case.prefill is not None:
+            # Two rows of every 16-token query tile (its first and last): a bounded sample.
+            p = case.prefill
+            rows = sorted({r for t in range(0, p.total_q, 16)
+                           for r in (t, min(t + 15, p.total_q - 1))})
+            stp = pool.Staged(dict(query=p.query, key_cache=kc, value_cache=vc,
+                                   block_tables=p.block_tables, query_start_loc=p.query_start_loc,
+                                   seq_lens=p.seq_lens))
+            try:
+                psec, pn = timed(lambda: stp.run("prefill_chunk", sc, "rows", rows))
+            finally:
+                stp.remove()
+            ctx = int(p.seq_lens[0]) - p.total_q  # one sequence's chunk
+            flops = 4 * case.head_dim * case.num_q_heads * sum(ctx + r + 1 for r in rows)
+            per[case.name + " (prefill chunk)"] = {
+                "seconds": round(psec, 4), "runs": pn,
+                "tflops": round(flops / psec / 1e12, 6),
+                "sample": f"{len(rows)} of {p.total_q} query rows (the first and last of every "
+                          f"16-row tile), all {case.num_q_heads} heads"}
+        del case, kc, vc
+    head = per["llama70b_decode_b128"]
+    try:
+        import platform
+
+        cpu_model = platform.processor() or platform.machine()
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        cpu_model = None
+    return {"value": head["gbs"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "host_cores_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
+            "seconds_per_call": head["seconds"], "seqs_per_s": head["seqs_per_s"],
+            "sample": f"the whole 128-sequence batch, {cores} worker processes each running the "
+                      f"fp64 NumPy oracle (gather + einsum, one thread each) on a share of the "
+                      f"sequences; median of {head['runs']} runs",
+            "per_config": per}
 
 
 if __name__ == "__main__":

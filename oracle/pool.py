@@ -1,4 +1,5 @@
-"""The CPU oracle's row-independent calls spread over host processes (test infrastructure).
+"""The CPU oracle's row-independent calls spread over host processes — test infrastructure
+(used by tests/ and by the benchmark's CPU-baseline leg; never by the library).
 
 The oracle computes every query row of a prefill chunk, and every sequence of a decode batch, on
 its own: the row's or sequence's output depends only on its own query and its own keys.  A
@@ -93,6 +94,42 @@ def _call(func_name: str, paths: Dict[str, str], scalars: dict, key: str,
     return np.asarray(out[part] if key == "seqs" else out)
 
 
+class Staged:
+    """A case's arrays written once to .npy files for the workers; remove() deletes them."""
+
+    def __init__(self, arrays: Dict[str, np.ndarray]):
+        self.dir = tempfile.mkdtemp(dir=_scratch_dir())
+        self.paths = {}
+        for k, a in arrays.items():
+            self.paths[k] = os.path.join(self.dir, k + ".npy")
+            np.save(self.paths[k], np.ascontiguousarray(a))
+
+    def run(self, func_name: str, scalars: dict, key: str, items: Sequence[int],
+            parts: Optional[int] = None) -> np.ndarray:
+        """oracle.<func_name>(**arrays, **scalars, <key>=items) computed in parts on the workers,
+        the outputs of `items` stacked in the order given."""
+        items = [int(i) for i in items]
+        if not items:
+            return np.zeros((0,))
+        n = parts or min(len(items), 2 * workers())
+        bounds = np.linspace(0, len(items), n + 1).astype(int)
+        chunks = [items[a:b] for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+        futs = [_pool().submit(_call, func_name, self.paths, scalars, key, c) for c in chunks]
+        return np.concatenate([f.result() for f in futs], axis=0)
+
+    def remove(self) -> None:
+        shutil.rmtree(self.dir, ignore_errors=True)
+
+
+def warm_up() -> None:
+    """Start every worker process (so that a timed run does not include their start-up)."""
+    list(_pool().map(_noop, range(4 * workers())))
+
+
+def _noop(i: int) -> int:
+    return i
+
+
 def run(func_name: str, arrays: Dict[str, np.ndarray], scalars: dict, key: str,
         items: Sequence[int], parts: Optional[int] = None) -> np.ndarray:
     """oracle.<func_name>(**arrays, **scalars, <key>=items), computed in parts on the workers.
@@ -100,22 +137,11 @@ def run(func_name: str, arrays: Dict[str, np.ndarray], scalars: dict, key: str,
     Returns the outputs of `items` stacked in the order given ([len(items)][...]).  `key` is
     "rows" for the prefill functions and "seqs" for the decode functions.
     """
-    items = [int(i) for i in items]
-    if not items:
-        return np.zeros((0,))
-    d = tempfile.mkdtemp(dir=_scratch_dir())
+    st = Staged(arrays)
     try:
-        paths = {}
-        for k, a in arrays.items():
-            paths[k] = os.path.join(d, k + ".npy")
-            np.save(paths[k], np.ascontiguousarray(a))
-        n = parts or min(len(items), 2 * workers())
-        bounds = np.linspace(0, len(items), n + 1).astype(int)
-        chunks = [items[a:b] for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
-        futs = [_pool().submit(_call, func_name, paths, scalars, key, c) for c in chunks]
-        return np.concatenate([f.result() for f in futs], axis=0)
+        return st.run(func_name, scalars, key, items, parts)
     finally:
-        shutil.rmtree(d, ignore_errors=True)
+        st.remove()
 
 
 def prefill_rows(func_name: str, query, key_cache, value_cache, block_tables, query_start_loc,

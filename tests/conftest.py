@@ -17,6 +17,6 @@ def pytest_collection_finish(session):
     # Their forkserver starts here, before any test initialises the GPU, so no process holding
     # GPU state is forked.
     if any(item.get_closest_marker("gpu") for item in session.items):
-        import oracle_pool
+        from oracle import pool as oracle_pool
 
         oracle_pool.start()

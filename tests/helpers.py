@@ -120,7 +120,7 @@ def cached_fp8_pools(cfg_id: int):
 def full_decode_oracle(cfg_id: int, fp8: bool = False) -> np.ndarray:
     """Oracle decode of every sequence of a named workload ([B][Hq][D] float64), over the pools
     after the step's reshape (bf16, or their E4M3 codes), computed on several host processes."""
-    import oracle_pool
+    from oracle import pool as oracle_pool
 
     case = cached_named_case(cfg_id)
     d = case.decode
@@ -136,7 +136,7 @@ def full_prefill_oracle(cfg_id: int, fp8: bool = False) -> np.ndarray:
     """Oracle output of every query row of a named workload's prefill chunk ([total_q][Hq][D]
     float64), over the pools after the chunk's reshape (bf16, or their E4M3 codes), computed on
     several host processes."""
-    import oracle_pool
+    from oracle import pool as oracle_pool
 
     case = cached_named_case(cfg_id)
     p = case.prefill
@@ -146,3 +146,22 @@ def full_prefill_oracle(cfg_id: int, fp8: bool = False) -> np.ndarray:
                                     vc, p.block_tables, p.query_start_loc, p.seq_lens,
                                     case.num_kv_heads, case.head_dim, case.block_size, case.scale,
                                     **extra)
+
+
+@functools.lru_cache(maxsize=1)
+def cached_tp_share_case(tp: int = 8) -> Case:
+    from workloads import tp_share_case
+
+    return tp_share_case(tp)
+
+
+@functools.lru_cache(maxsize=1)
+def full_tp_share_oracle(tp: int = 8) -> np.ndarray:
+    """Oracle decode of every sequence of the 70B-shaped batch's tensor-parallel share."""
+    from oracle import pool as oracle_pool
+
+    case = cached_tp_share_case(tp)
+    d = case.decode
+    return oracle_pool.decode_seqs("decode", d.query, case.key_cache, case.value_cache,
+                                   d.block_tables, d.seq_lens, case.num_kv_heads, case.head_dim,
+                                   case.block_size, case.scale)

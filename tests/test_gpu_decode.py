@@ -12,8 +12,9 @@ import pytest
 import torch
 
 import paged_kv_cache_444_amd as pa
-from helpers import (assert_close, cached_named_case, cached_oracle_pools, dev_i32, dev_i64,
-                     dev_u16, full_decode_oracle, host_u16, oracle_pools_after_reshape, upcast)
+from helpers import (assert_close, cached_named_case, cached_oracle_pools, cached_tp_share_case,
+                     dev_i32, dev_i64, dev_u16, full_decode_oracle, full_tp_share_oracle, host_u16,
+                     oracle_pools_after_reshape, upcast)
 from oracle import paged_attention as oracle
 from workloads import Spec, build_case
 
@@ -92,6 +93,22 @@ def test_decode_parity_named(cfg):
     got = upcast(gpu_decode(case, kc, vc))
     # every sequence of the batch (the oracle runs on several host processes)
     assert_close(got, full_decode_oracle(cfg), f"decode cfg{cfg}")
+
+
+@pytest.mark.parametrize("step", STEPS)
+def test_decode_parity_tp8_share(step, tune):
+    """One GPU's share of the 70B-shaped batch-128 decode at tensor parallelism 8 over KV heads:
+    8 query heads on 1 KV head, the same 128 lognormal lengths.  With one KV head the workgroup
+    head-quad split is off and every sequence is spread over several waves, so this runs the
+    per-wave split and the merge of many pieces per sequence."""
+    case = cached_tp_share_case(8)
+    d = case.decode
+    say(f"decode TP=8 share: {case.name}, Hq={case.num_q_heads}, Hkv={case.num_kv_heads}")
+    tune("PA_DECODE_MFMA", step)
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    a = gpu_decode(case, kc, vc)
+    assert np.array_equal(a, gpu_decode(case, kc, vc)), "not reproducible"
+    assert_close(upcast(a), full_tp_share_oracle(8), f"decode, TP=8 share ({step})")
 
 
 # ------------------------------------------------------------------------- shapes and edges

@@ -2,7 +2,7 @@
 
 import numpy as np
 
-import oracle_pool
+from oracle import pool as oracle_pool
 from oracle import fp8
 from oracle import paged_attention as oracle
 from workloads import Spec, build_case

@@ -20,4 +20,5 @@ from .inputs import (  # noqa: F401
     lognormal_lengths,
     named_case,
     NAMED_CASES,
+    tp_share_case,
 )

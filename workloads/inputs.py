@@ -483,6 +483,25 @@ def _spec_prefix_shared() -> Spec:
                 share_groups=groups)
 
 
+def _spec_tp_share(tp: int = 8) -> Spec:
+    # One GPU's share of the Llama-3.3-70B-shaped decode when its 8 KV heads are split over `tp`
+    # GPUs: the same 128 sequences and lengths as the batch-128 workload, with 8/tp KV heads and
+    # their 64/tp query heads.
+    rng = np.random.default_rng([444, 2, 0])
+    lens = lognormal_lengths(rng, 128)
+    return Spec(name=f"llama70b_decode_b128_tp{tp}_share", num_q_heads=64 // tp,
+                num_kv_heads=8 // tp, head_dim=128, block_size=16, seed=(444, 2, tp),
+                decode_lens=lens.tolist())
+
+
+def tp_share_case(tp: int = 8) -> Case:
+    """The 70B-shaped batch-128 decode as one GPU's share under tensor parallelism over KV heads
+    (tp divides 8): Hq = 64/tp, Hkv = 8/tp, same lengths."""
+    if tp not in (1, 2, 4, 8):
+        raise ValueError("tp must divide the 8 KV heads")
+    return build_case(_spec_tp_share(tp))
+
+
 NAMED_CASES = {
     1: _spec_tiny,
     2: _spec_llama70b_decode,

@@ -105,16 +105,14 @@ __device__ __forceinline__ void lds_dma_16(const uint16_t* src, unsigned m0) {
                : "memory", "m0");
 }
 
-// Where this wave's tile loads come from and go to; everything but `pool` and `sb` is
+// Where this wave's tile loads come from and go to; everything but `pool`, `pool8` and `sb` is
 // wave-uniform.
 struct TileSrc {
   const uint16_t* pool;    // K or V pool + KV head h + this lane's offset inside a piece
   const uint8_t* pool8;    // the same for FP8 pools (byte addressing)
-  long long block_stride;  // elements per physical block (all KV heads)
   unsigned lds;            // LDS byte address of this wave's first piece in stage 0
   int sb;                  // sub-block (0: keys 0-15 of the tile, 1: keys 16-31) of this lane
   int piece_step;          // source elements between this wave's consecutive pieces
-  int shift, bmask, max_id;  // log2(block_size), block_size - 1, num_blocks - 1
 };
 
 // Lane l of K piece (kt, ks): key kappa = 8*((l%16)/4) + l%4 + 4*kt of the tile, dims
@@ -125,10 +123,6 @@ __device__ __forceinline__ TileSrc tile_src(const PrefillParams& p, int h, const
   const int lane = threadIdx.x & 63;
   const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   TileSrc ts;
-  ts.shift = (p.block_size == 32) ? 5 : 4;
-  ts.bmask = p.block_size - 1;
-  ts.max_id = (int)(p.num_blocks - 1);
-  ts.block_stride = (long long)p.num_kv_heads * p.block_size * D;
   int off, first_piece;
   if constexpr (Fp8) {
     // Fetching lane j: piece (j/32) of the load's two, lane pair q = j%32, whose first lane is
@@ -174,29 +168,20 @@ __device__ __forceinline__ TileSrc tile_src(const PrefillParams& p, int h, const
   return ts;
 }
 
+// Issue this wave's loads of one tile into LDS stage `stage`.  `off` is the element offset in the
+// pool of the 16-key sub-block this lane's key lies in (its block's start plus the sub-block's
+// place in the block), from the workgroup's offset table.
 template <int D, bool Fp8>
-__device__ __forceinline__ void issue_tile(const TileSrc& ts, const int* ids_lds, int blk0,
-                                           int tile, int L, int stage) {
+__device__ __forceinline__ void issue_tile(const TileSrc& ts, long long off, int stage) {
   constexpr int NP = Fp8 ? D / 64 : D / 32;  // loads per wave
-  // Physical blocks of the tile's two sub-blocks.  Keys at or past L fetch block 0 (always
-  // inside the pool): their V rows are zeroed before use and their scores are masked.
-  long long base[2];
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const int key0 = tile * kKeyTile + 16 * sb;
-    int id = 0;
-    if (key0 < L) id = ids_lds[min(max((key0 >> ts.shift) - blk0, 0), kMaxTableLds - 1)];
-    id = min(max(__builtin_amdgcn_readfirstlane(id), 0), ts.max_id);  // stays inside the pool
-    base[sb] = (long long)id * ts.block_stride + (long long)(key0 & ts.bmask) * D;
-  }
   const unsigned m0 = ts.lds + (unsigned)stage * (4 * 16 * D * 2);
   if constexpr (Fp8) {
-    const uint8_t* src = ts.pool8 + (ts.sb ? base[1] : base[0]);  // one byte per element
+    const uint8_t* src = ts.pool8 + off;  // one byte per element
 #pragma unroll
     for (int pc = 0; pc < NP; ++pc)
       lds_dma_16(reinterpret_cast<const uint16_t*>(src + pc * ts.piece_step), m0 + pc * 1024);
   } else {
-    const uint16_t* src = ts.pool + (ts.sb ? base[1] : base[0]);
+    const uint16_t* src = ts.pool + off;
 #pragma unroll
     for (int pc = 0; pc < NP; ++pc) lds_dma_16(src + pc * ts.piece_step, m0 + pc * 1024);
   }
@@ -221,7 +206,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   constexpr int TQ = ROWS / G;     // query tokens per workgroup
   constexpr int TILE_ELEMS = 4 * 16 * D;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kStages][TILE_ELEMS];
-  __shared__ int ids_lds[kMaxTableLds];
+  // Pool element offset of every 16-key sub-block of this workgroup's key range, in key order.
+  __shared__ long long off_lds[kMaxTableLds];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -258,7 +244,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     row_lim[rt] = min(ctx + row_tok[rt], L - 1);  // last visible key
   }
 
-  // Q operand: rows as B, 32 dims per k-step, lane holds dims 8*(lane/16) .. +7.
+  // Q operand: rows as B, 32 dims per k-step, lane holds dims 8*(lane/16) .. +7.  The softmax
+  // scale times log2(e) is applied here, once (fp32 product rounded to bf16, nearest even), so
+  // the score product yields log2-domain scores y = q·k·scale·log2(e) directly.
   uint4 qb[RT][KS];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -269,24 +257,30 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint4 v = *(const uint4*)(p.query + qrow * D + 32 * ks + 8 * (lane >> 4));
-      qb[rt][ks] = row_ok[rt] ? v : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 sv = make_uint4(pack_bf16x2(bf16_lo(v.x) * c, bf16_hi(v.x) * c),
+                                  pack_bf16x2(bf16_lo(v.y) * c, bf16_hi(v.y) * c),
+                                  pack_bf16x2(bf16_lo(v.z) * c, bf16_hi(v.z) * c),
+                                  pack_bf16x2(bf16_lo(v.w) * c, bf16_hi(v.w) * c));
+      qb[rt][ks] = row_ok[rt] ? sv : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 
-  // Online-softmax state per row (the same in the four lanes sharing a row): m is the running
-  // maximum of raw scores, nmc = -m * scale * log2(e) (0 while m is -inf), thr = m + slack.
+  // Online-softmax state per row (the same in the four lanes sharing a row), in the log2
+  // domain: M is the running maximum of the row's scores y (-inf before its first key), and
+  // cz = -M (0 while M is -inf) is the initial accumulator of every score product, so the
+  // products yield z = y - M and the probabilities are exp2(z) with no further vector work.
+  // thr bounds z: -inf until M is set, then the slack; a z above it raises M (and rescales).
   // The running sum of the row's probabilities is accumulated on the matrix cores as one more
   // product, an all-ones A operand times the bf16 probabilities, so every element of lsum[rt]
   // holds the sum of the row the lane's column belongs to (the same rounded probabilities that
   // weight V).
-  f32x4_t acc[DT][RT], lsum[RT];
-  float m[RT], nmc[RT], thr[RT];
-  const float slack_raw = kRescaleSlack / c;
+  f32x4_t acc[DT][RT], lsum[RT], cz[RT];
+  float M[RT], thr[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    m[rt] = kNegInf;
-    nmc[rt] = 0.f;
+    M[rt] = kNegInf;
     thr[rt] = kNegInf;
+    cz[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     lsum[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -297,23 +291,29 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   const int t_end = (ke + kKeyTile - 1) / kKeyTile;  // empty range: t_end <= t_first
   // Keys above this need a per-row mask (non-causal: only keys at or past L, in the last tile).
   const int diag = p.noncausal ? L - 1 : ctx + q0;
-  // Table slice of this workgroup's keys [32*t_first, 32*t_end), clamped into the pool.
+  // Offset table of this workgroup's keys [32*t_first, 32*t_end): for 16-key sub-block j (keys
+  // 32*t_first + 16j ..), its physical block (clamped into the pool) times the block's size plus
+  // the sub-block's place in the block.  Sub-blocks at or past L point at block 0, always inside
+  // the pool: their V rows are zeroed before use and their scores are masked.
   const int bs = p.block_size;
-  const int blk0 = (t_first * kKeyTile) / bs;
-  const int nblk = (t_first < t_end) ? min(kMaxTableLds, (min(t_end * kKeyTile, L) - 1) / bs - blk0 + 1)
-                                     : 0;
   {
+    const int shift = (bs == 32) ? 5 : 4;
+    const long long block_stride = (long long)p.num_kv_heads * bs * D;
+    const int nsb = (t_first < t_end) ? min(2 * (t_end - t_first), kMaxTableLds) : 0;
     constexpr int kPer = kMaxTableLds / kPThreads;
     int v[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int i = threadIdx.x + kPThreads * k;
-      v[k] = (i < nblk) ? bt[blk0 + i] : 0;
+      const int key = (2 * t_first + i) * 16;
+      v[k] = (i < nsb && key < L) ? bt[key >> shift] : 0;
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int i = threadIdx.x + kPThreads * k;
-      ids_lds[i] = (i < nblk) ? min(max(v[k], 0), (int)(p.num_blocks - 1)) : 0;  // all valid ids
+      const int key = (2 * t_first + i) * 16;
+      const int id = min(max(v[k], 0), (int)(p.num_blocks - 1));
+      off_lds[i] = (i < nsb) ? (long long)id * block_stride + (long long)(key & (bs - 1)) * D : 0;
     }
   }
   // Every ordinary vector-memory load (query rows, table slice) is complete before the walk, so
@@ -323,9 +323,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   if (t_first < t_end) {
     constexpr int NP = Fp8 ? D / 64 : D / 32;  // tile loads per wave
     const TileSrc ts = tile_src<D, Fp8>(p, h, &lds[0][0]);
+    // This lane's sub-block offset for tile t (clamped to the range's last tile).
+    auto tile_off = [&](int t) __attribute__((always_inline)) {
+      return off_lds[min(2 * (min(t, t_end - 1) - t_first) + ts.sb, kMaxTableLds - 1)];
+    };
 #pragma unroll
-    for (int k = 0; k < kStages - 1; ++k)
-      issue_tile<D, Fp8>(ts, ids_lds, blk0, min(t_first + k, t_end - 1), L, k);
+    for (int k = 0; k < kStages - 1; ++k) issue_tile<D, Fp8>(ts, tile_off(t_first + k), k);
     // One key tile.  kMasked: the tile reaches past the first row's diagonal and the causal mask
     // is applied per score; those tiles are the last ones of the walk, so the two variants run
     // as two loops and the other tiles carry no per-score selects.
@@ -334,9 +337,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     auto walk_tile = [&](int t, auto masked_c) __attribute__((always_inline)) {
       constexpr bool kMasked = decltype(masked_c)::value;
       const int prev = (cur == 0) ? kStages - 1 : cur - 1;  // tile t-1's stage, free below
+      const long long next_off = tile_off(t + kStages - 1);  // read while the barrier waits
       wait_vmcnt<NP * (kStages - 2)>();  // this wave's part of tile t has landed
       __syncthreads();                   // all parts landed; every wave is done with tile t-1
-      issue_tile<D, Fp8>(ts, ids_lds, blk0, min(t + kStages - 1, t_end - 1), L, prev);
+      issue_tile<D, Fp8>(ts, next_off, prev);
       if (t * kKeyTile + kKeyTile > L) {  // block-uniform: zero V rows of keys at or past L
         if constexpr (Fp8) {
           uint8_t* vz = reinterpret_cast<uint8_t*>(&lds[cur][0]) + 32 * D;
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       auto scores = [&](int rt, f32x4_t (&sc)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          sc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          sc[kt] = cz[rt];  // z = y - M
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) sc[kt] = mfma(kf[kt][ks], qb[rt][ks], sc[kt]);
         }
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       // Online softmax of row tile rt, then its second product with the V fragments vf.
       auto softmax_pv = [&](int rt, const f32x4_t (&sc)[2], auto&& vf)
                             __attribute__((always_inline)) {
-        float x[8];  // raw scores; -inf where masked
+        float x[8];  // z = y - M; -inf where masked
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -414,20 +418,25 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
           for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
           mx = fmaxf(mx, xor16_f32(mx));
           mx = fmaxf(mx, xor32_f32(mx));
-          const float mn = fmaxf(m[rt], mx);  // raw units
-          if (mn != kNegInf && mn != m[rt]) {
-            const float alpha = fast_exp2((m[rt] - mn) * c);  // 0 when the old max is -inf
+          const float cz0 = cz[rt][0];
+          const float mn = fmaxf(M[rt], mx - cz0);  // the row's new maximum of y
+          if (mn != kNegInf && mn != M[rt]) {
+            const float alpha = fast_exp2(M[rt] - mn);  // 0 when the old max is -inf
             lsum[rt] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[dt][rt] *= alpha;
-            m[rt] = mn;
-            nmc[rt] = -mn * c;
-            thr[rt] = mn + slack_raw;
+            M[rt] = mn;
+            thr[rt] = kRescaleSlack;
+            // this tile's scores were taken against the old maximum: move them to the new one
+            const float shift = cz0 + mn;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] -= shift;
+            cz[rt] = f32x4_t{-mn, -mn, -mn, -mn};
           }
         }
         float pr[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, nmc[rt]));
+        for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(x[i]);
         // B operand of the second product: item j is key 8*(lane/16) + j of the tile (the V
         // fragments use the same order).
         const uint4 pb = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
@@ -483,7 +492,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     } else {
       const size_t u = orow * p.ws_splits + split;
       if (lane < 16) {
-        p.ws_ml[2 * u] = m[rt] * c;  // log2 domain; -inf for an empty or fully masked range
+        p.ws_ml[2 * u] = M[rt];  // log2 domain; -inf for an empty or fully masked range
         p.ws_ml[2 * u + 1] = lt;
       }
 #pragma unroll

@@ -323,6 +323,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   if (t_first < t_end) {
     constexpr int NP = Fp8 ? D / 64 : D / 32;  // tile loads per wave
     const TileSrc ts = tile_src<D, Fp8>(p, h, &lds[0][0]);
+    // The all-ones A operand of the row-sum product.  Passed through an empty asm statement it is
+    // opaque to the compiler, which then keeps it in four registers instead of rebuilding it in
+    // every tile.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+    u32x4_t ones_v = {kOnes, kOnes, kOnes, kOnes};
+    asm volatile("" : "+v"(ones_v));
+    const uint4 ones = __builtin_bit_cast(uint4, ones_v);
     // This lane's sub-block offset for tile t (clamped to the range's last tile).
     auto tile_off = [&](int t) __attribute__((always_inline)) {
       return off_lds[min(2 * (min(t, t_end - 1) - t_first) + ts.sb, kMaxTableLds - 1)];
@@ -441,8 +449,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
         // fragments use the same order).
         const uint4 pb = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                                     pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
-        constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
-        lsum[rt] = mfma(make_uint4(kOnes, kOnes, kOnes, kOnes), pb, lsum[rt]);
+        lsum[rt] = mfma(ones, pb, lsum[rt]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = mfma(vf(dt), pb, acc[dt][rt]);
       };

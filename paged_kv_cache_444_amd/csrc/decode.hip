@@ -644,6 +644,74 @@ __device__ __forceinline__ void compute_mstep(const MStepRegs<D, Fp8>& r,
         __builtin_bit_cast(s16x4_t, pb), st.acc[m], 0, 0, 0);
 }
 
+// End of a matrix-core piece of unit u = (s, h): normalise and write the output (the unit lies
+// wholly in the piece), or hand the unnormalised state to the cascade's state slot, or write the
+// piece's partial slot (or `coop`, the wave's LDS slot of a shared piece).
+template <int D, int G>
+__device__ __forceinline__ void finish_mpiece(const DecodeParams& p, const MState<D>& st, int s,
+                                              int h, int u, long long w, bool whole,
+                                              float* coop) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int Hq = p.num_q_heads;
+  const float c = p.scale_log2;
+  // The column's sum over its four lanes; lane (r16, q4) holds dims 16m + 4*q4 + i.
+  float lt = st.l + xor16_f32(st.l);
+  lt += __shfl_xor(lt, 32, 64);
+  if (r16 >= G) return;
+  const int g = r16;
+  float* slot = coop ? coop : p.partials + slot_of(p, w, u) * (G * (2 + D));
+  uint16_t* orow = p.out + ((size_t)s * Hq + (size_t)h * G + g) * D;
+  if (whole && p.state_ml) {
+    const size_t su = state_slot(p, (size_t)s * Hq + (size_t)h * G + g);
+    if (q4 == 0) {
+      p.state_ml[2 * su] = st.m * c;
+      p.state_ml[2 * su + 1] = lt;
+    }
+#pragma unroll
+    for (int m = 0; m < D / kSub; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p.state_acc[su * D + kSub * m + 4 * q4 + e] = st.acc[m][e] * p.v_scale;
+    return;
+  }
+  if (whole) {
+#pragma unroll
+    for (int m = 0; m < D / kSub; ++m) {
+      const f32x4_t a = st.acc[m];
+      *(uint2*)(orow + kSub * m + 4 * q4) =
+          make_uint2(pack_bf16x2(a[0] * p.v_scale / lt, a[1] * p.v_scale / lt),
+                     pack_bf16x2(a[2] * p.v_scale / lt, a[3] * p.v_scale / lt));
+    }
+    return;
+  }
+  if (q4 == 0) {
+    slot[g] = st.m * c;  // the merge works in the log2 domain
+    slot[G + g] = lt;
+  }
+  // Scalar stores: a slot holds G*(2+D) floats, so it is only 4-byte aligned when G is odd.
+#pragma unroll
+  for (int m = 0; m < D / kSub; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) slot[2 * G + g * D + kSub * m + 4 * q4 + e] = st.acc[m][e];
+}
+
+// B operand of the score product for the G query heads of (sequence s, KV head h): head r16
+// (zero past G), dims 8*q4 .. +7 of each 32-dim slice.
+template <int D, int G>
+__device__ __forceinline__ void load_qb(uint4 (&qb)[D / kSlice], const DecodeParams& p, int s,
+                                        int h) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const uint16_t* qg =
+      p.query + ((size_t)s * p.num_q_heads + (size_t)h * G + min(r16, G - 1)) * D + 8 * q4;
+#pragma unroll
+  for (int sl = 0; sl < D / kSlice; ++sl) {
+    const uint4 v = *(const uint4*)(qg + kSlice * sl);
+    qb[sl] = r16 < G ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
 // decode_piece on the matrix cores (same contract and partial-slot format).
 template <int D, int G, int Depth, bool Stream, bool Fp8>
 __device__ __forceinline__ void decode_piece_mfma(const DecodeParams& p, int s, int h, int j0,
@@ -732,45 +800,170 @@ __device__ __forceinline__ void decode_piece_mfma(const DecodeParams& p, int s, 
     }
   }
 
-  // Finish: the column's sum over its four lanes; lane (r16, q4) holds dims 16m + 4*q4 + i.
-  float lt = st.l + xor16_f32(st.l);
-  lt += __shfl_xor(lt, 32, 64);
-  if (r16 >= G) return;
-  const int g = r16;
-  float* slot = coop ? coop : p.partials + slot_of(p, w, u) * (G * (2 + D));
-  uint16_t* orow = p.out + ((size_t)s * Hq + (size_t)h * G + g) * D;
-  if (whole && p.state_ml) {
-    const size_t su = state_slot(p, (size_t)s * Hq + (size_t)h * G + g);
-    if (q4 == 0) {
-      p.state_ml[2 * su] = st.m * c;
-      p.state_ml[2 * su + 1] = lt;
-    }
+  finish_mpiece<D, G>(p, st, s, h, u, w, whole, coop);
+}
+
+// Where a piece's K/V come from: its sequence's table row (after a skipped prefix), a window of
+// 64 block ids of that row starting at logical block `win` (one per lane), and its KV head.
+struct MPieceSrc {
+  const int* bt;
+  int cols, win, ids;
+  size_t head_off;
+};
+
+// The static range [x, x1) of worker v on the matrix cores, piece after piece, with the next
+// piece's loads started early: its query operand and block-id window when the current piece
+// starts, and its first K/V step in the prefetch slot of the current piece's last step (where a
+// single piece would load nothing new).  A piece boundary then costs no dependent round trip.
+// Same pieces, partial slots and arithmetic as run_worker with decode_piece_mfma.
+template <int D, int G, bool Stream, bool Fp8>
+__device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Plan& plan,
+                                                long long v, int s, long long off, long long jn,
+                                                long long x, long long x1, bool quad) {
+  const int B = p.num_seqs;
+  const int U = quad ? p.num_kv_heads / kWaves : p.num_kv_heads;
+  if (x >= x1 || s < 0 || s >= B) return;
+  int n_s = steps_of(p, s);
+  if (n_s == 0) return;  // unreachable: every step lies in a sequence with steps
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int bs = p.block_size;
+  const int shift = (bs == 32) ? 5 : 4;
+  const size_t tile = (size_t)bs * D;
+  const size_t block_elems = (size_t)p.num_kv_heads * tile;
+  const float c = p.scale_log2;
+  const float slack_raw = kRescaleSlack / c;
+  auto head_of = [&](int unit) { return quad ? unit * kWaves + wave : unit; };
+  // Source of a piece of unit (ss, hh) starting at step j0: issues its block-id window load.
+  auto src_of = [&](int ss, int hh, int j0) __attribute__((always_inline)) {
+    MPieceSrc r;
+    const int skip_b = skip_blocks(p, ss);
+    r.bt = p.block_tables + (size_t)ss * p.max_blocks_per_seq + skip_b;
+    r.cols = p.max_blocks_per_seq - skip_b;
+    r.win = (j0 * kSub) / bs;
+    const int id = (r.win + lane < r.cols) ? r.bt[r.win + lane] : 0;
+    r.ids = min(max(id, 0), (int)(p.num_blocks - 1));
+    r.head_off = (size_t)hh * tile;
+    return r;
+  };
+  // K/V loads of one 16-token step at element offset `o` of the pools.
+  auto issue = [&](MStepRegs<D, Fp8>& r, size_t o) __attribute__((always_inline)) {
+    const int r16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
-    for (int m = 0; m < D / kSub; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        p.state_acc[su * D + kSub * m + 4 * q4 + e] = st.acc[m][e] * p.v_scale;
-    return;
-  }
-  if (whole) {
+    for (int sl = 0; sl < D / kSlice; ++sl)
+      r.k[sl] = load_elems<Stream, Fp8>(p.kpool, o + sl * (kSub * kSlice) + r16 * kSlice + 8 * q4);
 #pragma unroll
     for (int m = 0; m < D / kSub; ++m) {
-      const f32x4_t a = st.acc[m];
-      *(uint2*)(orow + kSub * m + 4 * q4) =
-          make_uint2(pack_bf16x2(a[0] * p.v_scale / lt, a[1] * p.v_scale / lt),
-                     pack_bf16x2(a[2] * p.v_scale / lt, a[3] * p.v_scale / lt));
+      const size_t e = o + (size_t)(kSub * m + r16) * kSub + 4 * q4;
+      if constexpr (Fp8) r.v[m] = load4<Stream>(reinterpret_cast<const uint8_t*>(p.vpool) + e);
+      else r.v[m] = load8_u16<Stream>(p.vpool + e);
     }
-    return;
+  };
+
+  int hu = (int)(off / n_s);
+  int j = (int)(off % n_s);
+  int h = head_of(hu);
+  MPieceSrc cs = src_of(s, h, j);
+  uint4 qb[D / kSlice];
+  load_qb<D, G>(qb, p, s, h);
+  MStepRegs<D, Fp8> ra, rb;
+  {
+    const int b = (j * kSub) >> shift;  // inside the window just loaded
+    const int id = __builtin_amdgcn_readlane(cs.ids, b - cs.win);
+    issue(ra, (size_t)id * block_elems + cs.head_off + (size_t)((j * kSub) & (bs - 1)) * D);
   }
-  if (q4 == 0) {
-    slot[g] = st.m * c;  // the merge works in the log2 domain
-    slot[G + g] = lt;
+  bool in_a = true;  // the current piece's first step is in ra
+  while (true) {
+    const int take = (int)min((long long)(n_s - j), x1 - x);
+    // The next piece of this worker: the next unit with steps, if the range goes on.
+    int s2 = s, hu2 = hu, n2 = n_s;
+    bool more = x + take < x1;
+    if (more && ++hu2 == U) {
+      hu2 = 0;
+      do {
+        ++s2;
+        n2 = (s2 < B) ? steps_of(p, s2) : 0;
+      } while (s2 < B && n2 == 0);
+      more = s2 < B;
+    }
+    if (!more) {  // nothing follows: the "next" source is this piece (its loads hit in cache)
+      s2 = s;
+      hu2 = hu;
+      n2 = n_s;
+    }
+    const int h2 = head_of(hu2);
+    MPieceSrc ns = src_of(s2, h2, 0);
+    uint4 qn[D / kSlice];
+    load_qb<D, G>(qn, p, s2, h2);
+
+    // This piece.
+    const int L = uniform(clamped_len(p, s));
+    const int u = s * p.num_kv_heads + h;
+    const bool whole = (j == 0) && (take == n_s);
+    if (j == 0 && lane == 0) p.unit_info[u] = make_int2((int)v, (int)plan.owner(x + n_s - 1, jn));
+    const int tok_end = min(L, (j + take) * kSub);
+    const int iend = j + take, ilast = iend - 1;
+    MState<D> st;
+    st.m = kNegInf;
+    st.nmc = 0.f;
+    st.thr = kNegInf;
+    st.l = 0.f;
+#pragma unroll
+    for (int m = 0; m < D / kSub; ++m) st.acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Loads of step `step`: inside the piece, or past its end the next piece's first step (the
+    // last step again when nothing follows).  One load path for both, so the compiler's counter
+    // waits stay exact.
+    auto ld = [&](MStepRegs<D, Fp8>& r, int step) __attribute__((always_inline)) {
+      const bool here = step <= ilast || !more;  // wave-uniform
+      int id;
+      size_t hoff, tin;
+      if (here) {
+        const int t0 = min(step, ilast) * kSub;
+        const int b = t0 >> shift;
+        if (b - cs.win >= 64) {  // rare: refill the block-id window
+          cs.win = b;
+          const int i2 = (cs.win + lane < cs.cols) ? cs.bt[cs.win + lane] : 0;
+          cs.ids = min(max(i2, 0), (int)(p.num_blocks - 1));
+        }
+        id = __builtin_amdgcn_readlane(cs.ids, b - cs.win);
+        hoff = cs.head_off;
+        tin = (size_t)(t0 & (bs - 1)) * D;
+      } else {
+        id = __builtin_amdgcn_readlane(ns.ids, 0);
+        hoff = ns.head_off;
+        tin = 0;
+      }
+      issue(r, (size_t)id * block_elems + hoff + tin);
+    };
+    // Steps alternate between two register sets; returns true when the last step was in
+    // `first` (the next piece's first step then sits in `second`).
+    auto walk = [&](MStepRegs<D, Fp8>& first, MStepRegs<D, Fp8>& second)
+                    __attribute__((always_inline)) {
+      int i = j;
+      while (true) {
+        ld(second, i + 1);
+        compute_mstep<D, Fp8>(first, qb, tok_end - i * kSub, c, slack_raw, st);
+        if (++i >= iend) return true;
+        ld(first, i + 1);
+        compute_mstep<D, Fp8>(second, qb, tok_end - i * kSub, c, slack_raw, st);
+        if (++i >= iend) return false;
+      }
+    };
+    const bool swap = in_a ? walk(ra, rb) : walk(rb, ra);
+    finish_mpiece<D, G>(p, st, s, h, u, v, whole, nullptr);
+    if (!more) break;
+    in_a = swap ? !in_a : in_a;
+    x += take;
+    ++jn;
+    s = s2;
+    hu = hu2;
+    n_s = n2;
+    h = h2;
+    j = 0;
+    cs = ns;
+#pragma unroll
+    for (int sl = 0; sl < D / kSlice; ++sl) qb[sl] = qn[sl];
   }
-  // Scalar stores: a slot holds G*(2+D) floats, so it is only 4-byte aligned when G is odd.
-#pragma unroll
-  for (int m = 0; m < D / kSub; ++m)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) slot[2 * G + g * D + kSub * m + 4 * q4 + e] = st.acc[m][e];
 }
 
 // A piece taken by the whole workgroup: wave r runs steps [j0 + take*r/kWaves,
@@ -849,6 +1042,10 @@ __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& pl
                                            int s, long long off, long long jn, long long x,
                                            long long x1, uint16_t (*p_sh)[G][8],
                                            float (*st)[G * (2 + D)] = nullptr, bool quad = false) {
+  if constexpr (Mfma && !Coop && Depth <= 1) {
+    run_worker_mfma<D, G, Stream, Fp8>(p, plan, v, s, off, jn, x, x1, quad);
+    return;
+  }
   const int B = p.num_seqs;
   const int Hkv = quad ? p.num_kv_heads / kWaves : p.num_kv_heads;
   if (x >= x1 || s < 0 || s >= B) return;

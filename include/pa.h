@@ -78,6 +78,11 @@ const char* pa_last_error(void);
  *                           statically; the rest is handed out in dynamic chunks
  *   PA_DECODE_CHUNK         1-256, default 4: smallest dynamic chunk, in steps
  *   PA_PREFILL_SPLITS       0-16, default 0 (automatic): forced context split of a prefill chunk
+ *   PA_DECODE_TAIL_Q10      0-512, default 0: share (in 1/1024) of the head-quad split's steps
+ *                           left to a dynamic tail of chunks that workgroups claim once their
+ *                           static range is done (results stay bitwise reproducible)
+ *   PA_DECODE_TAIL_Q10_FP8  the same for FP8 pools, default 0
+ *   PA_DECODE_TAIL_CHUNK    1-256, default 12: steps per dynamic tail chunk
  * The decode workspace size depends on PA_DECODE_WORKERS: query it after setting that.
  * pa_set_tunable returns PA_ERR_INVALID_ARG for an unknown name or an out-of-range value (the
  * value is then unchanged); pa_get_tunable writes the current value to *value.
@@ -228,8 +233,9 @@ pa_status_t pa_decode_fp8(void* out, const void* query, const void* key_cache,
  * Limit: the batch's scratch (about (num_seqs*num_kv_heads + 4 * CUs) * G * (head_dim + 2) * 4
  * bytes: 8.5 MB for 128 sequences of 8 KV heads, G 8, head_dim 128 on 256 CUs) must fit the
  * array; a larger batch returns PA_ERR_WORKSPACE before anything is launched (use pa_decode).
- * The whole batch is split statically (dynamic chunks are not used), which is also pa_decode's
- * default, so results equal pa_decode's bit for bit under the default tunables.
+ * The whole batch is split statically (no dynamic chunks, no dynamic tail), so results equal
+ * pa_decode's bit for bit when pa_decode's dynamic tail is off (PA_DECODE_TAIL_Q10 = 0), and
+ * agree with them within fp32 rounding otherwise.
  * Every call on a device uses that device's one array, and nothing in it has to start at a set
  * value: calls that overlap in time on one device (different streams, or threads) race on it and
  * give unspecified results; calls ordered on one stream are safe.  Other errors as pa_decode.

@@ -586,7 +586,8 @@ def trace_read(kernel_name: str):
 # never what is computed beyond fp32 rounding order.
 TUNABLES = ("PA_DECODE_PREFETCH", "PA_DECODE_PREFETCH_FP8", "PA_DECODE_MFMA", "PA_DECODE_QUAD",
             "PA_DECODE_PIECE_COST", "PA_DECODE_WORKERS", "PA_DECODE_STATIC_Q10", "PA_DECODE_CHUNK",
-            "PA_PREFILL_SPLITS")
+            "PA_PREFILL_SPLITS", "PA_DECODE_TAIL_Q10", "PA_DECODE_TAIL_Q10_FP8",
+            "PA_DECODE_TAIL_CHUNK")
 
 
 def set_tunable(name: str, value: int) -> None:

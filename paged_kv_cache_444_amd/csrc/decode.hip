@@ -816,13 +816,55 @@ struct MPieceSrc {
 // starts, and its first K/V step in the prefetch slot of the current piece's last step (where a
 // single piece would load nothing new).  A piece boundary then costs no dependent round trip.
 // Same pieces, partial slots and arithmetic as run_worker with decode_piece_mfma.
+//
+// Dynamic tail (quad workers, `tail` set): after its static range the workgroup takes the chunks
+// [S + d*C, S + (d+1)*C) of the step line in claim order (d from the workspace counter; chunk d is
+// worker ns + d, with its own partial slots), each claimed one range ahead so that its first
+// loads can be started inside the range before.  The claims travel through two LDS slots in
+// turn; every wave of the workgroup makes the same decisions, so all reach the same barriers.
 template <int D, int G, bool Stream, bool Fp8>
 __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Plan& plan,
                                                 long long v, int s, long long off, long long jn,
-                                                long long x, long long x1, bool quad) {
+                                                long long x, long long x1, bool quad,
+                                                bool tail = false,
+                                                const int* seq_prefix = nullptr,
+                                                unsigned* sh_claim = nullptr) {
   const int B = p.num_seqs;
   const int U = quad ? p.num_kv_heads / kWaves : p.num_kv_heads;
-  if (x >= x1 || s < 0 || s >= B) return;
+  // Sequence and step offset (within its U * n_s steps) of global step x0 of a dynamic chunk:
+  // the last sequence whose per-head prefix is <= x0 / U.
+  auto locate = [&](long long x0, int& so, long long& oo) {
+    const long long xh = x0 / U;
+    int lo = 0, hi = B;  // invariant: seq_prefix[lo] <= xh < seq_prefix[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seq_prefix[mid] <= xh) lo = mid;
+      else hi = mid;
+    }
+    so = lo;
+    oo = x0 - (long long)seq_prefix[lo] * U;
+  };
+  int par = 0;  // LDS slot of the next claim
+  // The next chunk to claim: range after range, each claim made when the range before begins.
+  auto claim = [&]() -> long long {
+    __syncthreads();  // publishes sh_claim[par], written when the range before began
+    const unsigned d = sh_claim[par];
+    par ^= 1;
+    if ((long long)d >= plan.nd) return -1;
+    if (threadIdx.x == 0) sh_claim[par] = atomicAdd(p.counter, 1u);
+    return (long long)d;
+  };
+  long long w = v;
+  if (tail && threadIdx.x == 0) sh_claim[0] = atomicAdd(p.counter, 1u);
+  if (x >= x1 || s < 0 || s >= B) {  // no static range: start with the first claimed chunk
+    if (!tail) return;
+    const long long d = claim();
+    if (d < 0) return;
+    w = plan.ns + d;
+    x = plan.start(w);
+    x1 = plan.start(w + 1);
+    locate(x, s, off);
+  }
   int n_s = steps_of(p, s);
   if (n_s == 0) return;  // unreachable: every step lies in a sequence with steps
   const int lane = threadIdx.x & 63;
@@ -875,8 +917,10 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
   bool in_a = true;  // the current piece's first step is in ra
   while (true) {
     const int take = (int)min((long long)(n_s - j), x1 - x);
-    // The next piece of this worker: the next unit with steps, if the range goes on.
-    int s2 = s, hu2 = hu, n2 = n_s;
+    // The next piece of this worker: the next unit with steps, if the range goes on, else (with
+    // the dynamic tail) the first piece of the next claimed chunk.
+    int s2 = s, hu2 = hu, n2 = n_s, j2 = 0;
+    long long w2 = w, x2 = x + take, x1n = x1;
     bool more = x + take < x1;
     if (more && ++hu2 == U) {
       hu2 = 0;
@@ -886,13 +930,28 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
       } while (s2 < B && n2 == 0);
       more = s2 < B;
     }
+    if (!more && tail) {
+      const long long d = claim();
+      if (d >= 0) {
+        w2 = plan.ns + d;
+        x2 = plan.start(w2);
+        x1n = plan.start(w2 + 1);
+        long long off2;
+        locate(x2, s2, off2);
+        n2 = steps_of(p, s2);
+        hu2 = (int)(off2 / n2);
+        j2 = (int)(off2 % n2);
+        more = true;
+      }
+    }
     if (!more) {  // nothing follows: the "next" source is this piece (its loads hit in cache)
       s2 = s;
       hu2 = hu;
       n2 = n_s;
+      j2 = j;
     }
     const int h2 = head_of(hu2);
-    MPieceSrc ns = src_of(s2, h2, 0);
+    MPieceSrc ns = src_of(s2, h2, j2);
     uint4 qn[D / kSlice];
     load_qb<D, G>(qn, p, s2, h2);
 
@@ -900,7 +959,7 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
     const int L = uniform(clamped_len(p, s));
     const int u = s * p.num_kv_heads + h;
     const bool whole = (j == 0) && (take == n_s);
-    if (j == 0 && lane == 0) p.unit_info[u] = make_int2((int)v, (int)plan.owner(x + n_s - 1, jn));
+    if (j == 0 && lane == 0) p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1, jn));
     const int tok_end = min(L, (j + take) * kSub);
     const int iend = j + take, ilast = iend - 1;
     MState<D> st;
@@ -928,10 +987,10 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
         id = __builtin_amdgcn_readlane(cs.ids, b - cs.win);
         hoff = cs.head_off;
         tin = (size_t)(t0 & (bs - 1)) * D;
-      } else {
+      } else {  // the next piece's first step, at the start of its block-id window
         id = __builtin_amdgcn_readlane(ns.ids, 0);
         hoff = ns.head_off;
-        tin = 0;
+        tin = (size_t)((j2 * kSub) & (bs - 1)) * D;
       }
       issue(r, (size_t)id * block_elems + hoff + tin);
     };
@@ -950,16 +1009,18 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
       }
     };
     const bool swap = in_a ? walk(ra, rb) : walk(rb, ra);
-    finish_mpiece<D, G>(p, st, s, h, u, v, whole, nullptr);
+    finish_mpiece<D, G>(p, st, s, h, u, w, whole, nullptr);
     if (!more) break;
     in_a = swap ? !in_a : in_a;
-    x += take;
+    x = x2;
+    x1 = x1n;
+    w = w2;
     ++jn;
     s = s2;
     hu = hu2;
     n_s = n2;
     h = h2;
-    j = 0;
+    j = j2;
     cs = ns;
 #pragma unroll
     for (int sl = 0; sl < D / kSlice; ++sl) qb[sl] = qn[sl];
@@ -1099,6 +1160,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ long long sh_start_x[kWaves + 1];
   __shared__ __attribute__((aligned(16))) uint16_t p_lds[kWaves][2][G][8];
   __shared__ unsigned sh_chunk;
+  __shared__ unsigned sh_claim[2];  // dynamic-tail claims, in turn
   __shared__ float coop_st[kWaves][G * (2 + D)];  // per-wave (m, l, acc) of a shared piece
   extern __shared__ int seq_prefix[];  // [B+1] steps per KV head before each sequence (dynamic mode)
 
@@ -1155,7 +1217,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // statically the plan (piece cost included) does not depend on the workspace's chunk slots.
   const bool dynamic =
       !quad && p.dyn_cap > 0 && p.static_frac_q10 < 1024 && plan.ns == p.num_workers;
-  if (dynamic) {
+  // Dynamic tail of the head-quad split: chunk d is worker ns + d, whose partial slots
+  // (ns + d + u/kWaves)*kWaves + u%kWaves stay inside the workspace for d < dyn_cap/kWaves.
+  const bool tail = Mfma && Depth <= 1 && quad && p.tail_q10 > 0 && p.dyn_cap > 0;
+  if (tail) {
+    plan.S = max(plan.ns, plan.T - plan.T * p.tail_q10 / 1024);
+    const long long rest = plan.T - plan.S;
+    const long long cap = p.dyn_cap / kWaves;
+    plan.C = max((long long)max(p.tail_chunk, 1), (rest + cap - 1) / cap);
+    plan.nd = (rest + plan.C - 1) / plan.C;
+  } else if (dynamic) {
     plan.S = max(plan.ns, plan.T * p.static_frac_q10 / 1024);
     const long long rest = plan.T - plan.S;
     plan.C = max((long long)p.chunk_steps, (rest + p.dyn_cap - 1) / p.dyn_cap);
@@ -1167,7 +1238,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
   // Piece cost, kept below half a worker's share of steps so that no static worker's cost range
   // falls inside one piece's overhead (every static worker gets at least one step).
-  plan.A = dynamic ? 0 : min((long long)p.piece_cost, plan.T / plan.ns / 2);
+  plan.A = (dynamic || tail) ? 0 : min((long long)p.piece_cost, plan.T / plan.ns / 2);
   plan.CT = plan.S + plan.A * seqs_nonempty * U;
   const long long wbase = (long long)blockIdx.x * kWaves;
   // Workers whose starts this block needs: its own (1 with quads, else kWaves) and the next one.
@@ -1204,7 +1275,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       ne_chunk += sh_scan_ne[k];
     }
     const long long excl = base + before + incl - n;
-    if (dynamic && s < B) seq_prefix[s] = (int)excl;
+    if ((dynamic || tail) && s < B) seq_prefix[s] = (int)excl;
     if (n > 0) {
       // The sequence's U units cover cost positions [c_lo, c_lo + U*(n + A)).
       const long long lo = excl * U;
@@ -1229,7 +1300,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     ne_base += ne_chunk;
     __syncthreads();
   }
-  if (dynamic && threadIdx.x == 0) seq_prefix[B] = (int)base;
+  if ((dynamic || tail) && threadIdx.x == 0) seq_prefix[B] = (int)base;
   __syncthreads();
 
   const long long w = quad ? (long long)blockIdx.x : wbase + wave;
@@ -1237,6 +1308,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   auto body = [&](auto stream) {
     constexpr bool S = decltype(stream)::value;
     const int k = quad ? 0 : wave;
+    if constexpr (Mfma && Depth <= 1) {
+      if (tail) {  // every workgroup: its static range (possibly empty), then claimed chunks
+        const bool own = w < plan.ns;
+        run_worker_mfma<D, G, S, Fp8>(p, plan, w, own ? sh_start_s[k] : -1,
+                                      sh_start_off[k], sh_start_j[k],
+                                      own ? sh_start_x[k] : plan.S,
+                                      own ? sh_start_x[k + 1] : plan.S, quad, true, seq_prefix,
+                                      sh_claim);
+        return;
+      }
+    }
     if (w < plan.ns)
       run_worker<D, G, Depth, S, Fp8, Mfma>(p, plan, w, sh_start_s[k], sh_start_off[k],
                                             sh_start_j[k], sh_start_x[k], sh_start_x[k + 1],
@@ -1394,8 +1476,10 @@ hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
   {
     TraceScope t("decode_partition", stream);
     const dim3 grid(p.num_workers / kWaves), block(kThreads);
-    const size_t lds =
-        (p.dyn_cap > 0 && p.static_frac_q10 < 1024) ? (size_t)(p.num_seqs + 1) * 4 : 0;
+    // The per-sequence prefix of the dynamic chunks (either kind).
+    const size_t lds = (p.dyn_cap > 0 && (p.static_frac_q10 < 1024 || p.tail_q10 > 0))
+                           ? (size_t)(p.num_seqs + 1) * 4
+                           : 0;
     switch (variant(p.kv_fp8 != 0)) {
       case Variant::kFp8Depth1:
         hipLaunchKernelGGL((decode_kernel<D, G, 1, true>), grid, block, lds, stream, p);

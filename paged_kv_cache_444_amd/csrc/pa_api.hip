@@ -141,7 +141,8 @@ constexpr TunableDef kTunableDefs[pa::kNumTunables] = {
     {"PA_DECODE_MFMA", 1, 0, 1},        {"PA_DECODE_QUAD", 1, 0, 1},
     {"PA_DECODE_PIECE_COST", 6, 0, 64}, {"PA_DECODE_WORKERS", 0, 0, 1 << 20},
     {"PA_DECODE_STATIC_Q10", 1024, 512, 1024}, {"PA_DECODE_CHUNK", 4, 1, 256},
-    {"PA_PREFILL_SPLITS", 0, 0, 16},
+    {"PA_PREFILL_SPLITS", 0, 0, 16},    {"PA_DECODE_TAIL_Q10", 0, 0, 512},
+    {"PA_DECODE_TAIL_Q10_FP8", 0, 0, 512}, {"PA_DECODE_TAIL_CHUNK", 12, 1, 256},
 };
 
 std::atomic<int>* tunable_values() {
@@ -426,6 +427,12 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
   p.quad = p.static_frac_q10 == 1024 && num_kv_heads % 4 == 0 &&
            pa::tunable(pa::kTuneDecodeQuad) != 0;
   p.piece_cost = pa::tunable(pa::kTuneDecodePieceCost);
+  // The dynamic tail needs the workspace's chunk counter, so the fixed-scratch entry point (which
+  // leaves nothing in its scratch to start at zero) keeps the static split.
+  p.tail_q10 = (p.quad && !static_layout)
+                   ? pa::tunable(fp8 ? pa::kTuneDecodeTailQ10Fp8 : pa::kTuneDecodeTailQ10)
+                   : 0;
+  p.tail_chunk = pa::tunable(pa::kTuneDecodeTailChunk);
   p.len_cap = max_seq_len;
   // FP8: the K scale joins the softmax scale and the V scale multiplies the outputs.
   p.scale_log2 = (fp8 ? scale * k_scale : scale) * 1.4426950408889634f;

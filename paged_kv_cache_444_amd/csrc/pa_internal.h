@@ -20,6 +20,9 @@ enum Tunable {
   kTuneDecodeStaticQ10,    // PA_DECODE_STATIC_Q10: share of steps split statically (512-1024)
   kTuneDecodeChunk,        // PA_DECODE_CHUNK: smallest dynamic chunk, in steps (1-256)
   kTunePrefillSplits,      // PA_PREFILL_SPLITS: forced context split of a prefill (0: automatic)
+  kTuneDecodeTailQ10,      // PA_DECODE_TAIL_Q10: share of head-quad steps left to the dynamic tail
+  kTuneDecodeTailQ10Fp8,   // PA_DECODE_TAIL_Q10_FP8: the same for FP8 pools
+  kTuneDecodeTailChunk,    // PA_DECODE_TAIL_CHUNK: steps per dynamic tail chunk (1-256)
   kNumTunables
 };
 int tunable(Tunable t);
@@ -52,6 +55,10 @@ struct DecodeParams {
   // Cost of starting a piece, in steps: the static split balances steps plus this much per unit
   // a worker starts, since each piece begins with dependent loads that nothing overlaps.
   int piece_cost;
+  // Dynamic tail of the head-quad split (matrix-core steps): the last tail_q10/1024 of the steps
+  // are cut into chunks of about tail_chunk steps that workgroups claim from `counter` once their
+  // static range is done, so workgroups served faster take more.  0: static split only.
+  int tail_q10, tail_chunk;
   // Lengths are clamped to this (min of max_seq_len and the table width) so a length beyond the
   // caller's bound cannot take a kernel outside the table.
   int len_cap;

@@ -295,6 +295,51 @@ def test_decode_piece_cost_split(quad, piece_cost, workers, tune):
                  f"decode with piece cost {piece_cost}")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("tail_q10,chunk", [(0, 12), (160, 12), (512, 1), (300, 64), (160, 3),
+                                            (512, 256)])
+def test_decode_dynamic_tail(tail_q10, chunk, fp8, tune):
+    """The head-quad split with its last steps handed out as claimed chunks: whichever
+    workgroup takes a chunk, the result must be the same bit for bit on every call (fixed partial
+    slots, merged in chunk order) and match the oracle; many short, empty and long sequences."""
+    lens = np.random.default_rng((444, 91)).integers(0, 3000, size=40).tolist()
+    lens[3] = lens[17] = 0
+    lens[5] = 1
+    case = build_case(Spec(name="tail", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=16, seed=(444, 92, tail_q10, chunk), decode_lens=lens))
+    d = case.decode
+    tune("PA_DECODE_TAIL_Q10_FP8" if fp8 else "PA_DECODE_TAIL_Q10", tail_q10)
+    tune("PA_DECODE_TAIL_CHUNK", chunk)
+    say(f"decode dynamic tail {tail_q10}/1024, chunk {chunk}, fp8 {fp8}")
+    if fp8:
+        from helpers import dev_u8, oracle_quantize_pool
+
+        kc8 = oracle_quantize_pool(case.key_cache, 0.02)
+        vc8 = oracle_quantize_pool(case.value_cache, 0.03)
+        gk, gv = dev_u8(kc8), dev_u8(vc8)
+
+        def run():
+            out = pa.decode_fp8(dev_u16(d.query), gk, gv, dev_i32(d.block_tables),
+                                dev_i32(d.seq_lens), num_kv_heads=8, block_size=16, k_scale=0.02,
+                                v_scale=0.03, scale=float(case.scale), max_seq_len=d.max_seq_len)
+            torch.cuda.synchronize()
+            return host_u16(out)
+
+        ref = oracle.decode_fp8(d.query, kc8, vc8, d.block_tables, d.seq_lens, 8, 128, 16,
+                                case.scale, 0.02, 0.03)
+    else:
+        kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+
+        def run():
+            return gpu_decode(case, kc, vc)
+
+        ref = oracle_decode(case, case.key_cache, case.value_cache)
+    a = run()
+    for _ in range(3):
+        assert np.array_equal(a, run()), "the dynamic tail changed the result between calls"
+    assert_close(upcast(a), ref, f"decode with a dynamic tail of {tail_q10}/1024")
+
+
 def test_decode_workspace_sizes_on_device():
     n = pa.decode_workspace_bytes(128, 64, 8, 128, 8192)
     assert n >= 128 * 8 * 8 * (128 + 2) * 4  # at least one partial slot per unit

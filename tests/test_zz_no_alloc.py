@@ -1,9 +1,10 @@
 """pa_decode_no_alloc, the decode entry point that allocates nothing (its scratch is the library's
 fixed per-device array), against pa_decode, the entry point that takes a caller workspace.
 
-Both run the same kernels with the same static split, so their outputs must be equal bit for bit,
-and both must match the fp64 oracle within |gpu - oracle| <= 1e-2 + 1e-2*|oracle|.  Two calls in a
-row share the one array: the second, smaller batch must not see anything the first left there.
+Both run the same kernels, and with pa_decode's dynamic tail off they make the same static split,
+so their outputs must be equal bit for bit; both must match the fp64 oracle within
+|gpu - oracle| <= 1e-2 + 1e-2*|oracle|.  Two calls in a row share the one array: the second,
+smaller batch must not see anything the first left there.
 """
 
 import ctypes
@@ -45,9 +46,11 @@ def _no_alloc_abi(case, kc, vc, q, bt, sl, d, out):
 
 
 def _workspace_decode(case, kc, vc, q, bt, sl, d):
-    return pa.decode(q, kc, vc, bt, sl, num_kv_heads=case.num_kv_heads,
-                     block_size=case.block_size, scale=float(case.scale),
-                     max_seq_len=int(d.max_seq_len))
+    # pa_decode with the static split only (no dynamic tail), the split pa_decode_no_alloc makes
+    with pa.tunables(PA_DECODE_TAIL_Q10=0):
+        return pa.decode(q, kc, vc, bt, sl, num_kv_heads=case.num_kv_heads,
+                         block_size=case.block_size, scale=float(case.scale),
+                         max_seq_len=int(d.max_seq_len))
 
 
 def test_no_alloc_equals_workspace_decode_on_two_calls():

@@ -743,7 +743,7 @@ def run_prefix_shared(args):
 
     us_plain, us_cascade = timed(plain), timed(cascade)
     us_plain2, us_cascade2 = timed(plain), timed(cascade)
-    names = ("prefill_chunk", "decode_partition", "decode_merge", "prefill_merge")
+    names = ("prefill_chunk", "decode_partition", "cascade_merge")
     pa.trace_enable(True)
     for n in names:
         pa.trace_read(n)

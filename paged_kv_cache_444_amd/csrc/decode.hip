@@ -1356,12 +1356,40 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   else body(std::true_type{});
 }
 
+// Merge thread layout: thread t owns chunks c = t + 256*k of four consecutive head-dim values,
+// row (4c)/D of the unit's G query heads, so each source of a chunk is one (m, l) pair and one
+// 16-byte acc load.  A partial slot holds G*(2+D) floats, so with G odd a slot's acc is only
+// 8-byte aligned: the acc loads assume 4-byte alignment.
+typedef float f32x4u_t __attribute__((ext_vector_type(4), aligned(4)));
+
+template <int D, int G>
+struct MergeLayout {
+  static constexpr int kChunks = G * D / 4;
+  static constexpr int kPer = (kChunks + 255) / 256;  // chunks per thread
+  // Chunk k of this thread, clamped to the last so every thread's loads stay inside the unit.
+  __device__ static int chunk(int k) { return min((int)threadIdx.x + 256 * k, kChunks - 1); }
+  __device__ static bool owns(int k) { return (int)threadIdx.x + 256 * k < kChunks; }
+};
+
+// Fold one (m, l, acc) source into a running state, in the log2 domain; an empty source (m =
+// -inf) changes nothing.
+__device__ __forceinline__ void merge_fold(float& M, float& lt, f32x4_t& a, float mv, float lv,
+                                           f32x4_t av) {
+  if (mv == kNegInf) return;
+  const float mn = fmaxf(M, mv);
+  const float c_old = fast_exp2(M - mn);  // M = -inf on the first source: c_old = 0
+  const float c_new = fast_exp2(mv - mn);
+  lt = lt * c_old + lv * c_new;
+  a = a * c_old + av * c_new;
+  M = mn;
+}
+
 // Combine the pieces of every unit that spans several waves; write zeros for empty sequences.
-// One pass over the pieces with an online rescale; each thread owns up to four outputs, whose
-// loads for one piece are independent of each other.
+// One pass over the pieces with an online rescale, four pieces' loads issued together.
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-  constexpr int PER = (G * D + 255) / 256;
+  using L = MergeLayout<D, G>;
+  constexpr int PER = L::kPer;
   const int u = blockIdx.x;
   const int s = u / p.num_kv_heads;
   const int h = u % p.num_kv_heads;
@@ -1387,57 +1415,130 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   info.x = max(info.x, 0);
   info.y = min(info.y, p.num_workers + p.dyn_cap - 1);
   if (info.x >= info.y) return;  // written by its only wave
-  float M[PER], lt[PER], a[PER];
+  float M[PER], lt[PER];
+  f32x4_t a[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     M[k] = kNegInf;
     lt[k] = 0.f;
-    a[k] = 0.f;
+    a[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  // Four pieces per round: their loads are issued together, then combined in worker order.
   constexpr int kRound = 4;
   for (int w0 = info.x; w0 <= info.y; w0 += kRound) {
-    float mv[kRound][PER], lv[kRound][PER], av[kRound][PER];
+    float mv[kRound][PER], lv[kRound][PER];
+    f32x4_t av[kRound][PER];
 #pragma unroll
     for (int r = 0; r < kRound; ++r) {
       const int w = min(w0 + r, info.y);
       const float* slot = p.partials + slot_of(p, w, u) * (G * (2 + D));
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
-        const int i = min(threadIdx.x + 256 * k, G * D - 1);
-        mv[r][k] = slot[i / D];
-        lv[r][k] = slot[G + i / D];
-        av[r][k] = slot[2 * G + i];
+        const int c = L::chunk(k);
+        mv[r][k] = slot[4 * c / D];
+        lv[r][k] = slot[G + 4 * c / D];
+        av[r][k] = *(const f32x4u_t*)(slot + 2 * G + 4 * c);
       }
     }
 #pragma unroll
     for (int r = 0; r < kRound; ++r) {
       if (w0 + r > info.y) break;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const float mn = fmaxf(M[k], mv[r][k]);
-        const float c_old = fast_exp2(M[k] - mn);  // M = -inf on the first piece: c_old = 0
-        const float c_new = fast_exp2(mv[r][k] - mn);
-        lt[k] = lt[k] * c_old + lv[r][k] * c_new;
-        a[k] = a[k] * c_old + av[r][k] * c_new;
-        M[k] = mn;
-      }
+      for (int k = 0; k < PER; ++k) merge_fold(M[k], lt[k], a[k], mv[r][k], lv[r][k], av[r][k]);
     }
   }
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int i = threadIdx.x + 256 * k;
-    if (i >= G * D) continue;
+    if (!L::owns(k)) continue;
+    const int c = L::chunk(k);
+    const f32x4_t o = a[k] * p.v_scale;
     if (p.state_ml) {
-      const size_t su = state_slot(p, row0 + i / D);
-      if (i % D == 0) {
+      const size_t su = state_slot(p, row0 + 4 * c / D);
+      if ((4 * c) % D == 0) {
         p.state_ml[2 * su] = M[k];
         p.state_ml[2 * su + 1] = lt[k];
       }
-      p.state_acc[su * D + i % D] = a[k] * p.v_scale;
+      *(f32x4_t*)(p.state_acc + su * D + (4 * c) % D) = o;
     } else {
-      orow[i] = to_bf16(a[k] * p.v_scale / lt[k]);
+      *(uint2*)(orow + 4 * c) = make_uint2(pack_bf16x2(o[0] / lt[k], o[1] / lt[k]),
+                                           pack_bf16x2(o[2] / lt[k], o[3] / lt[k]));
     }
+  }
+}
+
+// The final merge of a cascade call: every (sequence, query head) row combines the shared
+// prompt's states (splits 0 .. state_split-1 of the state workspace, in split order) with its
+// own tail, taken from the tail's pieces when several waves shared it, from the tail state the
+// decode kernel wrote when one wave took it whole, and left out when the row has no tail, then
+// writes the normalised output.
+template <int D, int G>
+__global__ __launch_bounds__(256) void cascade_merge_kernel(DecodeParams p) {
+  using L = MergeLayout<D, G>;
+  constexpr int PER = L::kPer;
+  const int u = blockIdx.x;
+  const int s = u / p.num_kv_heads;
+  const int h = u % p.num_kv_heads;
+  if (u == 0 && threadIdx.x == 0) *p.counter = 0u;  // ready for the next call
+  const size_t row0 = (size_t)s * p.num_q_heads + (size_t)h * G;
+  int2 info = p.unit_info[u];
+  info.x = max(info.x, 0);
+  info.y = min(info.y, p.num_workers + p.dyn_cap - 1);
+  const bool tail = clamped_len(p, s) > 0;
+  const bool pieces = tail && info.x < info.y;
+  // Sources in combination order: the workspace states (the prompt's splits, then the tail's
+  // when it was written whole), then the tail's pieces in worker order.
+  const int nstates = p.state_split + ((tail && !pieces) ? 1 : 0);
+  const int nsrc = nstates + (pieces ? info.y - info.x + 1 : 0);
+  float M[PER], lt[PER];
+  f32x4_t a[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    M[k] = kNegInf;
+    lt[k] = 0.f;
+    a[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // Eight sources per round: their loads are issued together, then folded in order.  The source
+  // of each load is picked by selecting its address, not by branching, so no wait for earlier
+  // loads separates them.  A piece's acc still lacks the V scale, which the workspace states
+  // carry.
+  constexpr int kRound = 8;
+  for (int q0 = 0; q0 < nsrc; q0 += kRound) {
+    float mv[kRound][PER], lv[kRound][PER], sc[kRound];
+    f32x4_t av[kRound][PER];
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const int q = min(q0 + r, nsrc - 1);
+      const bool is_state = q < nstates;  // block-uniform
+      const float* slot =
+          p.partials + slot_of(p, info.x + max(q - nstates, 0), u) * (G * (2 + D));
+      sc[r] = is_state ? 1.f : p.v_scale;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int c = L::chunk(k);
+        const size_t su = (row0 + 4 * c / D) * p.state_stride + q;
+        const float* pm = is_state ? p.state_ml + 2 * su : slot + 4 * c / D;
+        const float* pl = is_state ? p.state_ml + 2 * su + 1 : slot + G + 4 * c / D;
+        const float* pv = is_state ? p.state_acc + su * D + (4 * c) % D : slot + 2 * G + 4 * c;
+        mv[r][k] = *pm;
+        lv[r][k] = *pl;
+        av[r][k] = *(const f32x4u_t*)pv;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      if (q0 + r >= nsrc) break;
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        merge_fold(M[k], lt[k], a[k], mv[r][k], lv[r][k], av[r][k] * sc[r]);
+    }
+  }
+  uint16_t* orow = p.out + row0 * D;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (!L::owns(k)) continue;
+    const int c = L::chunk(k);
+    const float inv = lt[k] > 0.f ? 1.f / lt[k] : 0.f;
+    const f32x4_t o = a[k] * inv;
+    *(uint2*)(orow + 4 * c) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
   }
 }
 
@@ -1503,7 +1604,11 @@ hipError_t launch_dg(const DecodeParams& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  {
+  if (p.state_final) {
+    TraceScope t("cascade_merge", stream);
+    hipLaunchKernelGGL((cascade_merge_kernel<D, G>), dim3(p.num_seqs * p.num_kv_heads),
+                       dim3(256), 0, stream, p);
+  } else {
     TraceScope t("decode_merge", stream);
     hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(p.num_seqs * p.num_kv_heads), dim3(256),
                        0, stream, p);

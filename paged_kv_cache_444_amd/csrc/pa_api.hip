@@ -366,7 +366,8 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
                         size_t workspace_bytes, void* stream,
                         const int32_t* skip_lens = nullptr, float* state_ml = nullptr,
                         float* state_acc = nullptr, int state_stride = 0, int state_split = 0,
-                        bool validate_only = false, bool static_layout = false) {
+                        bool validate_only = false, bool static_layout = false,
+                        bool state_final = false) {
   if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (fp8 && !std::isfinite(scale * k_scale))
@@ -411,6 +412,7 @@ pa_status_t decode_impl(void* out, const void* query, const void* key_cache,
   p.state_acc = state_acc;
   p.state_stride = state_stride;
   p.state_split = state_split;
+  p.state_final = state_final;
   p.seq_lens = seq_lens;
   p.num_blocks = num_blocks;
   p.num_seqs = num_seqs;
@@ -671,15 +673,14 @@ pa_status_t cascade_impl(void* out, const void* query, const void* key_cache,
     return fail(PA_ERR_HIP, "internal: prompt split of %d keys", a.split_keys);
   hipError_t e = pa::launch_prefill(a, hs);
   if (e != hipSuccess) return hip_status(e, "decode_cascade (prompt)");
-  // 2. Each sequence's own tokens past its prompt, as decode with the prompt's blocks skipped;
-  //    the per-row state goes to the last split.
-  st = decode_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
-                   num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                   max_seq_len, scale, fp8, k_scale, v_scale, ws + c.dec_off,
-                   workspace_bytes - c.dec_off, stream, prefix_lens, ml, acc, S + 1, S);
-  if (st != PA_OK) return st;
-  // 3. Combine the prompt splits with the tail split of every row.
-  return hip_status(pa::launch_prefill_merge(a, hs), "decode_cascade (merge)");
+  // 2. Each sequence's own tokens past its prompt, as decode with the prompt's blocks skipped.
+  //    A tail taken whole by one wave leaves its state in the last split; the decode's merge
+  //    then combines the prompt splits with each row's tail and writes the output.
+  return decode_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, max_seq_len, scale, fp8, k_scale, v_scale,
+                     ws + c.dec_off, workspace_bytes - c.dec_off, stream, prefix_lens, ml, acc,
+                     S + 1, S, false, false, true);
 }
 
 }  // namespace

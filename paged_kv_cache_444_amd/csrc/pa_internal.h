@@ -73,10 +73,13 @@ struct DecodeParams {
   // head) row's final (m in the log2 domain, l) and unnormalised acc go to split state_split of
   // the prefill workspace layout (state_ml[2u], state_ml[2u+1], state_acc[u*D..],
   // u = row*state_stride + state_split) instead of the output.
+  // state_final nonzero: splits 0 .. state_split-1 of every row already hold states (the shared
+  // prompt's), and the merge combines them with this call's tail and writes the output, so no
+  // separate pass over the states is needed.
   const int32_t* skip_lens;
   float* state_ml;
   float* state_acc;
-  int state_stride, state_split;
+  int state_stride, state_split, state_final;
 };
 
 // Waves the decode kernel is launched with for this shape and pool type on the current device.

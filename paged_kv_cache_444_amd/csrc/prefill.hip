@@ -84,6 +84,7 @@ __device__ __forceinline__ float xor32_f32(float x) { return __shfl_xor(x, 32, 6
 #endif
 constexpr int kStages = PA_PREFILL_STAGES;
 constexpr int kMaxTableLds = 2048;  // block ids of one workgroup's key range
+constexpr unsigned kXcds = 8;       // accelerator dies (each with its own L2) of the GPU
 
 // s_waitcnt with vmcnt(n) and no wait on the other counters (gfx9 encoding).
 template <int N>
@@ -211,12 +212,27 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int s = blockIdx.z;
-  const int h = blockIdx.y / p.splits;
-  const int split = blockIdx.y % p.splits;
+  // Workgroups are handed to the XCDs in turn (linear id n to XCD n % 8), and each XCD has its own
+  // L2.  The query tiles of one (sequence, head, key range) read the same K/V tiles, so the
+  // linear id is remapped to give every XCD a contiguous run of logical ids: one XCD then holds
+  // all the query tiles of its (head, range) pairs and fetches their K/V from HBM once.
+  int bx, by, bz;
+  {
+    const unsigned nx = gridDim.x, ny = gridDim.y;
+    const unsigned n = nx * ny * gridDim.z;
+    const unsigned lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    const unsigned xcd = lin % kXcds, per = n / kXcds, extra = n % kXcds;
+    const unsigned logical = xcd * per + min(xcd, extra) + lin / kXcds;
+    bx = logical % nx;
+    by = (logical / nx) % ny;
+    bz = logical / (nx * ny);
+  }
+  const int s = bz;
+  const int h = by / p.splits;
+  const int split = by % p.splits;
   const int qs = p.query_start_loc[s];
   const int q_len = p.query_start_loc[s + 1] - qs;
-  const int q0 = blockIdx.x * TQ;
+  const int q0 = bx * TQ;
   if (q_len <= 0 || q0 >= q_len) return;  // block-uniform
   // With from_first_row the table row and length are those of the first query row, clamped into
   // the table (whose rows are then the total_q query rows) so a malformed query_start_loc cannot

@@ -671,6 +671,12 @@ pa_status_t cascade_impl(void* out, const void* query, const void* key_cache,
   a.v_scale = fp8 ? v_scale : 1.f;
   if (S > 1 && a.split_keys % 32)
     return fail(PA_ERR_HIP, "internal: prompt split of %d keys", a.split_keys);
+  // The tails' decode is checked before anything is launched.
+  st = decode_impl(out, query, key_cache, value_cache, num_blocks, block_tables, seq_lens,
+                   num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                   max_seq_len, scale, fp8, k_scale, v_scale, ws + c.dec_off,
+                   workspace_bytes - c.dec_off, stream, prefix_lens, ml, acc, S + 1, S, true);
+  if (st != PA_OK) return st;
   hipError_t e = pa::launch_prefill(a, hs);
   if (e != hipSuccess) return hip_status(e, "decode_cascade (prompt)");
   // 2. Each sequence's own tokens past its prompt, as decode with the prompt's blocks skipped.

@@ -64,6 +64,41 @@ def test_cascade_parity_prefix_shared_rollouts():
     assert_close(upcast(got), full_decode_oracle(5), "cascade decode cfg5")
 
 
+@pytest.mark.parametrize("side_stream", [False, True])
+def test_cascade_is_ordered_on_the_callers_stream(side_stream):
+    """The output is complete for the next operation on the caller's stream, with no device-wide
+    synchronisation in between (every kernel of the call, merge included, is ordered on that
+    stream).  Checked on the default stream and on a stream of its own, with the output poisoned
+    before each call."""
+    case = cached_named_case(5)
+    d = case.decode
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    r = case.reshape
+    pa.reshape_and_cache(dev_u16(r.key), dev_u16(r.value), kc, vc, dev_i64(r.slot_mapping),
+                         num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                         block_size=case.block_size)
+    gs = np.arange(0, 129, 16)
+    want = _cascade(case, kc, vc, gs, 4096)
+    pl = _prefix_lens(gs, 4096)
+    q, bt, sl = dev_u16(d.query), dev_i32(d.block_tables), dev_i32(d.seq_lens)
+    gsd, pld = dev_i32(gs.astype(np.int32)), dev_i32(pl)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream() if side_stream else torch.cuda.current_stream()
+    with torch.cuda.stream(stream):
+        out = torch.empty_like(q)
+        copies = []
+        for _ in range(3):
+            out.fill_(-1)  # bf16 0xBF80 everywhere: not an attention output here
+            pa.decode_cascade(q, kc, vc, bt, sl, gsd, pld, max_prefix_len=4096, max_group_size=16,
+                              num_kv_heads=case.num_kv_heads, block_size=case.block_size,
+                              scale=float(case.scale), max_seq_len=int(d.seq_lens.max()),
+                              out=out)
+            copies.append(out.clone())  # ordered after the call on the same stream
+    torch.cuda.synchronize()
+    for c in copies:
+        assert np.array_equal(host_u16(c), want), "output read on the caller's stream is incomplete"
+
+
 @pytest.mark.parametrize("Hq,Hkv,D,bs", [(8, 2, 64, 16), (16, 1, 64, 32), (64, 8, 128, 16),
                                          (16, 4, 256, 32), (4, 4, 128, 16)])
 def test_cascade_groups_tails_and_edges(Hq, Hkv, D, bs):

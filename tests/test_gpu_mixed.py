@@ -55,6 +55,44 @@ def test_overlapped_mixed_step_equals_serial_and_oracle():
     assert_close(upcast(serial_p), full_prefill_oracle(4), "prefill in the mixed step")
 
 
+@pytest.mark.parametrize("own_stream", [False, True])
+def test_mixed_step_outputs_are_ordered_on_the_callers_stream(own_stream):
+    """Both outputs are complete for the next operation on the caller's stream with no
+    device-wide synchronisation in between: the decode half's stream joins back before the call
+    returns.  The outputs are poisoned before each call; checked on the default stream and on a
+    stream of the caller's own."""
+    case = cached_named_case(4)
+    p, d, r = case.prefill, case.decode, case.reshape
+    Hkv, D, bs = case.num_kv_heads, case.head_dim, case.block_size
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    pa.reshape_and_cache(dev_u16(r.key), dev_u16(r.value), kc, vc, dev_i64(r.slot_mapping),
+                         num_kv_heads=Hkv, head_dim=D, block_size=bs)
+    pre = dict(query=dev_u16(p.query), key_cache=kc, value_cache=vc,
+               block_tables=dev_i32(p.block_tables), query_start_loc=dev_i32(p.query_start_loc),
+               seq_lens=dev_i32(p.seq_lens), num_kv_heads=Hkv, block_size=bs,
+               max_q_len=p.max_q_len, max_seq_len=p.max_seq_len, scale=float(case.scale))
+    dec = dict(query=dev_u16(d.query), key_cache=kc, value_cache=vc,
+               block_tables=dev_i32(d.block_tables), seq_lens=dev_i32(d.seq_lens),
+               num_kv_heads=Hkv, block_size=bs, scale=float(case.scale),
+               max_seq_len=d.max_seq_len)
+    serial_p = host_u16(pa.prefill_chunk(**pre))
+    serial_d = host_u16(pa.decode(**dec))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream() if own_stream else torch.cuda.current_stream()
+    with torch.cuda.stream(stream):
+        pre["out"], dec["out"] = torch.empty_like(pre["query"]), torch.empty_like(dec["query"])
+        copies = []
+        for _ in range(3):
+            pre["out"].fill_(-1)
+            dec["out"].fill_(-1)
+            pout, dout = pa.mixed_step(pre, dec)
+            copies.append((pout.clone(), dout.clone()))  # ordered after the call on `stream`
+    torch.cuda.synchronize()
+    for cp, cd in copies:
+        assert np.array_equal(host_u16(cp), serial_p), "prefill output incomplete on the stream"
+        assert np.array_equal(host_u16(cd), serial_d), "decode output incomplete on the stream"
+
+
 def test_overlapped_mixed_step_fp8_equals_serial_and_oracle():
     """The same mixed step over an FP8 cache quantised by the oracle (chunk tokens included)."""
     case = cached_named_case(4)

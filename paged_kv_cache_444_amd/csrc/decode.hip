@@ -822,13 +822,56 @@ struct MPieceSrc {
 // worker ns + d, with its own partial slots), each claimed one range ahead so that its first
 // loads can be started inside the range before.  The claims travel through two LDS slots in
 // turn; every wave of the workgroup makes the same decisions, so all reach the same barriers.
-template <int D, int G, bool Stream, bool Fp8>
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// bf16 matrix-core steps keep register loads: staged through LDS they measured about 0.7 us
+// slower at the 70B shape, where the bf16 walk is bound by HBM rather than by its loads in flight.
+constexpr bool kStageBf16 = false;
+// Matrix-core steps stage each step's K and V in LDS: the K tile and the V tile of one 16-token
+// sub-block of one KV head are each kSub * D contiguous elements of the pool, so a wave fetches
+// them with 16-byte direct global->LDS loads (1 KB per instruction) and then reads its operands
+// from LDS.  A step then takes D/32 (FP8) or D/16 (bf16) load instructions instead of 3*D/32
+// register loads of 4 to 16 bytes; the number of loads a wave keeps in flight, not their bytes,
+// was what bounded the step rate.
+template <int D, bool Fp8>
+constexpr int kStageBytes = 2 * kSub * D * (Fp8 ? 1 : 2);
+template <int D, bool Fp8>
+constexpr int kDmaPerStep = kStageBytes<D, Fp8> / 1024;
+
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at LDS byte address
+// m0 + 16*l (m0 wave-uniform).  Written as inline assembly so the compiler does not treat the
+// walk's LDS reads as dependent on it (it would wait for every such load before each read); the
+// walk waits for these loads itself.  The load has no register result.  It first waits for this
+// wave's LDS reads issued before it, so a slot is never refilled while its last reads are still
+// pending.
+template <bool Stream>
+__device__ __forceinline__ void lds_dma_16(const uint8_t* src, unsigned m0) {
+  if constexpr (Stream)
+    asm volatile(
+        "s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off nt"
+        :
+        : "v"(src), "s"(m0)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(src), "s"(m0)
+        : "memory", "m0");
+}
+
+template <int D, int G, int Dep, bool Stream, bool Fp8>
 __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Plan& plan,
                                                 long long v, int s, long long off, long long jn,
                                                 long long x, long long x1, bool quad,
-                                                bool tail = false,
+                                                lds_u8* stage, bool tail = false,
                                                 const int* seq_prefix = nullptr,
                                                 unsigned* sh_claim = nullptr) {
+  // Steps staged through LDS (FP8 pools always, bf16 pools with kStageBf16).
+  constexpr bool kStaged = Fp8 || kStageBf16;
   const int B = p.num_seqs;
   const int U = quad ? p.num_kv_heads / kWaves : p.num_kv_heads;
   // Sequence and step offset (within its U * n_s steps) of global step x0 of a dynamic chunk:
@@ -888,18 +931,35 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
     r.head_off = (size_t)hh * tile;
     return r;
   };
-  // K/V loads of one 16-token step at element offset `o` of the pools.
-  auto issue = [&](MStepRegs<D, Fp8>& r, size_t o) __attribute__((always_inline)) {
-    const int r16 = lane & 15, q4 = lane >> 4;
+  // K/V loads of one 16-token step at element offset `o` of the pools: into the registers `r`,
+  // or (FP8) into LDS stage slot `slot` of this wave.
+  constexpr int kEl = Fp8 ? 1 : 2;  // bytes per pool element
+  auto issue = [&](MStepRegs<D, Fp8>& r, int slot, size_t o) __attribute__((always_inline)) {
+    if constexpr (kStaged) {
+      const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.kpool) + o * kEl + 16 * lane;
+      const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.vpool) + o * kEl + 16 * lane;
+      const unsigned dst = __builtin_amdgcn_readfirstlane(
+          (unsigned)(uintptr_t)(stage + slot * kStageBytes<D, Fp8>));
 #pragma unroll
-    for (int sl = 0; sl < D / kSlice; ++sl)
-      r.k[sl] = load_elems<Stream, Fp8>(p.kpool, o + sl * (kSub * kSlice) + r16 * kSlice + 8 * q4);
+      for (int c = 0; c < kDmaPerStep<D, Fp8> / 2; ++c)
+        lds_dma_16<Stream>(kb + 1024 * c, dst + 1024 * c);
 #pragma unroll
-    for (int m = 0; m < D / kSub; ++m) {
-      const size_t e = o + (size_t)(kSub * m + r16) * kSub + 4 * q4;
-      if constexpr (Fp8) r.v[m] = load4<Stream>(reinterpret_cast<const uint8_t*>(p.vpool) + e);
-      else r.v[m] = load8_u16<Stream>(p.vpool + e);
+      for (int c = 0; c < kDmaPerStep<D, Fp8> / 2; ++c)
+        lds_dma_16<Stream>(vb + 1024 * c, dst + kSub * D * kEl + 1024 * c);
+      (void)r;
+    } else {
+      const int r16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+      for (int sl = 0; sl < D / kSlice; ++sl)
+        r.k[sl] = load_elems<Stream, Fp8>(p.kpool, o + sl * (kSub * kSlice) + r16 * kSlice + 8 * q4);
+#pragma unroll
+      for (int m = 0; m < D / kSub; ++m)
+        r.v[m] = load8_u16<Stream>(p.vpool + o + (size_t)(kSub * m + r16) * kSub + 4 * q4);
     }
+    // Staged: keep the compiler from moving the current step's products, which wait for their
+    // own loads, ahead of these, so the next step's loads leave as early as the source issues
+    // them.
+    if constexpr (kStaged) __builtin_amdgcn_sched_barrier(0);
   };
 
   int hu = (int)(off / n_s);
@@ -908,14 +968,24 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
   MPieceSrc cs = src_of(s, h, j);
   uint4 qb[D / kSlice];
   load_qb<D, G>(qb, p, s, h);
-  MStepRegs<D, Fp8> ra, rb;
+  // Dep + 1 register sets rotate over the steps; Dep steps' loads are in flight while one is
+  // computed.
+  static_assert(Dep == 1 || Dep == 2, "prefetch depth");
+  MStepRegs<D, Fp8> ra, rb, rc;
   {
-    const int b = (j * kSub) >> shift;  // inside the window just loaded
-    const int id = __builtin_amdgcn_readlane(cs.ids, b - cs.win);
-    issue(ra, (size_t)id * block_elems + cs.head_off + (size_t)((j * kSub) & (bs - 1)) * D);
+    // The first Dep steps of the first piece (a step past the unit repeats its last one: it is
+    // then computed fully masked, or not at all).
+    auto first = [&](MStepRegs<D, Fp8>& r, int slot, int jj) __attribute__((always_inline)) {
+      jj = min(jj, n_s - 1);
+      const int b = (jj * kSub) >> shift;  // inside the window just loaded (b - win <= 1)
+      const int id = __builtin_amdgcn_readlane(cs.ids, b - cs.win);
+      issue(r, slot, (size_t)id * block_elems + cs.head_off + (size_t)((jj * kSub) & (bs - 1)) * D);
+    };
+    first(ra, 0, j);
+    if constexpr (Dep == 2) first(rb, 1, j + 1);
   }
-  bool in_a = true;  // the current piece's first step is in ra
-  while (true) {
+  bool in_a = true;  // register steps: the current piece's first step is in ra
+  while (true) {  // each piece starts with its first Dep steps' loads in flight (ra, then rb)
     const int take = (int)min((long long)(n_s - j), x1 - x);
     // The next piece of this worker: the next unit with steps, if the range goes on, else (with
     // the dynamic tail) the first piece of the next claimed chunk.
@@ -962,6 +1032,9 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
     if (j == 0 && lane == 0) p.unit_info[u] = make_int2((int)w, (int)plan.owner(x + n_s - 1, jn));
     const int tok_end = min(L, (j + take) * kSub);
     const int iend = j + take, ilast = iend - 1;
+    // The staged walk covers a multiple of Dep + 1 steps; the ones past the piece are fully
+    // masked.  The register walk ends with the piece.
+    const int iwalk = kStaged ? j + (take + Dep) / (Dep + 1) * (Dep + 1) : iend;
     MState<D> st;
     st.m = kNegInf;
     st.nmc = 0.f;
@@ -969,11 +1042,11 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
     st.l = 0.f;
 #pragma unroll
     for (int m = 0; m < D / kSub; ++m) st.acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // Loads of step `step`: inside the piece, or past its end the next piece's first step (the
-    // last step again when nothing follows).  One load path for both, so the compiler's counter
-    // waits stay exact.
-    auto ld = [&](MStepRegs<D, Fp8>& r, int step) __attribute__((always_inline)) {
-      const bool here = step <= ilast || !more;  // wave-uniform
+    // Loads of step `step`: inside the piece (a masked step past its end repeats the last one),
+    // or, from iwalk on, the next piece's steps (the last step again when nothing follows).  One
+    // load path for all, so the compiler's counter waits stay exact.
+    auto ld = [&](MStepRegs<D, Fp8>& r, int slot, int step) __attribute__((always_inline)) {
+      const bool here = step < iwalk || !more;  // wave-uniform
       int id;
       size_t hoff, tin;
       if (here) {
@@ -987,31 +1060,93 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
         id = __builtin_amdgcn_readlane(cs.ids, b - cs.win);
         hoff = cs.head_off;
         tin = (size_t)(t0 & (bs - 1)) * D;
-      } else {  // the next piece's first step, at the start of its block-id window
-        id = __builtin_amdgcn_readlane(ns.ids, 0);
+      } else {  // the next piece's step j2 + (step - iwalk), at the start of its id window
+        const int jj = min(j2 + (step - iwalk), n2 - 1);
+        id = __builtin_amdgcn_readlane(ns.ids, ((jj * kSub) >> shift) - ns.win);
         hoff = ns.head_off;
-        tin = (size_t)((j2 * kSub) & (bs - 1)) * D;
+        tin = (size_t)((jj * kSub) & (bs - 1)) * D;
       }
-      issue(r, (size_t)id * block_elems + hoff + tin);
+      issue(r, slot, (size_t)id * block_elems + hoff + tin);
     };
-    // Steps alternate between two register sets; returns true when the last step was in
-    // `first` (the next piece's first step then sits in `second`).
-    auto walk = [&](MStepRegs<D, Fp8>& first, MStepRegs<D, Fp8>& second)
-                    __attribute__((always_inline)) {
-      int i = j;
-      while (true) {
-        ld(second, i + 1);
-        compute_mstep<D, Fp8>(first, qb, tok_end - i * kSub, c, slack_raw, st);
-        if (++i >= iend) return true;
-        ld(first, i + 1);
-        compute_mstep<D, Fp8>(second, qb, tok_end - i * kSub, c, slack_raw, st);
-        if (++i >= iend) return false;
+    // One step: from the registers `r`, or (FP8) from LDS slot `slot` once its loads, and so
+    // every older vector-memory operation, are done (the Dep later steps' loads may still fly).
+    auto cstep = [&](MStepRegs<D, Fp8>& r, int slot, int i) __attribute__((always_inline)) {
+      if constexpr (kStaged) {
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kDmaPerStep<D, Fp8> * Dep) : "memory");
+        const lds_u8* src = stage + slot * kStageBytes<D, Fp8>;
+        const int r16 = lane & 15, q4 = lane >> 4;
+        MStepRegs<D, Fp8> t;
+        // The same elements the register loads take: K slice sl, token r16, elements 8*q4 ..;
+        // V row 16m + r16, tokens 4*q4 .. .
+#pragma unroll
+        for (int sl = 0; sl < D / kSlice; ++sl) {
+          const lds_u8* a = src + (sl * (kSub * kSlice) + r16 * kSlice + 8 * q4) * kEl;
+          if constexpr (Fp8) {
+            const u32x2_t k = *(const __attribute__((address_space(3))) u32x2_t*)a;
+            t.k[sl] = make_uint2(k.x, k.y);
+          } else {
+            const u32x4_t k = *(const __attribute__((address_space(3))) u32x4_t*)a;
+            t.k[sl] = make_uint4(k.x, k.y, k.z, k.w);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < D / kSub; ++m) {
+          const lds_u8* a = src + (kSub * D + (kSub * m + r16) * kSub + 4 * q4) * kEl;
+          if constexpr (Fp8) {
+            t.v[m] = *(const __attribute__((address_space(3))) uint32_t*)a;
+          } else {
+            const u32x2_t v = *(const __attribute__((address_space(3))) u32x2_t*)a;
+            t.v[m] = make_uint2(v.x, v.y);
+          }
+        }
+        compute_mstep<D, Fp8>(t, qb, tok_end - i * kSub, c, slack_raw, st);
+        (void)r;
+      } else {
+        compute_mstep<D, Fp8>(r, qb, tok_end - i * kSub, c, slack_raw, st);
       }
     };
-    const bool swap = in_a ? walk(ra, rb) : walk(rb, ra);
+    if constexpr (kStaged) {
+      // Staged steps rotate through the LDS slots, Dep + 1 per iteration, each slot refilled Dep
+      // steps ahead as soon as it is free.  The walk is padded with fully masked steps (they add
+      // nothing) to whole rotations, so the next piece's first steps always land in slots 0
+      // (and 1), and the walk exists once in the compiled code.
+      for (int i = j; i < iwalk; i += Dep + 1) {
+        if constexpr (Dep == 1) {
+          ld(rb, 1, i + 1);
+          cstep(ra, 0, i);
+          ld(ra, 0, i + 2);
+          cstep(rb, 1, i + 1);
+        } else {
+          ld(rc, 2, i + 2);
+          cstep(ra, 0, i);
+          ld(ra, 0, i + 3);
+          cstep(rb, 1, i + 1);
+          ld(rb, 1, i + 4);
+          cstep(rc, 2, i + 2);
+        }
+      }
+    } else {
+      static_assert(kStaged || Dep == 1, "register steps prefetch one step");
+      // Register steps alternate between the two register sets; returns true when the last step
+      // was in `first` (the next piece's first step then sits in `second`).  Both orders are
+      // compiled, so no step past the piece is computed.
+      auto walk = [&](MStepRegs<D, Fp8>& first, MStepRegs<D, Fp8>& second)
+                      __attribute__((always_inline)) {
+        int i = j;
+        while (true) {
+          ld(second, 1, i + 1);
+          cstep(first, 0, i);
+          if (++i >= iend) return true;
+          ld(first, 0, i + 1);
+          cstep(second, 1, i);
+          if (++i >= iend) return false;
+        }
+      };
+      const bool swap = in_a ? walk(ra, rb) : walk(rb, ra);
+      in_a = swap ? !in_a : in_a;
+    }
     finish_mpiece<D, G>(p, st, s, h, u, w, whole, nullptr);
     if (!more) break;
-    in_a = swap ? !in_a : in_a;
     x = x2;
     x1 = x1n;
     w = w2;
@@ -1102,9 +1237,11 @@ template <int D, int G, int Depth, bool Stream, bool Fp8, bool Mfma, bool Coop =
 __device__ __forceinline__ void run_worker(const DecodeParams& p, const Plan& plan, long long v,
                                            int s, long long off, long long jn, long long x,
                                            long long x1, uint16_t (*p_sh)[G][8],
-                                           float (*st)[G * (2 + D)] = nullptr, bool quad = false) {
-  if constexpr (Mfma && !Coop && Depth <= 1) {
-    run_worker_mfma<D, G, Stream, Fp8>(p, plan, v, s, off, jn, x, x1, quad);
+                                           float (*st)[G * (2 + D)] = nullptr, bool quad = false,
+                                           lds_u8* stage = nullptr) {
+  if constexpr (Mfma && !Coop) {
+    run_worker_mfma<D, G, (Depth >= 2 ? 2 : 1), Stream, Fp8>(p, plan, v, s, off, jn, x, x1, quad,
+                                                             stage);
     return;
   }
   const int B = p.num_seqs;
@@ -1162,6 +1299,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ unsigned sh_chunk;
   __shared__ unsigned sh_claim[2];  // dynamic-tail claims, in turn
   __shared__ float coop_st[kWaves][G * (2 + D)];  // per-wave (m, l, acc) of a shared piece
+  // Per-wave ring of staged steps (FP8 matrix-core steps; a placeholder otherwise).
+  constexpr bool kStagedK = Mfma && (Fp8 || kStageBf16);
+  constexpr int kSlots = kStagedK ? (Depth >= 2 ? 3 : 2) : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t
+      stage_lds[kWaves][kSlots][kStagedK ? kStageBytes<D, Fp8> : 16];
   extern __shared__ int seq_prefix[];  // [B+1] steps per KV head before each sequence (dynamic mode)
 
   // Total steps of the batch.  The first kThreads sequences' step counts stay in a register for
@@ -1311,10 +1453,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     if constexpr (Mfma && Depth <= 1) {
       if (tail) {  // every workgroup: its static range (possibly empty), then claimed chunks
         const bool own = w < plan.ns;
-        run_worker_mfma<D, G, S, Fp8>(p, plan, w, own ? sh_start_s[k] : -1,
+        run_worker_mfma<D, G, 1, S, Fp8>(p, plan, w, own ? sh_start_s[k] : -1,
                                       sh_start_off[k], sh_start_j[k],
                                       own ? sh_start_x[k] : plan.S,
-                                      own ? sh_start_x[k + 1] : plan.S, quad, true, seq_prefix,
+                                      own ? sh_start_x[k + 1] : plan.S, quad,
+                                      (lds_u8*)&stage_lds[wave][0][0], true, seq_prefix,
                                       sh_claim);
         return;
       }
@@ -1322,7 +1465,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     if (w < plan.ns)
       run_worker<D, G, Depth, S, Fp8, Mfma>(p, plan, w, sh_start_s[k], sh_start_off[k],
                                             sh_start_j[k], sh_start_x[k], sh_start_x[k + 1],
-                                            p_lds[wave], nullptr, quad);
+                                            p_lds[wave], nullptr, quad,
+                                            (lds_u8*)&stage_lds[wave][0][0]);
     if (!dynamic) return;  // block-uniform
 
     // Dynamic chunks, each shared by the whole workgroup (one counter increment per chunk; the

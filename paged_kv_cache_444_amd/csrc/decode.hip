@@ -88,13 +88,17 @@ __device__ __forceinline__ int steps_of(const DecodeParams& p, int s) {
   return (clamped_len(p, s) + kSub - 1) / kSub;
 }
 
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves: shifts by 1, 2, 4 and 8 within
+// each 16-lane row (lanes without a source read 0), then row 0's and row 2's totals broadcast
+// into rows 1 and 3, then lane 31's prefix into rows 2 and 3.  Six dependent adds, where the
+// shuffle form took six LDS permutes.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
   return x;
 }
 
@@ -109,15 +113,25 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 // step x of the batch's j-th non-empty unit costs position x + A*(j+1) on a line of length
 // CT = S + A * (non-empty units).  Worker v starts at the first step whose cost position reaches
 // v*CT/ns; A = 0 gives the even split of steps.  Dynamic chunks keep A = 0.
+// floor(n / d) for 0 <= n < 2^53 and d > 0.  The correctly rounded double quotient is at most one
+// above the exact floor (rounding is monotone and every integer below 2^53 is a double), so one
+// exact integer check finishes it.  It replaces the long 64-bit integer division sequence on the
+// partition's critical path at the start of every launch.
+__device__ __forceinline__ long long div_nonneg(long long n, long long d) {
+  long long q = (long long)((double)n / (double)d);
+  if (q * d > n) --q;
+  return q;
+}
+
 struct Plan {
   long long T, S, ns, C, nd, A, CT;
   __device__ long long start(long long v) const {  // A = 0 only
-    return v <= ns ? v * S / ns : min(T, S + (v - ns) * C);
+    return v <= ns ? div_nonneg(v * S, ns) : min(T, S + (v - ns) * C);
   }
-  __device__ long long target(long long v) const { return v * CT / ns; }
+  __device__ long long target(long long v) const { return div_nonneg(v * CT, ns); }
   // Worker holding step x, which lies in non-empty unit j.
   __device__ long long owner(long long x, long long j) const {
-    return x < S ? ((x + A * (j + 1) + 1) * ns - 1) / CT : ns + (x - S) / C;
+    return x < S ? div_nonneg((x + A * (j + 1) + 1) * ns - 1, CT) : ns + div_nonneg(x - S, C);
   }
 };
 
@@ -962,8 +976,8 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
     if constexpr (kStaged) __builtin_amdgcn_sched_barrier(0);
   };
 
-  int hu = (int)(off / n_s);
-  int j = (int)(off % n_s);
+  int hu = (int)div_nonneg(off, n_s);
+  int j = (int)(off - (long long)hu * n_s);
   int h = head_of(hu);
   MPieceSrc cs = src_of(s, h, j);
   uint4 qb[D / kSlice];
@@ -1009,8 +1023,8 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
         long long off2;
         locate(x2, s2, off2);
         n2 = steps_of(p, s2);
-        hu2 = (int)(off2 / n2);
-        j2 = (int)(off2 % n2);
+        hu2 = (int)div_nonneg(off2, n2);
+        j2 = (int)(off2 - (long long)hu2 * n2);
         more = true;
       }
     }
@@ -1380,7 +1394,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
   // Piece cost, kept below half a worker's share of steps so that no static worker's cost range
   // falls inside one piece's overhead (every static worker gets at least one step).
-  plan.A = (dynamic || tail) ? 0 : min((long long)p.piece_cost, plan.T / plan.ns / 2);
+  plan.A = (dynamic || tail) ? 0 : min((long long)p.piece_cost, div_nonneg(plan.T, plan.ns) / 2);
   plan.CT = plan.S + plan.A * seqs_nonempty * U;
   const long long wbase = (long long)blockIdx.x * kWaves;
   // Workers whose starts this block needs: its own (1 with quads, else kWaves) and the next one.
@@ -1429,7 +1443,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         if (wk >= plan.ns) break;
         const long long t = plan.target(wk);
         if (t >= c_lo && t < c_lo + U * per_unit) {
-          const long long kk = (t - c_lo) / per_unit;
+          const long long kk = div_nonneg(t - c_lo, per_unit);
           const long long o = max(0LL, t - c_lo - kk * per_unit - plan.A);
           sh_start_s[k] = s;
           sh_start_off[k] = kk * n + o;
@@ -1440,10 +1454,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     base += chunk;
     ne_base += ne_chunk;
-    __syncthreads();
+    if (c + kThreads < B) __syncthreads();  // the next chunk rewrites sh_scan
   }
   if ((dynamic || tail) && threadIdx.x == 0) seq_prefix[B] = (int)base;
-  __syncthreads();
+  __syncthreads();  // publishes sh_start_* and seq_prefix
 
   const long long w = quad ? (long long)blockIdx.x : wbase + wave;
   // One instantiation of the worker per load kind (the choice is uniform over the grid).

@@ -1124,19 +1124,22 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
       // steps ahead as soon as it is free.  The walk is padded with fully masked steps (they add
       // nothing) to whole rotations, so the next piece's first steps always land in slots 0
       // (and 1), and the walk exists once in the compiled code.
+      // A step past the piece only keeps the loads regular (each wait counts a fixed number of
+      // loads per step); its product is skipped.  The compiler does not track the staged loads,
+      // so the branch costs no extra counter waits.
       for (int i = j; i < iwalk; i += Dep + 1) {
         if constexpr (Dep == 1) {
           ld(rb, 1, i + 1);
           cstep(ra, 0, i);
           ld(ra, 0, i + 2);
-          cstep(rb, 1, i + 1);
+          if (i + 1 < iend) cstep(rb, 1, i + 1);
         } else {
           ld(rc, 2, i + 2);
           cstep(ra, 0, i);
           ld(ra, 0, i + 3);
-          cstep(rb, 1, i + 1);
+          if (i + 1 < iend) cstep(rb, 1, i + 1);
           ld(rb, 1, i + 4);
-          cstep(rc, 2, i + 2);
+          if (i + 2 < iend) cstep(rc, 2, i + 2);
         }
       }
     } else {
@@ -1341,10 +1344,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       shares |= p.block_tables[(size_t)s * row + a] == p.block_tables[(size_t)(s + 1) * row + b];
   }
   shares = __any(shares);
+  // Wave totals.  When every per-head step count of the batch fits an int (it does unless the
+  // batch holds 2^35 tokens per head), the DPP scan's last lane gives them; otherwise 64-bit
+  // shuffles do.
+  nonempty = __builtin_amdgcn_readlane(wave_inclusive_scan(nonempty), 63);
+  if ((long long)B * ((p.len_cap + kSub - 1) / kSub) < (1LL << 31)) {
+    mine = __builtin_amdgcn_readlane(wave_inclusive_scan((int)mine), 63);
+  } else {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mine += __shfl_xor(mine, o, 64);
-    nonempty += __shfl_xor(nonempty, o, 64);
+    for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
   }
   if (lane == 0) {
     sh_sum[wave] = mine;

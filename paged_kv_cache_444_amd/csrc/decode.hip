@@ -833,15 +833,20 @@ struct MPieceSrc {
 //
 // Dynamic tail (quad workers, `tail` set): after its static range the workgroup takes the chunks
 // [S + d*C, S + (d+1)*C) of the step line in claim order (d from the workspace counter; chunk d is
-// worker ns + d, with its own partial slots), each claimed one range ahead so that its first
-// loads can be started inside the range before.  The claims travel through two LDS slots in
-// turn; every wave of the workgroup makes the same decisions, so all reach the same barriers.
+// worker ns + d, with its own partial slots).  Each claim is made inside the walk of the range's
+// last piece, kClaimLead steps before its end: late enough that the workgroups which run ahead
+// take the chunks, early enough that the chunk's block ids, query and first step are loading while
+// the piece finishes.  The claims travel through two LDS slots in turn; every wave of the
+// workgroup makes the same decisions, so all reach the same barriers.
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // bf16 matrix-core steps keep register loads: staged through LDS they measured about 0.7 us
 // slower at the 70B shape, where the bf16 walk is bound by HBM rather than by its loads in flight.
 constexpr bool kStageBf16 = false;
+// Steps before the end of a range's last piece at which the workgroup claims its next tail chunk
+// (2, 4 and 8 measured alike at the 70B shape).
+constexpr int kClaimLead = 2;
 // Matrix-core steps stage each step's K and V in LDS: the K tile and the V tile of one 16-token
 // sub-block of one KV head are each kSub * D contiguous elements of the pool, so a wave fetches
 // them with 16-byte direct global->LDS loads (1 KB per instruction) and then reads its operands
@@ -902,17 +907,17 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
     oo = x0 - (long long)seq_prefix[lo] * U;
   };
   int par = 0;  // LDS slot of the next claim
-  // The next chunk to claim: range after range, each claim made when the range before begins.
+  // Claims the next chunk (-1: none left).  One counter increment per workgroup, published in
+  // LDS; the slots alternate, so the barrier of the claim between two writes of one slot orders
+  // the later write after every wave's read of the earlier one.
   auto claim = [&]() -> long long {
-    __syncthreads();  // publishes sh_claim[par], written when the range before began
+    if (threadIdx.x == 0) sh_claim[par] = atomicAdd(p.counter, 1u);
+    __syncthreads();
     const unsigned d = sh_claim[par];
     par ^= 1;
-    if ((long long)d >= plan.nd) return -1;
-    if (threadIdx.x == 0) sh_claim[par] = atomicAdd(p.counter, 1u);
-    return (long long)d;
+    return ((long long)d < plan.nd) ? (long long)d : -1;
   };
   long long w = v;
-  if (tail && threadIdx.x == 0) sh_claim[0] = atomicAdd(p.counter, 1u);
   if (x >= x1 || s < 0 || s >= B) {  // no static range: start with the first claimed chunk
     if (!tail) return;
     const long long d = claim();
@@ -1014,30 +1019,37 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
       } while (s2 < B && n2 == 0);
       more = s2 < B;
     }
-    if (!more && tail) {
-      const long long d = claim();
-      if (d >= 0) {
-        w2 = plan.ns + d;
-        x2 = plan.start(w2);
-        x1n = plan.start(w2 + 1);
-        long long off2;
-        locate(x2, s2, off2);
-        n2 = steps_of(p, s2);
-        hu2 = (int)div_nonneg(off2, n2);
-        j2 = (int)(off2 - (long long)hu2 * n2);
-        more = true;
-      }
-    }
+    // The range ends with this piece: the next chunk is claimed inside its walk.
+    bool pend = !more && tail;
     if (!more) {  // nothing follows: the "next" source is this piece (its loads hit in cache)
       s2 = s;
       hu2 = hu;
       n2 = n_s;
       j2 = j;
     }
-    const int h2 = head_of(hu2);
+    int h2 = head_of(hu2);
     MPieceSrc ns = src_of(s2, h2, j2);
     uint4 qn[D / kSlice];
     load_qb<D, G>(qn, p, s2, h2);
+    // Claims the next chunk and makes it the next piece (its block-id window and query start
+    // loading); with none left the next source stays this piece.
+    auto resolve = [&]() __attribute__((always_inline)) {
+      pend = false;
+      const long long d = claim();
+      if (d < 0) return;
+      w2 = plan.ns + d;
+      x2 = plan.start(w2);
+      x1n = plan.start(w2 + 1);
+      long long off2;
+      locate(x2, s2, off2);
+      n2 = steps_of(p, s2);
+      hu2 = (int)div_nonneg(off2, n2);
+      j2 = (int)(off2 - (long long)hu2 * n2);
+      more = true;
+      h2 = head_of(hu2);
+      ns = src_of(s2, h2, j2);
+      load_qb<D, G>(qn, p, s2, h2);
+    };
 
     // This piece.
     const int L = uniform(clamped_len(p, s));
@@ -1049,6 +1061,9 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
     // The staged walk covers a multiple of Dep + 1 steps; the ones past the piece are fully
     // masked.  The register walk ends with the piece.
     const int iwalk = kStaged ? j + (take + Dep) / (Dep + 1) * (Dep + 1) : iend;
+    // The walk's first step at which a pending claim is made (the first loads past the walk need
+    // its answer).
+    const int icl = max(j, iwalk - max(kClaimLead, kStaged ? Dep + 1 : 1));
     MState<D> st;
     st.m = kNegInf;
     st.nmc = 0.f;
@@ -1128,6 +1143,7 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
       // loads per step); its product is skipped.  The compiler does not track the staged loads,
       // so the branch costs no extra counter waits.
       for (int i = j; i < iwalk; i += Dep + 1) {
+        if (pend && i >= icl) resolve();
         if constexpr (Dep == 1) {
           ld(rb, 1, i + 1);
           cstep(ra, 0, i);
@@ -1151,9 +1167,11 @@ __device__ __forceinline__ void run_worker_mfma(const DecodeParams& p, const Pla
                       __attribute__((always_inline)) {
         int i = j;
         while (true) {
+          if (pend && i >= icl) resolve();
           ld(second, 1, i + 1);
           cstep(first, 0, i);
           if (++i >= iend) return true;
+          if (pend && i >= icl) resolve();
           ld(first, 0, i + 1);
           cstep(second, 1, i);
           if (++i >= iend) return false;

@@ -340,6 +340,31 @@ def test_decode_dynamic_tail(tail_q10, chunk, fp8, tune):
     assert_close(upcast(a), ref, f"decode with a dynamic tail of {tail_q10}/1024")
 
 
+@pytest.mark.parametrize("tail_q10,chunk", [(64, 8), (160, 4)])
+def test_decode_dynamic_tail_named(tail_q10, chunk, tune):
+    """The dynamic tail at the 70B batch-128 shape (every CU's workgroup claims chunks near the end
+    of its static range): the same bits on every call and every sequence matching the oracle."""
+    case = cached_named_case(2)
+    tune("PA_DECODE_TAIL_Q10", tail_q10)
+    tune("PA_DECODE_TAIL_CHUNK", chunk)
+    say(f"decode dynamic tail {tail_q10}/1024, chunk {chunk}, 70B batch 128")
+    d = case.decode
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    q, bt, sl = dev_u16(d.query), dev_i32(d.block_tables), dev_i32(d.seq_lens)
+    ws = torch.zeros(pa.decode_workspace_bytes(d.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                               case.head_dim, d.max_seq_len),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        out = pa.decode(q, kc, vc, bt, sl, num_kv_heads=case.num_kv_heads, block_size=16,
+                        scale=float(case.scale), max_seq_len=d.max_seq_len, workspace=ws)
+        outs.append(host_u16(out))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0]), "the dynamic tail changed the result between calls"
+    assert_close(upcast(outs[0]), full_decode_oracle(2),
+                 f"decode with a dynamic tail of {tail_q10}/1024 at the 70B shape")
+
+
 def test_decode_workspace_sizes_on_device():
     n = pa.decode_workspace_bytes(128, 64, 8, 128, 8192)
     assert n >= 128 * 8 * 8 * (128 + 2) * 4  # at least one partial slot per unit

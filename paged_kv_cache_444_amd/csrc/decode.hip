@@ -305,7 +305,7 @@ __device__ __forceinline__ void compute_step(const StepRegs<D>& r, const uint4 (
   bool raise = false;
 #pragma unroll
   for (int j = 0; j < O; ++j) raise |= fmaxf(own[0][j], own[1][j]) > st.own_thr[j];
-  if (__ballot(raise)) {
+  if (__builtin_expect(__ballot(raise) != 0, 0)) {  // rare: kept out of line
     float alpha[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -632,7 +632,9 @@ __device__ __forceinline__ void compute_mstep(const MStepRegs<D, Fp8>& r,
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = (!tail || 4 * q4 + i < nvalid) ? sc[i] : kNegInf;
   const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  if (__ballot(mx > st.thr)) {
+  // Raising the maximum is rare: its code is kept out of line, so the step's common path has no
+  // taken branch.
+  if (__builtin_expect(__ballot(mx > st.thr) != 0, 0)) {
     float cm = fmaxf(mx, xor16_f32(mx));
     cm = fmaxf(cm, __shfl_xor(cm, 32, 64));  // the column's max over its 16 tokens
     const float mn = fmaxf(st.m, cm);

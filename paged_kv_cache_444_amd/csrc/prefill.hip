@@ -436,7 +436,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
         bool raise = false;
 #pragma unroll
         for (int i = 0; i < 8; ++i) raise |= x[i] > thr[rt];
-        if (__ballot(raise)) {
+        // The bf16 walk keeps the rare branch out of line (its common path then has no taken
+        // branch: 0.4 % faster); the FP8 walk measured slower that way.
+        const bool any_raise = __ballot(raise) != 0;
+        if (Fp8 ? any_raise : __builtin_expect(any_raise, 0)) {
           float mx = x[0];
 #pragma unroll
           for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);

@@ -1609,29 +1609,39 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     lt[k] = 0.f;
     a[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  constexpr int kRound = 4;
-  for (int w0 = info.x; w0 <= info.y; w0 += kRound) {
-    float mv[kRound][PER], lv[kRound][PER];
-    f32x4_t av[kRound][PER];
+  // Rounds of four pieces' loads, or eight when the unit has more than four pieces (units split
+  // over many waves, as with one KV head): a unit's pieces then arrive in one round trip.  The
+  // fold order is the same either way.
+  auto fold_all = [&](auto round_c) __attribute__((always_inline)) {
+    constexpr int kRound = decltype(round_c)::value;
+    for (int w0 = info.x; w0 <= info.y; w0 += kRound) {
+      float mv[kRound][PER], lv[kRound][PER];
+      f32x4_t av[kRound][PER];
 #pragma unroll
-    for (int r = 0; r < kRound; ++r) {
-      const int w = min(w0 + r, info.y);
-      const float* slot = p.partials + slot_of(p, w, u) * (G * (2 + D));
+      for (int r = 0; r < kRound; ++r) {
+        const int w = min(w0 + r, info.y);
+        const float* slot = p.partials + slot_of(p, w, u) * (G * (2 + D));
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int c = L::chunk(k);
-        mv[r][k] = slot[4 * c / D];
-        lv[r][k] = slot[G + 4 * c / D];
-        av[r][k] = *(const f32x4u_t*)(slot + 2 * G + 4 * c);
+        for (int k = 0; k < PER; ++k) {
+          const int c = L::chunk(k);
+          mv[r][k] = slot[4 * c / D];
+          lv[r][k] = slot[G + 4 * c / D];
+          av[r][k] = *(const f32x4u_t*)(slot + 2 * G + 4 * c);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRound; ++r) {
+        if (w0 + r > info.y) break;
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+          merge_fold(M[k], lt[k], a[k], mv[r][k], lv[r][k], av[r][k]);
       }
     }
-#pragma unroll
-    for (int r = 0; r < kRound; ++r) {
-      if (w0 + r > info.y) break;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) merge_fold(M[k], lt[k], a[k], mv[r][k], lv[r][k], av[r][k]);
-    }
-  }
+  };
+  if (info.y - info.x >= 4)  // block-uniform
+    fold_all(std::integral_constant<int, 8>{});
+  else
+    fold_all(std::integral_constant<int, 4>{});
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     if (!L::owns(k)) continue;

@@ -58,7 +58,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 // Fewer steps than this per worker would make partial slots and their merge outweigh the work
-// (at 8, a batch of 128 sequences on one KV head used every wave and spent 1.1 us more per call).
+// (at 8, a batch of 128 sequences on one KV head used every wave and spent 1.1 us more per call),
+// unless there are as many units as workers: a unit alone on its worker needs no partial.
 constexpr int kMinStepsPerWave = 16;
 // log2-domain slack before the running max is raised: probabilities stay below 2^8.
 constexpr float kRescaleSlack = 8.0f;
@@ -1397,7 +1398,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   plan.T = per_head * U;
   if (plan.T == 0) return;  // block-uniform
   const long long workers = quad ? (long long)gridDim.x : (long long)p.num_workers;
-  plan.ns = min(workers, (plan.T + kMinStepsPerWave - 1) / kMinStepsPerWave);
+  plan.ns = min(workers, max(seqs_nonempty * U, (plan.T + kMinStepsPerWave - 1) / kMinStepsPerWave));
   // Dynamic chunks only when a share of the steps is left to them: with the whole batch split
   // statically the plan (piece cost included) does not depend on the workspace's chunk slots.
   const bool dynamic =

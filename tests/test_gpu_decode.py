@@ -177,6 +177,19 @@ def test_decode_many_short_sequences_and_wide_batch():
     assert_close(got, oracle_decode(case, case.key_cache, case.value_cache), "700 short sequences")
 
 
+@pytest.mark.parametrize("max_len", [16, 64])
+def test_decode_one_unit_per_worker(max_len):
+    """A batch of 128 sequences of one to four steps at the 70B head shape: the plan gives every
+    unit its own workgroup (no partial slots, no merge work) and must still match the oracle."""
+    lens = np.random.default_rng((24, max_len)).integers(1, max_len + 1, size=128).tolist()
+    case = build_case(Spec(name="oneunit", num_q_heads=64, num_kv_heads=8, head_dim=128,
+                           block_size=16, seed=(25, max_len), decode_lens=lens))
+    kc, vc = dev_u16(case.key_cache), dev_u16(case.value_cache)
+    got = upcast(gpu_decode(case, kc, vc))
+    assert_close(got, oracle_decode(case, case.key_cache, case.value_cache),
+                 f"128 sequences of at most {max_len} tokens")
+
+
 @pytest.mark.parametrize("step", STEPS)
 @pytest.mark.parametrize("workers", [4, 12, 64])
 def test_decode_few_workers_long_ranges(workers, step, tune):

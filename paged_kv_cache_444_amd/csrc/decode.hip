@@ -1345,9 +1345,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       stage_lds[kWaves][kSlots][kStagedK ? kStageBytes<D, Fp8> : 16];
   extern __shared__ int seq_prefix[];  // [B+1] steps per KV head before each sequence (dynamic mode)
 
+  // Prefix sharing (several sequences reading the same physical blocks, as when many samples
+  // continue one prompt) shows as a sequence starting at the same block as the next one.  Such a
+  // batch re-reads blocks, so its K/V loads stay ordinary; any other batch streams them.
+  int shares = 0;
+  const size_t row = (size_t)p.max_blocks_per_seq;
   // Total steps of the batch.  The first kThreads sequences' step counts stay in a register for
   // the prefix sums below, so small batches read their lengths once.
-  const int n_first = (int)threadIdx.x < B ? steps_of(p, threadIdx.x) : 0;
+  int n_first = 0;
+  if (!p.skip_lens && B > 0 && row > 0) {
+    // Nothing skipped: the first probe compares first table entries, which do not depend on the
+    // lengths, so its two loads go out with the length load and the three share one round trip
+    // (taken one after the other they cost two at the start of every launch).  The loads are
+    // unconditional, at indices clamped into the batch, so that no branch holds a wait.
+    const int t = threadIdx.x;
+    const int len = p.seq_lens[min(t, B - 1)];
+    const int e0 = p.block_tables[(size_t)min(t, B - 1) * row];
+    const int e1 = p.block_tables[(size_t)min(t + 1, B - 1) * row];
+    n_first = t < B ? (max(min(max(len, 0), p.len_cap), 0) + kSub - 1) / kSub : 0;  // steps_of
+    shares = t + 1 < B && e0 == e1;
+  } else if ((int)threadIdx.x < B) {
+    n_first = steps_of(p, threadIdx.x);
+  }
   long long mine = n_first;
   int nonempty = n_first > 0;
   for (int s = threadIdx.x + kThreads; s < B; s += kThreads) {
@@ -1355,40 +1374,58 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     mine += n;
     nonempty += n > 0;
   }
-  // Prefix sharing (several sequences reading the same physical blocks, as when many samples
-  // continue one prompt) shows as a sequence starting at the same block as the next one.  Such a
-  // batch re-reads blocks, so its K/V loads stay ordinary; any other batch streams them.
-  int shares = 0;
-  const size_t row = (size_t)p.max_blocks_per_seq;
-  for (int s = threadIdx.x; s + 1 < B; s += kThreads) {
+  for (int s = threadIdx.x + (p.skip_lens || row == 0 ? 0 : kThreads); s + 1 < B; s += kThreads) {
     const int a = skip_blocks(p, s), b = skip_blocks(p, s + 1);  // first attended entries
     if (a < (int)row && b < (int)row)
       shares |= p.block_tables[(size_t)s * row + a] == p.block_tables[(size_t)(s + 1) * row + b];
   }
   shares = __any(shares);
-  // Wave totals.  When every per-head step count of the batch fits an int (it does unless the
-  // batch holds 2^35 tokens per head), the DPP scan's last lane gives them; otherwise 64-bit
-  // shuffles do.
-  nonempty = __builtin_amdgcn_readlane(wave_inclusive_scan(nonempty), 63);
-  if ((long long)B * ((p.len_cap + kSub - 1) / kSub) < (1LL << 31)) {
-    mine = __builtin_amdgcn_readlane(wave_inclusive_scan((int)mine), 63);
+  // When every per-head step count of the batch fits an int (it does unless the batch holds 2^35
+  // tokens per head), DPP scans serve; otherwise 64-bit shuffles give the wave totals.
+  const bool int_sums = (long long)B * ((p.len_cap + kSub - 1) / kSub) < (1LL << 31);
+  // One pass (a batch of at most kThreads sequences, one per thread): the wave scans of the step
+  // counts give the totals and the prefix sums at once, so a single barrier publishes both and a
+  // second one the workers' starts (four barriers in the general form).
+  const bool one_pass = B <= kThreads && int_sums;
+  int incl0 = 0, ne_incl0 = 0;
+  if (one_pass) {
+    incl0 = wave_inclusive_scan(n_first);
+    ne_incl0 = wave_inclusive_scan(nonempty);  // n_first > 0: no second chunk added to it
+    if (lane == 63) {
+      sh_scan[wave] = incl0;
+      sh_scan_ne[wave] = ne_incl0;
+      sh_shares[wave] = shares;
+    }
   } else {
+    nonempty = __builtin_amdgcn_readlane(wave_inclusive_scan(nonempty), 63);
+    if (int_sums) {
+      mine = __builtin_amdgcn_readlane(wave_inclusive_scan((int)mine), 63);
+    } else {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
-  }
-  if (lane == 0) {
-    sh_sum[wave] = mine;
-    sh_nonempty[wave] = nonempty;
-    sh_shares[wave] = shares;
+      for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
+    }
+    if (lane == 0) {
+      sh_sum[wave] = mine;
+      sh_nonempty[wave] = nonempty;
+      sh_shares[wave] = shares;
+    }
   }
   __syncthreads();
   long long per_head = 0;
   long long seqs_nonempty = 0;
   bool shared = false;
+  int before0 = 0, ne_before0 = 0;  // one pass: the waves before this one
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) {
-    per_head += sh_sum[k];
-    seqs_nonempty += sh_nonempty[k];
+    if (one_pass) {
+      per_head += sh_scan[k];
+      seqs_nonempty += sh_scan_ne[k];
+      before0 += (k < wave) ? sh_scan[k] : 0;
+      ne_before0 += (k < wave) ? sh_scan_ne[k] : 0;
+    } else {
+      per_head += sh_sum[k];
+      seqs_nonempty += sh_nonempty[k];
+    }
     shared |= sh_shares[k] != 0;
   }
   // quad: the workgroup is one worker over units of kWaves consecutive KV heads.
@@ -1430,61 +1467,73 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // Workers whose starts this block needs: its own (1 with quads, else kWaves) and the next one.
   const int n_own = quad ? 1 : kWaves;
   const long long wfirst = quad ? (long long)blockIdx.x : wbase;
-  if (threadIdx.x <= n_own) {
+  // Sequence s has n steps per head, excl steps per head before it and ne_excl non-empty
+  // sequences before it: record it as the start of every worker of this block whose target
+  // falls in its cost range.  The ranges of the non-empty sequences tile [0, CT), so each static
+  // worker's start is written by exactly one thread.
+  auto place = [&](int s, int n, long long excl, long long ne_excl) {
+    if ((dynamic || tail) && s < B) seq_prefix[s] = (int)excl;
+    if (n <= 0) return;
+    // The sequence's U units cover cost positions [c_lo, c_lo + U*(n + A)).
+    const long long lo = excl * U;
+    const long long j0 = ne_excl * U;
+    const long long c_lo = lo + plan.A * j0;
+    const long long per_unit = n + plan.A;
+    for (int k = 0; k <= n_own; ++k) {
+      const long long wk = wfirst + k;
+      if (wk >= plan.ns) break;
+      const long long t = plan.target(wk);
+      if (t >= c_lo && t < c_lo + U * per_unit) {
+        const long long kk = div_nonneg(t - c_lo, per_unit);
+        const long long o = max(0LL, t - c_lo - kk * per_unit - plan.A);
+        sh_start_s[k] = s;
+        sh_start_off[k] = kk * n + o;
+        sh_start_j[k] = j0 + kk;
+        sh_start_x[k] = lo + kk * n + o;
+      }
+    }
+  };
+  // Workers at or past ns start (and end) at S.  In one pass only they take the defaults, so no
+  // barrier has to order the defaults before the placements.
+  if ((int)threadIdx.x <= n_own && (!one_pass || wfirst + (int)threadIdx.x >= plan.ns)) {
     sh_start_s[threadIdx.x] = -1;
     sh_start_off[threadIdx.x] = 0;
     sh_start_j[threadIdx.x] = 0;
-    sh_start_x[threadIdx.x] = plan.S;  // workers at or past ns start (and end) at S
+    sh_start_x[threadIdx.x] = plan.S;
   }
-  __syncthreads();
-
-  // Prefix sums over sequences: locate where each static worker of this block starts, and keep
-  // the prefix in LDS for the dynamic chunks.
-  long long base = 0, ne_base = 0;
-  for (int c = 0; c < B; c += kThreads) {
-    const int s = c + threadIdx.x;
-    const int n = (c == 0) ? n_first : (s < B ? steps_of(p, s) : 0);
-    const int ne = n > 0;
-    const int incl = wave_inclusive_scan(n);
-    const int ne_incl = wave_inclusive_scan(ne);
-    if (lane == 63) {
-      sh_scan[wave] = incl;
-      sh_scan_ne[wave] = ne_incl;
-    }
+  long long base = 0;
+  if (one_pass) {
+    place(threadIdx.x, n_first, before0 + incl0 - n_first, ne_before0 + ne_incl0 - (n_first > 0));
+    base = per_head;
+  } else {
     __syncthreads();
-    int before = 0, chunk = 0, ne_before = 0, ne_chunk = 0;
-#pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
-      before += (k < wave) ? sh_scan[k] : 0;
-      chunk += sh_scan[k];
-      ne_before += (k < wave) ? sh_scan_ne[k] : 0;
-      ne_chunk += sh_scan_ne[k];
-    }
-    const long long excl = base + before + incl - n;
-    if ((dynamic || tail) && s < B) seq_prefix[s] = (int)excl;
-    if (n > 0) {
-      // The sequence's U units cover cost positions [c_lo, c_lo + U*(n + A)).
-      const long long lo = excl * U;
-      const long long j0 = (ne_base + ne_before + ne_incl - ne) * U;
-      const long long c_lo = lo + plan.A * j0;
-      const long long per_unit = n + plan.A;
-      for (int k = 0; k <= n_own; ++k) {
-        const long long wk = wfirst + k;
-        if (wk >= plan.ns) break;
-        const long long t = plan.target(wk);
-        if (t >= c_lo && t < c_lo + U * per_unit) {
-          const long long kk = div_nonneg(t - c_lo, per_unit);
-          const long long o = max(0LL, t - c_lo - kk * per_unit - plan.A);
-          sh_start_s[k] = s;
-          sh_start_off[k] = kk * n + o;
-          sh_start_j[k] = j0 + kk;
-          sh_start_x[k] = lo + kk * n + o;
-        }
+    // Prefix sums over sequences, kThreads at a time: locate where each static worker of this
+    // block starts, and keep the prefix in LDS for the dynamic chunks.
+    long long ne_base = 0;
+    for (int c = 0; c < B; c += kThreads) {
+      const int s = c + threadIdx.x;
+      const int n = (c == 0) ? n_first : (s < B ? steps_of(p, s) : 0);
+      const int ne = n > 0;
+      const int incl = wave_inclusive_scan(n);
+      const int ne_incl = wave_inclusive_scan(ne);
+      if (lane == 63) {
+        sh_scan[wave] = incl;
+        sh_scan_ne[wave] = ne_incl;
       }
+      __syncthreads();
+      int before = 0, chunk = 0, ne_before = 0, ne_chunk = 0;
+#pragma unroll
+      for (int k = 0; k < kWaves; ++k) {
+        before += (k < wave) ? sh_scan[k] : 0;
+        chunk += sh_scan[k];
+        ne_before += (k < wave) ? sh_scan_ne[k] : 0;
+        ne_chunk += sh_scan_ne[k];
+      }
+      place(s, n, base + before + incl - n, ne_base + ne_before + ne_incl - ne);
+      base += chunk;
+      ne_base += ne_chunk;
+      if (c + kThreads < B) __syncthreads();  // the next chunk rewrites sh_scan
     }
-    base += chunk;
-    ne_base += ne_chunk;
-    if (c + kThreads < B) __syncthreads();  // the next chunk rewrites sh_scan
   }
   if ((dynamic || tail) && threadIdx.x == 0) seq_prefix[B] = (int)base;
   __syncthreads();  // publishes sh_start_* and seq_prefix

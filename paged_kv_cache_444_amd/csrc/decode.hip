@@ -1633,6 +1633,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   if (u == 0 && threadIdx.x == 0) *p.counter = 0u;  // ready for the next call
   uint16_t* orow = p.out + ((size_t)s * p.num_q_heads + (size_t)h * G) * D;
   const size_t row0 = (size_t)s * p.num_q_heads + (size_t)h * G;
+  // The unit's worker range is loaded with the length, before the branch on it, so the two
+  // share one round trip.  (An empty sequence's range is stale and never read.)
+  int2 info = p.unit_info[u];
   if (clamped_len(p, s) == 0) {
     if (p.state_ml) {  // no keys here: an empty state
       for (int i = threadIdx.x; i < G * D; i += 256) {
@@ -1648,7 +1651,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     for (int i = threadIdx.x; i < G * D; i += 256) orow[i] = 0;
     return;
   }
-  int2 info = p.unit_info[u];
   info.x = max(info.x, 0);
   info.y = min(info.y, p.num_workers + p.dyn_cap - 1);
   if (info.x >= info.y) return;  // written by its only wave

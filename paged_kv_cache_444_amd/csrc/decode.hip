@@ -1374,11 +1374,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     mine += n;
     nonempty += n > 0;
   }
-  for (int s = threadIdx.x + (p.skip_lens || row == 0 ? 0 : kThreads); s + 1 < B; s += kThreads) {
-    const int a = skip_blocks(p, s), b = skip_blocks(p, s + 1);  // first attended entries
-    if (a < (int)row && b < (int)row)
-      shares |= p.block_tables[(size_t)s * row + a] == p.block_tables[(size_t)(s + 1) * row + b];
-  }
+  // With leading blocks skipped (the cascade's tails) the shared prefix has been taken out and
+  // attended once elsewhere, so no probe is made and the tails stream: probing their first
+  // attended entries would wait for the skips first.
+  for (int s = threadIdx.x + kThreads; !p.skip_lens && row > 0 && s + 1 < B; s += kThreads)
+    shares |= p.block_tables[(size_t)s * row] == p.block_tables[(size_t)(s + 1) * row];
   shares = __any(shares);
   // When every per-head step count of the batch fits an int (it does unless the batch holds 2^35
   // tokens per head), DPP scans serve; otherwise 64-bit shuffles give the wave totals.

@@ -753,7 +753,7 @@ pa_status_t prefill_impl(void* out, const void* query, const void* key_cache,
                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                          int32_t max_seq_len, float scale, bool fp8, float k_scale,
                          float v_scale, void* workspace, size_t workspace_bytes, void* stream,
-                         bool validate_only = false) {
+                         bool validate_only = false, bool concurrent = false) {
   if (fp8 && (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (fp8 && !std::isfinite(scale * k_scale))
@@ -813,6 +813,7 @@ pa_status_t prefill_impl(void* out, const void* query, const void* key_cache,
   p.scale_log2 = (fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
   p.kv_fp8 = fp8;
   p.v_scale = fp8 ? v_scale : 1.f;
+  p.concurrent = concurrent;
   if (need > 0) {
     const size_t rows = (size_t)total_q * num_q_heads * p.splits;
     p.ws_ml = static_cast<float*>(workspace);
@@ -862,12 +863,15 @@ pa_status_t pa_prefill_chunk_fp8(void* out, const void* query, const void* key_c
 
 namespace {
 
-pa_status_t prefill_call(const pa_prefill_args& a, void* stream, bool validate_only) {
+// concurrent: another kernel (the mixed step's decode) runs beside the chunk on the same CUs.
+pa_status_t prefill_call(const pa_prefill_args& a, void* stream, bool validate_only,
+                         bool concurrent = false) {
   return prefill_impl(a.out, a.query, a.key_cache, a.value_cache, a.num_blocks, a.block_tables,
                       a.query_start_loc, a.seq_lens, a.num_seqs, a.total_q, a.max_q_len,
                       a.num_q_heads, a.num_kv_heads, a.head_dim, a.block_size,
                       a.max_blocks_per_seq, a.max_seq_len, a.scale, a.kv_fp8 != 0, a.k_scale,
-                      a.v_scale, a.workspace, a.workspace_bytes, stream, validate_only);
+                      a.v_scale, a.workspace, a.workspace_bytes, stream, validate_only,
+                      concurrent);
 }
 
 pa_status_t decode_call(const pa_decode_args& a, void* stream, bool validate_only) {
@@ -962,7 +966,7 @@ pa_status_t pa_mixed_step(const pa_prefill_args* prefill, const pa_decode_args* 
   // Once the fork is recorded the join is always made, so later work on `stream` waits for
   // whatever was launched on the side stream even when a launch fails.
   st = decode_call(*decode, side_stream, false);
-  if (st == PA_OK) st = prefill_call(*prefill, stream, false);
+  if (st == PA_OK) st = prefill_call(*prefill, stream, false, true);
   if ((e = hipEventRecord(join, side)) != hipSuccess ||
       (e = hipStreamWaitEvent(hs, join, 0)) != hipSuccess)
     return st != PA_OK ? st : hip_status(e, "mixed_step (join)");

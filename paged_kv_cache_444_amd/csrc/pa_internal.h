@@ -137,6 +137,10 @@ struct PrefillParams {
   // multiplied by v_scale (1 for bf16 pools).
   int kv_fp8;
   float v_scale;
+  // Nonzero when another kernel runs beside this one on the same CUs (the mixed step's decode on
+  // its side stream).  Otherwise each wave raises its issue priority over its softmax and second
+  // product, which a concurrent kernel's waves would then wait behind.
+  int concurrent;
 };
 
 // Context split chosen for a prefill launch (it sizes the workspace).

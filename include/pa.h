@@ -70,7 +70,7 @@ const char* pa_last_error(void);
  *   PA_DECODE_PREFETCH_FP8  1-2, default 1: the same for FP8 pools
  *   PA_DECODE_MFMA          0-1, default 1: bf16 decode steps on the matrix cores (0: vector ALUs)
  *   PA_DECODE_QUAD          0-1, default 1: workgroup workers over units of four KV heads
- *   PA_DECODE_PIECE_COST    0-64, default 6: steps' worth of cost per unit a decode worker starts
+ *   PA_DECODE_PIECE_COST    0-64, default 4: steps' worth of cost per unit a decode worker starts
  *   PA_DECODE_WORKERS       default 0 (one workgroup of four waves per CU): total decode worker
  *                           waves, rounded down to a multiple of 4 and capped at what can be
  *                           resident; values below 4 mean the default

@@ -139,7 +139,7 @@ struct TunableDef {
 constexpr TunableDef kTunableDefs[pa::kNumTunables] = {
     {"PA_DECODE_PREFETCH", 1, 0, 2},    {"PA_DECODE_PREFETCH_FP8", 1, 1, 2},
     {"PA_DECODE_MFMA", 1, 0, 1},        {"PA_DECODE_QUAD", 1, 0, 1},
-    {"PA_DECODE_PIECE_COST", 6, 0, 64}, {"PA_DECODE_WORKERS", 0, 0, 1 << 20},
+    {"PA_DECODE_PIECE_COST", 4, 0, 64}, {"PA_DECODE_WORKERS", 0, 0, 1 << 20},
     {"PA_DECODE_STATIC_Q10", 1024, 512, 1024}, {"PA_DECODE_CHUNK", 4, 1, 256},
     {"PA_PREFILL_SPLITS", 0, 0, 16},    {"PA_DECODE_TAIL_Q10", 0, 0, 512},
     {"PA_DECODE_TAIL_Q10_FP8", 0, 0, 512}, {"PA_DECODE_TAIL_CHUNK", 12, 1, 256},

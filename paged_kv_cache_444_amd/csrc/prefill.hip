@@ -563,17 +563,32 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
   if (unit >= (size_t)p.total_q * p.num_q_heads) return;
   const int d = 4 * (threadIdx.x % TPH);
   const size_t u0 = unit * p.ws_splits;
-  float M = kNegInf;
-  for (int j = 0; j < p.ws_splits; ++j) M = fmaxf(M, p.ws_ml[2 * (u0 + j)]);
-  float lt = 0.f;
+  // One pass with an online rescale, four splits' (m, l, acc) loads issued together per round
+  // (indices clamped to the last split), so a row with at most four splits costs one round trip
+  // where a pass for the maximum and then one for the sums cost two.  An empty range (m = -inf)
+  // adds nothing.
+  constexpr int kRound = 4;
+  float M = kNegInf, lt = 0.f;
   f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-  if (M != kNegInf) {
-    for (int j = 0; j < p.ws_splits; ++j) {
-      const float mj = p.ws_ml[2 * (u0 + j)];
-      if (mj == kNegInf) continue;  // empty range for this row
-      const float w = fast_exp2(mj - M);
-      lt += p.ws_ml[2 * (u0 + j) + 1] * w;
-      a += *(const f32x4_t*)(p.ws_acc + (u0 + j) * D + d) * w;
+  for (int j0 = 0; j0 < p.ws_splits; j0 += kRound) {
+    float mv[kRound], lv[kRound];
+    f32x4_t av[kRound];
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const size_t u = u0 + min(j0 + r, p.ws_splits - 1);
+      mv[r] = p.ws_ml[2 * u];
+      lv[r] = p.ws_ml[2 * u + 1];
+      av[r] = *(const f32x4_t*)(p.ws_acc + u * D + d);
+    }
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      if (j0 + r >= p.ws_splits || mv[r] == kNegInf) continue;
+      const float mn = fmaxf(M, mv[r]);
+      const float c_old = fast_exp2(M - mn);  // 0 while M is -inf
+      const float c_new = fast_exp2(mv[r] - mn);
+      lt = lt * c_old + lv[r] * c_new;
+      a = a * c_old + av[r] * c_new;
+      M = mn;
     }
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;

@@ -204,11 +204,11 @@ __device__ __forceinline__ uint4 widen8(const uint2& w) {
                     fp8_pair_to_bf16<false>(w.y), fp8_pair_to_bf16<true>(w.y));
 }
 
-// Prio: each wave takes a raised issue priority from the start of a row tile's softmax to the
-// end of its second product, and the normal one for the score products.  The two waves of a
-// SIMD then settle into alternating phases, one wave's exponentials and probability products
-// issuing ahead of the other wave's score products: 4.4 % (bf16) and 6 % (FP8) off the chunk.
-// Off when another kernel shares the CUs, whose waves would wait behind the raised ones.
+// Prio: each wave takes a raised issue priority over its softmax and second products, and the
+// normal one for the score products.  The two waves of a SIMD then settle into alternating
+// phases, one wave's exponentials and probability products issuing ahead of the other wave's
+// score products: about 6 % (bf16) and 7 % (FP8) off the chunk.  Off when another kernel shares
+// the CUs, whose waves would wait behind the raised ones.
 template <int D, int G, bool Fp8, bool Prio>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
   constexpr int RT = kRowTiles<D>;
@@ -443,7 +443,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
       // Online softmax of row tile rt, then its second product with the V fragments vf.
       auto softmax_pv = [&](int rt, const f32x4_t (&sc)[2], auto&& vf)
                             __attribute__((always_inline)) {
-        if constexpr (Prio) __builtin_amdgcn_s_setprio(1);
         float x[8];  // z = y - M; -inf where masked
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -496,7 +495,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
         lsum[rt] = mfma(ones, pb, lsum[rt]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[dt][rt] = mfma(vf(dt), pb, acc[dt][rt]);
-        if constexpr (Prio) __builtin_amdgcn_s_setprio(0);
       };
       if constexpr (RT == 2) {
         // Row tile 1's scores are issued before row tile 0's softmax and row tile 0's second
@@ -506,14 +504,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
         for (int dt = 0; dt < DT; ++dt) vf[dt] = v_frag(dt);
         auto vreg = [&](int dt) __attribute__((always_inline)) { return vf[dt]; };
         f32x4_t s0[2], s1[2];
+        // bf16 drops the raised priority only for the score products (it stays up over the next
+        // tile's barrier and fragment reads); FP8 drops it as soon as the second products are
+        // issued (kept up until the scores, FP8 measured 8 % slower; bf16 1.6 % faster).
+        if constexpr (Prio && !Fp8) __builtin_amdgcn_s_setprio(0);
         scores(0, s0);
         scores(1, s1);
+        if constexpr (Prio) __builtin_amdgcn_s_setprio(1);
         softmax_pv(0, s0, vreg);
         softmax_pv(1, s1, vreg);
+        if constexpr (Prio && Fp8) __builtin_amdgcn_s_setprio(0);
       } else {
         f32x4_t s0[2];
         scores(0, s0);
+        if constexpr (Prio) __builtin_amdgcn_s_setprio(1);
         softmax_pv(0, s0, v_frag);
+        if constexpr (Prio) __builtin_amdgcn_s_setprio(0);
       }
       cur = (cur == kStages - 1) ? 0 : cur + 1;
     };
@@ -523,6 +529,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillParams p) {
     for (; t < t_mask; ++t) walk_tile(t, std::false_type{});
     for (; t < t_end; ++t) walk_tile(t, std::true_type{});
     wait_vmcnt<0>();  // no tile load may still be writing LDS when the workgroup ends
+    if constexpr (Prio) __builtin_amdgcn_s_setprio(0);
   }
 
   // Finish: normalise or hand the split's state over.
